@@ -1,0 +1,320 @@
+"""Pins of the CPU oracle against facts that do not come from the oracle itself:
+numpy's IEEE float16 conversion, exact rational arithmetic, closed forms of the
+quantisers on inputs that already lie on the quantisation grid, textbook dense
+matmul, integer einsum, Higham's summation bound, and the invariants the pages
+state (split batch equals the halves; masked experts give zero rows)."""
+from fractions import Fraction
+
+import numpy as np
+import pytest
+
+import oracle
+from quantized_moe_expert_quantize_amd import inputs
+from tests import _decode
+
+U64 = 2.0 ** -53          # unit roundoff of fp64
+
+
+def gamma(n, u):
+    return n * u / (1 - n * u)
+
+
+# ---------------------------------------------------------------- fp16 -----
+
+def test_fp16_decode_exhaustive():
+    h = np.arange(65536, dtype=np.uint32).astype(np.uint16)
+    got = oracle.fp16_to_fp32(h)
+    ref = h.view(np.float16).astype(np.float32)
+    nan = np.isnan(ref)
+    assert np.array_equal(np.isnan(got), nan)
+    assert np.array_equal(got[~nan].view(np.uint32), ref[~nan].view(np.uint32))
+
+
+def _fp16_edges():
+    v = [0.0, -0.0, 1.0, -1.0, 65504.0, 65519.996, 65520.0, -65520.0, 65536.0, 1e30, -1e30,
+         2.0 ** -14, 2.0 ** -24, 2.0 ** -25, -2.0 ** -25, 1.5 * 2.0 ** -25, 2.0 ** -26,
+         3 * 2.0 ** -25, 5 * 2.0 ** -25, 2.0 ** -14 - 2.0 ** -25, 2.0 ** -14 - 2.0 ** -24,
+         1.0 + 2.0 ** -11, 1.0 + 3 * 2.0 ** -11, 1.0 + 2.0 ** -11 + 2.0 ** -23, 2049.0, 2051.0,
+         np.inf, -np.inf, 1.0 / 127.0, 4064.0 / 127.0]
+    return np.array(v, dtype=np.float32)
+
+
+def test_fp16_encode_edges_and_random():
+    rng = np.random.default_rng(123)
+    bits = rng.integers(0, 2 ** 32, size=1_000_000, dtype=np.uint64).astype(np.uint32)
+    rand_any = bits.view(np.float32)
+    rand_range = (rng.standard_normal(1_000_000) * rng.choice([1e-6, 1e-3, 1.0, 1e3, 3e4], 1_000_000)).astype(np.float32)
+    # values exactly halfway between neighbouring fp16 numbers (ties-to-even cases)
+    h = rng.integers(0, 0x7bff, size=100_000).astype(np.uint16)
+    lo = h.view(np.float16).astype(np.float64)
+    hi = (h + 1).astype(np.uint16).view(np.float16).astype(np.float64)
+    ties = ((lo + hi) / 2).astype(np.float32)
+    for f in (_fp16_edges(), rand_any, rand_range, ties):
+        got = oracle.fp32_to_fp16(f)
+        with np.errstate(over="ignore"):
+            ref = f.astype(np.float16).view(np.uint16)
+        nan = np.isnan(f)
+        assert np.array_equal(got[~nan], ref[~nan])
+        assert np.all(np.isnan(got[nan].view(np.float16)))
+
+
+# ---------------------------------------------------------------- Q8_1 -----
+
+def test_q8_1_zero_block():
+    y = oracle.quantize_q8_1(np.zeros((2, 64), np.float32))
+    assert not y.any()
+
+
+def test_q8_1_constant_block():
+    for c in (0.5, -3.25, 1e-3):
+        y = oracle.quantize_q8_1(np.full((1, 32), c, np.float32))
+        d, s, q = _decode.q8_1(y, 32)
+        assert np.all(q == (127 if c > 0 else -127))
+        assert d[0, 0] == np.float16(np.float32(abs(c)) / np.float32(127))
+        assert s[0, 0] == np.float16(np.float32(np.float32(abs(c)) / np.float32(127)) * np.float32(q.sum()))
+
+
+def test_q8_1_single_nonzero():
+    x = np.zeros((1, 32), np.float32)
+    x[0, 7] = -0.3
+    _, _, q = _decode.q8_1(oracle.quantize_q8_1(x), 32)
+    assert q[0, 0, 7] == -127 and np.count_nonzero(q) == 1
+
+
+def test_q8_1_exact_grid_recovery():
+    """Inputs q*2^j with an element of magnitude 127 quantise back to exactly q, d = 2^j."""
+    rng = np.random.default_rng(5)
+    q = rng.integers(-127, 128, size=(64, 32))
+    q[np.arange(64), rng.integers(0, 32, 64)] = rng.choice([-127, 127], 64)
+    j = rng.integers(-20, 4, size=(64, 1))
+    x = (q * np.exp2(j)).astype(np.float32)
+    y = oracle.quantize_q8_1(x.reshape(8, 256))
+    d, s, qq = _decode.q8_1(y, 256)
+    assert np.array_equal(qq.reshape(64, 32), q)
+    assert np.array_equal(d.reshape(64), np.exp2(j[:, 0]))
+    # s = fp16(d * sum q): d*sum is exact here, so numpy's own float16 gives the answer
+    assert np.array_equal(s.reshape(64), (np.exp2(j[:, 0]) * q.sum(1)).astype(np.float16).astype(np.float64))
+
+
+def test_q8_1_rounding_is_half_away_from_zero():
+    x = np.zeros((1, 32), np.float32)
+    x[0, 0] = 127.0           # amax = 127 -> d = 1 exactly
+    x[0, 1:9] = [2.5, -2.5, 0.5, -0.5, 1.5, -1.5, 126.5, -3.5]
+    _, _, q = _decode.q8_1(oracle.quantize_q8_1(x), 32)
+    assert q[0, 0, :9].tolist() == [127, 3, -3, 1, -1, 2, -2, 127, -4]
+
+
+def test_q8_1_random_properties():
+    x = inputs.activations(64, 2816, seed=3)
+    d, s, q = _decode.q8_1(oracle.quantize_q8_1(x), 2816)
+    xb = x.reshape(64, 88, 32).astype(np.float64)
+    amax = np.abs(xb).max(-1)
+    d32 = (amax.astype(np.float32) / np.float32(127)).astype(np.float64)
+    assert np.all(np.abs(q) <= 127)
+    assert np.all(np.abs(q).max(-1) == 127)                       # the amax element maps to +-127
+    # half a step, widened by the fp32 rounding of x/d (|x/d| <= 127)
+    assert np.all(np.abs(xb - q * d32[..., None]) <= (0.5 + 128 * 2.0 ** -23) * d32[..., None])
+    assert np.all(np.sign(q) * np.sign(xb) >= 0)
+    assert np.array_equal(d, d32.astype(np.float32).astype(np.float16).astype(np.float64))
+
+
+# ---------------------------------------------------------------- Q4_0 -----
+
+def test_q4_0_exact_grid_recovery():
+    """(c) * d with codes c in [-8, 7] and one c = -8 quantise back to q = c + 8 and d."""
+    rng = np.random.default_rng(9)
+    c = rng.integers(-7, 8, size=(100, 32))
+    c[np.arange(100), rng.integers(0, 32, 100)] = -8
+    d = rng.choice([-1, 1], size=(100, 1)) * np.exp2(rng.integers(-14, 2, size=(100, 1)).astype(np.float64))
+    x = (c * d).astype(np.float32)
+    dd, qq = _decode.q4_0(oracle.quantize_q4_0(x.reshape(25, 128)), 128)
+    assert np.array_equal(qq.reshape(100, 32), c)
+    assert np.array_equal(dd.reshape(100), d[:, 0])
+
+
+def test_q4_0_nibble_order_and_clamp():
+    x = np.zeros((1, 32), np.float32)
+    x[0, 0] = -8.0               # max magnitude, negative -> d = 1
+    x[0, 1] = 7.0
+    x[0, 16] = 3.0               # high nibble of byte 0
+    x[0, 17] = -1.0
+    y = oracle.quantize_q4_0(x)
+    assert y[0, 0:2].view(np.float16)[0] == 1.0
+    assert y[0, 2] == (0 | (11 << 4))        # elements 0 and 16
+    assert y[0, 3] == (15 | (7 << 4))        # elements 1 and 17
+    # positive maximum: d is negative and the value -m maps past 7 -> clamped to 15
+    x2 = np.zeros((1, 32), np.float32)
+    x2[0, 3] = 4.0
+    x2[0, 4] = -4.0
+    d2, q2 = _decode.q4_0(oracle.quantize_q4_0(x2), 32)
+    assert d2[0, 0] == -0.5 and q2[0, 0, 3] == -8 and q2[0, 0, 4] == 7
+    # all-zero block: d = 0, every code 8 (value 0)
+    d3, q3 = _decode.q4_0(oracle.quantize_q4_0(np.zeros((1, 32), np.float32)), 32)
+    assert d3[0, 0] == 0 and np.all(q3 == 0)
+
+
+def test_q4_0_random_error_bound():
+    w = inputs.weights(2, 16, 256, seed=1).reshape(32, 256)
+    d, q = _decode.q4_0(oracle.quantize_q4_0(w), 256)
+    xb = w.reshape(32, 8, 32).astype(np.float64)
+    ad = np.abs(d)[..., None]
+    # half a step, except at the clamped top code 7 (x/d may reach 8), plus the fp16
+    # rounding of d (|q| <= 8) and the fp32 rounding of x/d
+    step = np.where(q == 7, 1.0, 0.5 + 8 * 2.0 ** -23)
+    assert np.all(np.abs(xb - q * d[..., None]) <= step * ad + 8 * ad * 2.0 ** -11)
+    assert np.all(np.abs(q).max(-1) == 8)               # the max-magnitude element has code 0
+
+
+# ---------------------------------------------------------------- MoE ------
+
+def _tiny(seed=0, E=8, top_k=2, T=16, K=256, N=128, kind="uniform"):
+    w = oracle.quantize_q4_0(inputs.weights(E, N, K, seed=seed))
+    a = oracle.quantize_q8_1(inputs.activations(T, K, seed=seed))
+    ids = inputs.routing(T, E, top_k, seed=seed, kind=kind)
+    return w, a, ids, dict(E=E, N=N, K=K, T=T, top_k=top_k)
+
+
+def _run(w, a, ids, c, **kw):
+    return oracle.moe(w, a, ids, c["E"], c["N"], c["K"], c["T"], c["top_k"], **kw)
+
+
+def test_moe_exact_rational_bruteforce():
+    """Exact value with Fractions; the oracle's fp64 error is within gamma_nb * sum|term|."""
+    w, a, ids, c = _tiny(E=3, top_k=2, T=3, K=96, N=5)
+    out, ab = _run(w, a, ids, c, want_abssum=True)
+    wd, wq = _decode.q4_0(w.reshape(3, 5, -1), 96)
+    ad, _, aq = _decode.q8_1(a, 96)
+    nb = 3
+    for p in range(c["T"] * c["top_k"]):
+        t, e = p // 2, int(ids.reshape(-1)[p])
+        for n in range(5):
+            exact = Fraction(0)
+            for b in range(nb):
+                P = sum(int(wq[e, n, b, i]) * int(aq[t, b, i]) for i in range(32))
+                exact += Fraction(P) * Fraction(wd[e, n, b]) * Fraction(ad[t, b])
+            err = abs(Fraction(out[p, n]) - exact)
+            assert err <= Fraction(gamma(nb, U64)) * Fraction(ab[p, n])
+
+
+def test_moe_dense_special_case_matches_numpy_matmul():
+    """E = 1, top_k = 1 reduces the MoE to a dense dequantise-then-matmul."""
+    w, a, ids, c = _tiny(E=1, top_k=1, T=9, K=320, N=33)
+    out, ab = _run(w, a, ids, c, want_abssum=True)
+    wd, wq = _decode.q4_0(w.reshape(33, -1), 320)
+    ad, _, aq = _decode.q8_1(a, 320)
+    Wf = (wq * wd[..., None]).reshape(33, 320)
+    Af = (aq * ad[..., None]).reshape(9, 320)
+    ref = Af @ Wf.T
+    # both sides round only in fp64 sums; numpy's blocked sum is bounded the same way
+    bound = 2 * gamma(320, U64) * (np.abs(Af) @ np.abs(Wf).T)
+    assert np.all(np.abs(out - ref) <= bound)
+
+
+def test_moe_partials_match_integer_einsum():
+    w, a, ids, c = _tiny()
+    P = oracle.moe_partials(w, a, ids, c["E"], c["N"], c["K"], c["T"], c["top_k"])
+    _, wq = _decode.q4_0(w.reshape(c["E"], c["N"], -1), c["K"])
+    _, _, aq = _decode.q8_1(a, c["K"])
+    tok = np.arange(c["T"] * c["top_k"]) // c["top_k"]
+    ref = np.einsum("pnbi,pbi->pnb", wq[ids.reshape(-1)], aq[tok])
+    assert P.dtype == np.int32 and np.array_equal(P, ref)
+    assert np.abs(P).max() <= 8 * 127 * 32
+
+
+def test_moe_outputs_equal_scaled_partials_sum():
+    w, a, ids, c = _tiny(seed=4)
+    out = _run(w, a, ids, c)
+    P = oracle.moe_partials(w, a, ids, c["E"], c["N"], c["K"], c["T"], c["top_k"]).astype(np.float64)
+    wd, _ = _decode.q4_0(w.reshape(c["E"], c["N"], -1), c["K"])
+    ad, _, _ = _decode.q8_1(a, c["K"])
+    tok = np.arange(c["T"] * c["top_k"]) // c["top_k"]
+    terms = P * wd[ids.reshape(-1)] * ad[tok][:, None, :]
+    ref = terms.sum(-1)
+    assert np.all(np.abs(out - ref) <= 2 * gamma(8, U64) * np.abs(terms).sum(-1))
+
+
+def test_moe_closed_forms():
+    E, N, K, T, k = 2, 3, 64, 2, 1
+    nb = K // 32
+    # all weight codes 8 -> every output exactly zero
+    w = np.zeros((E, N, nb, 18), np.uint8)
+    w[..., 0:2] = np.frombuffer(np.float16(0.75).tobytes(), np.uint8)
+    w[..., 2:] = 0x88
+    a = oracle.quantize_q8_1(inputs.activations(T, K, seed=2))
+    ids = np.array([[1], [0]], np.int32)
+    assert not oracle.moe(w.reshape(-1), a, ids, E, N, K, T, k).any()
+    # one nonzero weight code against a one-hot activation: out = d4*d8*(q4-8)*q8
+    w2 = w.copy()
+    w2[1, 2, 1, 2 + 5] = 0x80 | 13                      # element 5 of block 1 -> code 13 (value 5)
+    x = np.zeros((T, K), np.float32)
+    x[0, 32 + 5] = -2.0                                 # block 1, element 5 -> q = -127
+    a2 = oracle.quantize_q8_1(x)
+    out = oracle.moe(w2.reshape(-1), a2, ids, E, N, K, T, k)
+    d8 = float(np.float16(np.float32(2.0) / np.float32(127)))
+    expect = np.zeros((T * k, N))
+    expect[0, 2] = 0.75 * d8 * 5 * -127
+    assert np.array_equal(out, expect)
+
+
+def test_moe_masked_and_duplicate_ids():
+    w, a, ids, c = _tiny()
+    bad = ids.copy()
+    bad[0, 0] = -1
+    bad[3, 1] = c["E"]
+    bad[5, 1] = bad[5, 0]                               # duplicate expert within a token
+    out = _run(w, a, bad, c)
+    ref = _run(w, a, ids, c)
+    assert not out[0].any() and not out[3 * 2 + 1].any()
+    assert np.array_equal(out[5 * 2 + 1], out[5 * 2 + 0])
+    keep = np.ones(out.shape[0], bool)
+    keep[[0, 7, 11]] = False
+    assert np.array_equal(out[keep], ref[keep])
+
+
+def test_moe_split_batch_equals_halves():
+    """A batch equals the same batch computed as two halves [FreeToken PR #185, "Test"]."""
+    w, a, ids, c = _tiny(T=17)
+    full = _run(w, a, ids, c)
+    nb36 = c["K"] // 32 * 36
+    h = 9
+    c1 = dict(c, T=h)
+    c2 = dict(c, T=c["T"] - h)
+    a_ = a.reshape(c["T"], nb36)
+    o1 = _run(w, np.ascontiguousarray(a_[:h]).reshape(-1), np.ascontiguousarray(ids[:h]), c1)
+    o2 = _run(w, np.ascontiguousarray(a_[h:]).reshape(-1), np.ascontiguousarray(ids[h:]), c2)
+    assert np.array_equal(full, np.concatenate([o1, o2]))
+
+
+def test_moe_token_permutation_and_expert_relabel():
+    w, a, ids, c = _tiny(seed=7)
+    out = _run(w, a, ids, c)
+    rng = np.random.default_rng(0)
+    perm = rng.permutation(c["T"])
+    nb36 = c["K"] // 32 * 36
+    a_p = np.ascontiguousarray(a.reshape(c["T"], nb36)[perm]).reshape(-1)
+    out_p = _run(w, a_p, np.ascontiguousarray(ids[perm]), c)
+    assert np.array_equal(out_p.reshape(c["T"], c["top_k"], -1), out.reshape(c["T"], c["top_k"], -1)[perm])
+    relabel = rng.permutation(c["E"])                   # new id of old expert e is relabel[e]
+    w_r = np.empty_like(w.reshape(c["E"], -1))
+    w_r[relabel] = w.reshape(c["E"], -1)
+    out_r = _run(np.ascontiguousarray(w_r).reshape(-1), a, np.ascontiguousarray(relabel[ids]).astype(np.int32), c)
+    assert np.array_equal(out_r, out)
+
+
+def test_moe_pairs_matches_full():
+    w, a, ids, c = _tiny(seed=2, kind="zipf")
+    full, ab = _run(w, a, ids, c, want_abssum=True)
+    pairs = np.array([0, 5, 31, 17, 5], np.int64)
+    sub, sab = oracle.moe_pairs(w, a, ids, c["E"], c["N"], c["K"], c["T"], c["top_k"], pairs, want_abssum=True)
+    assert np.array_equal(sub, full[pairs]) and np.array_equal(sab, ab[pairs])
+
+
+def test_routing_generators():
+    u = inputs.routing(4096, 128, 8, seed=0)
+    assert u.shape == (4096, 8) and u.min() >= 0 and u.max() < 128
+    assert all(len(set(r)) == 8 for r in u[:512].tolist())
+    z = inputs.routing(8192, 128, 8, seed=0, kind="zipf")
+    counts = np.bincount(z.reshape(-1), minlength=128)
+    assert all(len(set(r)) == 8 for r in z[:512].tolist())
+    assert counts[0] > 20 * counts[-1]                 # hot and cold experts
+    assert np.array_equal(inputs.routing(4096, 128, 8, seed=0), u)
