@@ -1,0 +1,164 @@
+/*
+ * ftq.h -- C ABI of libftq: the mixture-of-experts expert matmul with 4-bit
+ * block-quantized weights (Q4_0) against 8-bit block-quantized activations
+ * (Q8_1) on AMD Instinct MI355X (gfx950).
+ *
+ * What the library computes.  For every flat (token, top-k) pair
+ * p = t*top_k + j, with e = topk_ids[t][j]:
+ *
+ *     out[p][n] = sum over blocks b of  P[p][n][b] * d4[e][n][b] * d8[t][b]
+ *     P[p][n][b] = sum_{i<32} (q4[e][n][b][i] - 8) * q8[t][b][i]     (exact int)
+ *
+ * i.e. the routed expert's Q4_0 rows dotted with the token's Q8_1 row, one
+ * output row per pair.  This is the MoE GEMV of FreeToken PR #185 ("fix(kernel):
+ * launch GGUF MoE GEMV token axis on grid.x, not grid.z", sections Problem and
+ * Fix), generalised so that batches of any size run, with no 65535-pair limit
+ * and 64-bit size arithmetic (mlxcel PR #652, "fix(cuda/quantized): chunk
+ * long-prompt qmm launches to avoid gridDim>65535 and int overflow", Summary).
+ *
+ * Block formats (GGUF; the pages name them, the layouts are the GGUF ones):
+ *   Q4_0 block, 18 bytes: fp16 d, then 16 bytes; byte i holds element i in its
+ *       low nibble and element i+16 in its high nibble; value = (nibble-8)*d.
+ *   Q8_1 block, 36 bytes: fp16 d, fp16 s, then 32 int8 q; value = q*d and
+ *       s = d * sum(q).  The matmul reads d and q only.
+ *
+ * Conventions shared by every entry point:
+ *   - Sizes are int64_t.  Pointers are device pointers on the current HIP
+ *     device unless stated.  Work is enqueued on `stream` (0 = null stream);
+ *     no call synchronises, allocates, frees or reads device data back to the
+ *     host, so every call may be recorded into a HIP graph.
+ *   - The caller owns every buffer.  The library writes only the outputs and
+ *     the workspace named in each call.
+ *   - Arguments are validated before anything is enqueued; on a bad argument
+ *     nothing is launched and FTQ_ERR_INVALID_ARG (or FTQ_ERR_UNSUPPORTED /
+ *     FTQ_ERR_WORKSPACE) is returned.
+ *   - Every kernel launch is checked immediately after it is issued; a
+ *     rejected launch returns FTQ_ERR_LAUNCH and ftq_last_error() names the
+ *     kernel, grid, block and LDS bytes (FreeToken PR #185, Fix: a rejected
+ *     launch reports the geometry that caused it instead of latching).  The
+ *     error is cleared, so the next call is unaffected.  Faults during
+ *     execution surface at the caller's next synchronisation, as for any
+ *     asynchronous HIP work.
+ *   - No C++ exception crosses this interface.
+ */
+#ifndef FTQ_H
+#define FTQ_H
+
+#include <stddef.h>
+#include <stdint.h>
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+    FTQ_OK = 0,
+    FTQ_ERR_INVALID_ARG = 1,  /* bad size, null or misaligned pointer        */
+    FTQ_ERR_WORKSPACE = 2,    /* workspace missing or smaller than required  */
+    FTQ_ERR_LAUNCH = 3,       /* a kernel launch was rejected               */
+    FTQ_ERR_UNSUPPORTED = 4,  /* valid request this build does not handle    */
+    FTQ_ERR_HIP = 5           /* a HIP runtime query failed                  */
+} ftq_status;
+
+typedef enum {
+    FTQ_PATH_AUTO = 0,        /* chosen on the host from the sizes alone     */
+    FTQ_PATH_GEMV = 1,        /* memory-bound path for few pairs per expert  */
+    FTQ_PATH_GROUPED = 2      /* expert-sorted int8-MFMA tiles for prefill   */
+} ftq_path;
+
+#define FTQ_QK 32
+#define FTQ_Q4_0_BLOCK_BYTES 18
+#define FTQ_Q8_1_BLOCK_BYTES 36
+
+/*
+ * Quantize fp32 activations to Q8_1 (the activation quantiser that runs before
+ * the MoE GEMV; FreeToken PR #185, Fix, "quantize_row_q8_1_cuda").
+ *   x: fp32 [T][K], row-major, 16-byte aligned.      K % 32 == 0, T >= 0.
+ *   y: [T][K/32] Q8_1 blocks (36 B each), 4-byte aligned, written.
+ * Per 32-value block: amax = max|x|, d = amax/127 (fp32, IEEE division),
+ * q = round-half-away-from-zero(x/d) (0 when amax == 0), s = d*sum(q) in fp32;
+ * d and s stored as fp16 (round to nearest even).  Bit-exact and deterministic.
+ * T == 0 is a no-op.  Any number of rows: the launch has no 65535 limit.
+ */
+int ftq_quantize_q8_1(const float* x, int64_t T, int64_t K, void* y, hipStream_t stream);
+
+/*
+ * Quantize fp32 weights to Q4_0 (weight preparation; not part of the matmul).
+ *   w: fp32 [rows][K], 16-byte aligned.  K % 32 == 0.
+ *   y: [rows][K/32] Q4_0 blocks (18 B each), 2-byte aligned, written.
+ * Per block: m = the element of largest magnitude (first on ties), d = m/-8,
+ * q = clamp(round-half-away(x/d) + 8, 0, 15) (8 when d == 0); d stored fp16.
+ */
+int ftq_quantize_q4_0(const float* w, int64_t rows, int64_t K, void* y, hipStream_t stream);
+
+/*
+ * The path FTQ_PATH_AUTO takes for these sizes (FTQ_PATH_GEMV or
+ * FTQ_PATH_GROUPED), or -FTQ_ERR_INVALID_ARG for invalid sizes.  Pure host
+ * arithmetic: the choice never depends on device data, so a batch and any
+ * split of it into halves of similar size take the same path.
+ */
+int ftq_moe_select_path(int64_t E, int64_t N, int64_t K, int64_t T, int64_t top_k);
+
+/*
+ * Exact workspace size in bytes that ftq_moe_q4_0_q8_1 needs for these sizes
+ * and this path (FTQ_PATH_AUTO resolved as above); 0 means none.  Returns -1
+ * for invalid sizes.  Host arithmetic only.
+ */
+int64_t ftq_moe_workspace_bytes(int64_t E, int64_t N, int64_t K, int64_t T, int64_t top_k, int path);
+
+/*
+ * The MoE expert matmul.
+ *   w:        [E][N][K/32] Q4_0 blocks (expert e, row n, block b at byte
+ *             ((e*N + n)*(K/32) + b)*18), 2-byte aligned.
+ *   a:        [T][K/32] Q8_1 blocks, 4-byte aligned (ftq_quantize_q8_1 output).
+ *   topk_ids: int32 [T][top_k], 4-byte aligned.  Ids outside [0, E) give an
+ *             all-zero output row (masking of non-local experts, "Current Bug:
+ *             CuTeDSLMoERunner", Bug 8).  Repeated ids are allowed.
+ *   out:      fp32 [T*top_k][N], row p = t*top_k + j, 4-byte aligned, written.
+ *   workspace: device scratch of at least ftq_moe_workspace_bytes(...) bytes,
+ *             256-byte aligned (may be NULL when that is 0).  Its contents on
+ *             entry do not matter; calls sharing one workspace must not overlap.
+ *   path:     FTQ_PATH_AUTO, FTQ_PATH_GEMV or FTQ_PATH_GROUPED.  Both paths
+ *             compute the same values; each is deterministic and batch
+ *             invariant (a row's bits do not depend on the other rows).
+ * Limits: K % 32 == 0; E, N, top_k >= 1; top_k <= E; T >= 0 (T == 0: no-op);
+ * T*top_k < 2^31.  Output offsets use 64-bit arithmetic throughout.
+ */
+int ftq_moe_q4_0_q8_1(const void* w, const void* a, const int32_t* topk_ids, float* out,
+                      int64_t E, int64_t N, int64_t K, int64_t T, int64_t top_k,
+                      void* workspace, size_t workspace_bytes, int path, hipStream_t stream);
+
+/*
+ * Checking aid: the same computation, but instead of the fp32 outputs it
+ * writes the exact integer block partials
+ *   partials: int32 [T*top_k][N][K/32], P[p][n][b] as defined above
+ * (zeros for masked pairs), produced by the chosen path's own kernels and
+ * index arithmetic.  Same arguments, limits and workspace as above.
+ */
+int ftq_moe_q4_0_q8_1_partials(const void* w, const void* a, const int32_t* topk_ids,
+                               int32_t* partials, int64_t E, int64_t N, int64_t K, int64_t T,
+                               int64_t top_k, void* workspace, size_t workspace_bytes, int path,
+                               hipStream_t stream);
+
+/* Message for the last failing call on this thread ("" if none).  The pointer
+ * stays valid until the next ftq_* call on the same thread. */
+const char* ftq_last_error(void);
+
+/* Library version string, e.g. "ftq 0.1.0 gfx950". */
+const char* ftq_version(void);
+
+/*
+ * Test hook: while `threads` > 0, every launch on this thread asks for
+ * `threads` threads per block, so that a geometry the device rejects can be
+ * exercised from the host.  The library's own pre-launch geometry check turns
+ * it into FTQ_ERR_LAUNCH before anything is enqueued.  0 restores normal
+ * operation.
+ */
+void ftq_debug_force_block_threads(int threads);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* FTQ_H */

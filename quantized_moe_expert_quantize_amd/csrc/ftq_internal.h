@@ -1,0 +1,113 @@
+// Internal declarations shared by the library's translation units: the error
+// channel, device limits, the checked launch helper, and the per-file launch
+// functions that the C entry points call.
+#pragma once
+
+#include <hip/hip_runtime.h>
+
+#include <cstdint>
+#include <cstdio>
+#include <string>
+
+#include "../../include/ftq.h"
+
+namespace ftq {
+
+constexpr int kQK = 32;
+constexpr int kQ4Bytes = 18;
+constexpr int kQ8Bytes = 36;
+
+// Thread-local error text, returned by ftq_last_error().
+void set_error(const char* fmt, ...) __attribute__((format(printf, 1, 2)));
+void clear_error();
+
+// Per-device limits, queried once per device.
+struct DeviceLimits {
+    int device = -1;
+    int64_t max_grid_x = 0;       // blocks along x
+    int64_t max_threads = 0;      // threads per block
+    int64_t max_lds = 0;          // dynamic + static LDS bytes per block
+    int cu_count = 0;
+};
+int device_limits(DeviceLimits* out);   // FTQ_OK or FTQ_ERR_HIP
+
+int forced_block_threads();             // test hook value (0 = off)
+
+// Launch `kernel` with a 1-D grid, after checking the geometry against the
+// device limits, and check the launch right after it is issued.  `name`
+// identifies the kernel in error messages.
+template <typename... KArgs, typename... Args>
+int launch(const char* name, void (*kernel)(KArgs...), int64_t grid, int block, size_t lds,
+           hipStream_t stream, Args... args)
+{
+    DeviceLimits lim;
+    int st = device_limits(&lim);
+    if (st != FTQ_OK) return st;
+    int forced = forced_block_threads();
+    if (forced > 0) block = forced;
+    // AQL packets carry the grid in work-items per dimension as uint32.
+    const int64_t items = grid * (int64_t)block;
+    if (grid < 1 || grid > lim.max_grid_x || block < 1 || block > lim.max_threads ||
+        items > (int64_t)UINT32_MAX || (int64_t)lds > lim.max_lds) {
+        set_error("launch of %s rejected before issue: grid=(%lld,1,1) block=(%d,1,1) lds=%zu B "
+                  "(device %d limits: grid.x<=%lld, block<=%lld, grid*block<=4294967295, lds<=%lld B)",
+                  name, (long long)grid, block, lds, lim.device, (long long)lim.max_grid_x,
+                  (long long)lim.max_threads, (long long)lim.max_lds);
+        return FTQ_ERR_LAUNCH;
+    }
+    (void)hipGetLastError();   // errors of earlier, unrelated calls are not ours to report
+    hipLaunchKernelGGL(kernel, dim3((uint32_t)grid), dim3(block), lds, stream, args...);
+    hipError_t err = hipGetLastError();
+    if (err != hipSuccess) {
+        set_error("launch of %s failed: %s (%s) grid=(%lld,1,1) block=(%d,1,1) lds=%zu B",
+                  name, hipGetErrorName(err), hipGetErrorString(err), (long long)grid, block, lds);
+        return FTQ_ERR_LAUNCH;
+    }
+    return FTQ_OK;
+}
+
+// Number of workgroups for a grid-stride kernel: enough to fill the device
+// several times over, never more than the work needs.
+int64_t stride_grid(int64_t work_groups_needed, const DeviceLimits& lim, int per_cu = 16);
+
+// ---- per-file launchers ------------------------------------------------------
+
+int run_quantize_q8_1(const float* x, int64_t T, int64_t K, void* y, hipStream_t s);
+int run_quantize_q4_0(const float* w, int64_t rows, int64_t K, void* y, hipStream_t s);
+
+// Bucketing of pairs by expert (ids outside [0,E) go to the extra bucket E).
+struct BucketPlan {
+    int64_t pairs = 0;        // T * top_k
+    int64_t buckets = 0;      // E + 1
+    int64_t chunks = 0;       // ceil(pairs / kBucketChunk)
+    int64_t tile_m = 0;       // rows per grouped tile (0: no tile table needed)
+    // byte offsets inside the workspace
+    int64_t off_counts = 0;   // int32 [chunks][buckets]: per-chunk counts, then per-chunk bases
+    int64_t off_offsets = 0;  // int32 [buckets + 1]: start slot of each bucket
+    int64_t off_tiles = 0;    // int32 [buckets + 1]: first tile of each bucket
+    int64_t off_sorted = 0;   // int32 [pairs]: pair ids grouped by bucket, ascending within one
+    int64_t bytes = 0;
+};
+constexpr int kBucketChunk = 1024;   // pairs per wave in the counting and scatter passes
+BucketPlan make_bucket_plan(int64_t pairs, int64_t E, int64_t tile_m);
+int run_bucket(const int32_t* ids, int64_t E, const BucketPlan& plan, void* ws, hipStream_t s);
+
+struct MoeArgs {
+    const void* w;
+    const void* a;
+    const int32_t* ids;
+    float* out;            // fp32 outputs, or
+    int32_t* partials;     // integer partials when non-null
+    int64_t E, N, K, T, top_k;
+};
+
+// GEMV path; `bucketed` selects the pair list from the workspace (else the
+// kernel scans the ids itself).
+int run_gemv(const MoeArgs& m, const BucketPlan* plan, const void* ws, hipStream_t s);
+constexpr int64_t kGemvScanMaxPairs = 4096;
+
+// Grouped MFMA path.
+int run_grouped(const MoeArgs& m, const BucketPlan& plan, const void* ws, hipStream_t s);
+int64_t grouped_tile_m(const MoeArgs& m);
+
+}  // namespace ftq

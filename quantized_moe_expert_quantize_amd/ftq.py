@@ -1,0 +1,175 @@
+"""Thin Python binding of libftq (the C ABI declared in include/ftq.h).
+
+Argument marshalling only: every step of the computation runs in the HIP
+kernels of libftq.so.  PyTorch supplies device memory and the current stream.
+There is no fallback: if the library is missing or the device is not a GPU,
+the calls raise.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import torch
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_PKG, "libftq.so")
+
+OK, ERR_INVALID_ARG, ERR_WORKSPACE, ERR_LAUNCH, ERR_UNSUPPORTED, ERR_HIP = range(6)
+PATH_AUTO, PATH_GEMV, PATH_GROUPED = 0, 1, 2
+QK, Q4_0_BYTES, Q8_1_BYTES = 32, 18, 36
+
+EXPORTS = (
+    "ftq_quantize_q8_1", "ftq_quantize_q4_0", "ftq_moe_select_path", "ftq_moe_workspace_bytes",
+    "ftq_moe_q4_0_q8_1", "ftq_moe_q4_0_q8_1_partials", "ftq_last_error", "ftq_version",
+    "ftq_debug_force_block_threads",
+)
+
+
+class FtqError(RuntimeError):
+    def __init__(self, status: int, message: str):
+        super().__init__(f"ftq status {status}: {message}")
+        self.status = status
+
+
+_lib = None
+
+
+def lib() -> ctypes.CDLL:
+    """Load libftq.so (built in-tree by quantized_moe_expert_quantize_amd.build)."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIB_PATH):
+        raise FtqError(-1, f"{LIB_PATH} is not built; run `python -m quantized_moe_expert_quantize_amd.build`")
+    L = ctypes.CDLL(LIB_PATH)
+    P, I64, I32, SZ = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int, ctypes.c_size_t
+    L.ftq_quantize_q8_1.argtypes = [P, I64, I64, P, P]
+    L.ftq_quantize_q8_1.restype = I32
+    L.ftq_quantize_q4_0.argtypes = [P, I64, I64, P, P]
+    L.ftq_quantize_q4_0.restype = I32
+    L.ftq_moe_select_path.argtypes = [I64, I64, I64, I64, I64]
+    L.ftq_moe_select_path.restype = I32
+    L.ftq_moe_workspace_bytes.argtypes = [I64, I64, I64, I64, I64, I32]
+    L.ftq_moe_workspace_bytes.restype = I64
+    L.ftq_moe_q4_0_q8_1.argtypes = [P, P, P, P, I64, I64, I64, I64, I64, P, SZ, I32, P]
+    L.ftq_moe_q4_0_q8_1.restype = I32
+    L.ftq_moe_q4_0_q8_1_partials.argtypes = [P, P, P, P, I64, I64, I64, I64, I64, P, SZ, I32, P]
+    L.ftq_moe_q4_0_q8_1_partials.restype = I32
+    L.ftq_last_error.restype = ctypes.c_char_p
+    L.ftq_version.restype = ctypes.c_char_p
+    L.ftq_debug_force_block_threads.argtypes = [I32]
+    L.ftq_debug_force_block_threads.restype = None
+    _lib = L
+    return L
+
+
+def last_error() -> str:
+    return lib().ftq_last_error().decode()
+
+
+def version() -> str:
+    return lib().ftq_version().decode()
+
+
+def _check(status: int):
+    if status != OK:
+        raise FtqError(status, last_error())
+
+
+def _stream(stream=None) -> int:
+    s = stream if stream is not None else torch.cuda.current_stream()
+    return s.cuda_stream
+
+
+def _dev(t: torch.Tensor, name: str, dtype=None):
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a GPU tensor")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if dtype is not None and t.dtype != dtype:
+        raise ValueError(f"{name} must be {dtype}, got {t.dtype}")
+    return t.data_ptr()
+
+
+def quantize_q8_1(x: torch.Tensor, out: torch.Tensor | None = None, stream=None) -> torch.Tensor:
+    """fp32 [T, K] -> uint8 [T, K/32*36] Q8_1 blocks."""
+    T, K = x.shape
+    if out is None:
+        out = torch.empty((T, K // QK * Q8_1_BYTES), dtype=torch.uint8, device=x.device)
+    _check(lib().ftq_quantize_q8_1(_dev(x, "x", torch.float32), T, K, _dev(out, "out", torch.uint8), _stream(stream)))
+    return out
+
+
+def quantize_q4_0(w: torch.Tensor, out: torch.Tensor | None = None, stream=None) -> torch.Tensor:
+    """fp32 [..., K] -> uint8 [..., K/32*18] Q4_0 blocks."""
+    K = w.shape[-1]
+    rows = w.numel() // K if K else 0
+    if out is None:
+        out = torch.empty(tuple(w.shape[:-1]) + (K // QK * Q4_0_BYTES,), dtype=torch.uint8, device=w.device)
+    _check(lib().ftq_quantize_q4_0(_dev(w, "w", torch.float32), rows, K, _dev(out, "out", torch.uint8), _stream(stream)))
+    return out
+
+
+def select_path(E: int, N: int, K: int, T: int, top_k: int) -> int:
+    r = lib().ftq_moe_select_path(E, N, K, T, top_k)
+    if r < 0:
+        raise FtqError(-r, last_error())
+    return r
+
+
+def workspace_bytes(E: int, N: int, K: int, T: int, top_k: int, path: int = PATH_AUTO) -> int:
+    r = lib().ftq_moe_workspace_bytes(E, N, K, T, top_k, path)
+    if r < 0:
+        raise FtqError(ERR_INVALID_ARG, last_error())
+    return r
+
+
+def _moe_args(w, a, topk_ids, E, N, K):
+    T, top_k = topk_ids.shape
+    nb = K // QK
+    if w.numel() != E * N * nb * Q4_0_BYTES:
+        raise ValueError("w must hold E*N*(K/32) Q4_0 blocks")
+    if a.numel() != T * nb * Q8_1_BYTES:
+        raise ValueError("a must hold T*(K/32) Q8_1 blocks")
+    return T, top_k
+
+
+def _workspace(ws, need, device):
+    if need == 0:
+        return None, 0
+    if ws is None:
+        ws = torch.empty(need, dtype=torch.uint8, device=device)
+    if ws.numel() < need:
+        raise ValueError(f"workspace needs {need} bytes")
+    return ws, ws.numel()
+
+
+def moe(w: torch.Tensor, a: torch.Tensor, topk_ids: torch.Tensor, E: int, N: int, K: int,
+        path: int = PATH_AUTO, out: torch.Tensor | None = None, workspace: torch.Tensor | None = None,
+        stream=None) -> torch.Tensor:
+    """MoE expert matmul: fp32 out [T*top_k, N]."""
+    T, top_k = _moe_args(w, a, topk_ids, E, N, K)
+    if out is None:
+        out = torch.empty((T * top_k, N), dtype=torch.float32, device=a.device)
+    need = workspace_bytes(E, N, K, T, top_k, path)
+    ws, ws_n = _workspace(workspace, need, a.device)
+    _check(lib().ftq_moe_q4_0_q8_1(
+        _dev(w, "w", torch.uint8), _dev(a, "a", torch.uint8), _dev(topk_ids, "topk_ids", torch.int32),
+        _dev(out, "out", torch.float32), E, N, K, T, top_k,
+        ws.data_ptr() if ws is not None else None, ws_n, path, _stream(stream)))
+    return out
+
+
+def moe_partials(w: torch.Tensor, a: torch.Tensor, topk_ids: torch.Tensor, E: int, N: int, K: int,
+                 path: int = PATH_AUTO, stream=None) -> torch.Tensor:
+    """Exact integer block partials int32 [T*top_k, N, K/32]."""
+    T, top_k = _moe_args(w, a, topk_ids, E, N, K)
+    out = torch.empty((T * top_k, N, K // QK), dtype=torch.int32, device=a.device)
+    need = workspace_bytes(E, N, K, T, top_k, path)
+    ws, ws_n = _workspace(None, need, a.device)
+    _check(lib().ftq_moe_q4_0_q8_1_partials(
+        _dev(w, "w", torch.uint8), _dev(a, "a", torch.uint8), _dev(topk_ids, "topk_ids", torch.int32),
+        _dev(out, "partials", torch.int32), E, N, K, T, top_k,
+        ws.data_ptr() if ws is not None else None, ws_n, path, _stream(stream)))
+    return out

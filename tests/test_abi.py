@@ -1,0 +1,116 @@
+"""The C ABI on the host: the library loads, exports every function that
+include/ftq.h declares, and rejects bad arguments before anything reaches the
+GPU (no call here touches a device)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+from quantized_moe_expert_quantize_amd import ftq
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def _declared():
+    text = open(os.path.join(ROOT, "include", "ftq.h")).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(ftq_[a-z0-9_]+)\s*\(", text)))
+
+
+def test_header_declares_the_binding_exports():
+    assert _declared() == sorted(ftq.EXPORTS)
+
+
+def test_library_exports_every_declared_symbol():
+    L = ftq.lib()
+    for name in _declared():
+        assert hasattr(L, name), name
+        assert ctypes.cast(getattr(L, name), ctypes.c_void_p).value
+
+
+def test_version():
+    assert ftq.version().startswith("ftq ") and "gfx950" in ftq.version()
+
+
+def _moe(L, w=1, a=1, ids=1, out=1, E=8, N=64, K=256, T=4, k=2, ws=None, wsb=0, path=0):
+    P = lambda v: ctypes.c_void_p(v) if v else None
+    return L.ftq_moe_q4_0_q8_1(P(w and 0x1000 * w), P(a and 0x2000 * a), P(ids and 0x3000 * ids),
+                               P(out and 0x4000 * out), E, N, K, T, k, P(ws), wsb, path, None)
+
+
+@pytest.mark.parametrize("kw", [
+    dict(K=250), dict(K=0), dict(K=-32), dict(E=0), dict(N=0), dict(k=0), dict(T=-1),
+    dict(k=9), dict(path=7), dict(w=0), dict(a=0), dict(ids=0), dict(out=0),
+])
+def test_moe_rejects_invalid_arguments(kw):
+    L = ftq.lib()
+    assert _moe(L, **kw) == ftq.ERR_INVALID_ARG
+    assert ftq.last_error()
+
+
+def test_moe_rejects_misaligned_pointers():
+    L = ftq.lib()
+    P = ctypes.c_void_p
+    base = 0x100000
+    args = [P(base), P(base), P(base), P(base)]
+    for i, off in ((0, 1), (1, 2), (2, 2), (3, 2)):
+        bad = list(args)
+        bad[i] = P(base + off)
+        assert L.ftq_moe_q4_0_q8_1(*bad, 8, 64, 256, 4, 2, None, 0, ftq.PATH_GEMV, None) == ftq.ERR_INVALID_ARG
+        assert "misaligned" in ftq.last_error()
+
+
+def test_moe_limits_are_unsupported_not_overflowing():
+    L = ftq.lib()
+    assert _moe(L, T=2 ** 31, k=1, E=1) == ftq.ERR_UNSUPPORTED
+    assert "2^31" in ftq.last_error()
+    assert _moe(L, E=5000, k=2) == ftq.ERR_UNSUPPORTED
+
+
+def test_moe_zero_tokens_is_a_noop():
+    L = ftq.lib()
+    assert _moe(L, T=0, w=0, a=0, ids=0, out=0) == ftq.OK
+    assert ftq.workspace_bytes(8, 64, 256, 0, 2) == 0
+
+
+def test_grouped_needs_workspace():
+    L = ftq.lib()
+    need = ftq.workspace_bytes(8, 64, 256, 64, 2, ftq.PATH_GROUPED)
+    assert need > 0
+    assert _moe(L, T=64, path=ftq.PATH_GROUPED) == ftq.ERR_WORKSPACE
+    assert _moe(L, T=64, path=ftq.PATH_GROUPED, ws=0x100000, wsb=need - 1) == ftq.ERR_WORKSPACE
+    assert _moe(L, T=64, path=ftq.PATH_GROUPED, ws=0x100010, wsb=need) == ftq.ERR_INVALID_ARG  # not 256-aligned
+
+
+def test_path_choice_is_host_arithmetic_of_sizes():
+    # decode sizes take the GEMV path, prefill sizes the grouped MFMA path
+    assert ftq.select_path(8, 14336, 4096, 1, 2) == ftq.PATH_GEMV
+    assert ftq.select_path(8, 14336, 4096, 8, 2) == ftq.PATH_GEMV
+    assert ftq.select_path(8, 14336, 4096, 64, 2) == ftq.PATH_GROUPED
+    assert ftq.select_path(128, 1408, 2816, 1, 8) == ftq.PATH_GEMV
+    for T in (2048, 4096, 8191, 8192, 16384):
+        assert ftq.select_path(128, 1408, 2816, T, 8) == ftq.PATH_GROUPED
+    assert ftq.workspace_bytes(8, 14336, 4096, 1, 2) == 0
+    with pytest.raises(ftq.FtqError):
+        ftq.select_path(8, 14336, 4095, 1, 2)
+
+
+def test_workspace_is_monotone_and_exact_for_bucketing():
+    prev = 0
+    for T in (64, 1000, 4096, 8192, 16384):
+        b = ftq.workspace_bytes(128, 1408, 2816, T, 8, ftq.PATH_GROUPED)
+        assert b >= 4 * T * 8 and b > prev
+        prev = b
+
+
+def test_quantize_rejects_invalid_arguments():
+    L = ftq.lib()
+    P = ctypes.c_void_p
+    assert L.ftq_quantize_q8_1(P(0x1000), 4, 48, P(0x2000), None) == ftq.ERR_INVALID_ARG
+    assert L.ftq_quantize_q8_1(P(0x1004), 4, 64, P(0x2000), None) == ftq.ERR_INVALID_ARG
+    assert L.ftq_quantize_q8_1(None, 4, 64, P(0x2000), None) == ftq.ERR_INVALID_ARG
+    assert L.ftq_quantize_q8_1(None, 0, 64, None, None) == ftq.OK
+    assert L.ftq_quantize_q4_0(P(0x1000), 4, 40, P(0x2000), None) == ftq.ERR_INVALID_ARG
+    assert L.ftq_quantize_q4_0(P(0x1000), 4, 64, P(0x2001), None) == ftq.ERR_INVALID_ARG
+    assert L.ftq_quantize_q4_0(None, 0, 64, None, None) == ftq.OK

@@ -1,0 +1,161 @@
+"""GPU vs oracle parity through the C ABI: quantiser bytes bit-exact, integer
+block partials bit-exact, fp32 outputs within the stated tolerance, for both
+paths, on small shapes that span several tiles and ragged tails."""
+import numpy as np
+import pytest
+import torch
+
+from quantized_moe_expert_quantize_amd import ftq
+from tests._cases import Case, assert_matches_oracle, say
+
+pytestmark = pytest.mark.gpu
+
+PATHS = [ftq.PATH_GEMV, ftq.PATH_GROUPED]
+PATH_NAMES = {ftq.PATH_GEMV: "gemv", ftq.PATH_GROUPED: "grouped", ftq.PATH_AUTO: "auto"}
+
+# (E, N, K, T, top_k, routing)
+SHAPES = {
+    "tiny": (8, 128, 256, 16, 2, "uniform"),               # the tiny workload
+    "ragged_odd_nb": (4, 77, 96, 9, 3, "uniform"),         # K/32 = 3 (odd), N not a tile multiple
+    "one_block": (3, 40, 32, 5, 1, "uniform"),             # K = 32
+    "page1_rows": (16, 200, 2816, 33, 4, "uniform"),       # page-1 hidden size, ragged N
+    "zipf": (32, 160, 512, 300, 8, "zipf"),                # skewed routing: hot and cold experts
+    "many_pairs_per_expert": (4, 136, 384, 200, 2, "uniform"),
+}
+
+
+@pytest.fixture(scope="module", params=list(SHAPES))
+def case(request):
+    E, N, K, T, k, kind = SHAPES[request.param]
+    say(f"[case] {request.param}: E={E} N={N} K={K} T={T} top_k={k} routing={kind}")
+    return Case(E, N, K, T, k, seed=11, kind=kind)
+
+
+def test_quantizers_bit_exact(case):
+    case.assert_same_bytes()
+
+
+@pytest.mark.parametrize("path", PATHS, ids=lambda p: PATH_NAMES[p])
+def test_partials_bit_exact(case, path):
+    got = case.partials(path)
+    ref = case.oracle_partials()
+    assert got.dtype == np.int32 and np.array_equal(got, ref)
+
+
+@pytest.mark.parametrize("path", PATHS + [ftq.PATH_AUTO], ids=lambda p: PATH_NAMES[p])
+def test_outputs_match_oracle(case, path):
+    got = case.run(path).cpu().numpy()
+    ref, ab = case.oracle_out()
+    assert_matches_oracle(got, ref, ab, case.nb)
+
+
+@pytest.mark.parametrize("path", PATHS, ids=lambda p: PATH_NAMES[p])
+def test_deterministic(case, path):
+    a = case.run(path).cpu().numpy()
+    b = case.run(path).cpu().numpy()
+    assert np.array_equal(a.view(np.uint32), b.view(np.uint32))
+
+
+def test_masked_and_duplicate_ids():
+    E, N, K, T, k = 6, 96, 192, 40, 3
+    ids = Case(E, N, K, T, k, seed=3).ids.copy()
+    ids[0, 0] = -1
+    ids[5, 2] = E
+    ids[7, :] = 2**31 - 1
+    ids[9, 1] = ids[9, 0]          # the same expert twice for one token
+    c = Case(E, N, K, T, k, seed=3, ids=ids)
+    ref, ab = c.oracle_out()
+    for path in PATHS:
+        got = c.run(path).cpu().numpy()
+        assert_matches_oracle(got, ref, ab, c.nb)
+        assert not got[0].any() and not got[5 * k + 2].any() and not got[7 * k:8 * k].any()
+        assert np.array_equal(c.partials(path), c.oracle_partials())
+
+
+def test_all_ids_masked_gives_zeros():
+    E, N, K, T, k = 4, 64, 64, 20, 2
+    c = Case(E, N, K, T, k, ids=np.full((T, k), -5, np.int32))
+    for path in PATHS:
+        out = c.run(path)
+        assert not out.any()
+
+
+def test_single_expert_dense_case():
+    c = Case(1, 300, 640, 70, 1, seed=5)
+    ref, ab = c.oracle_out()
+    for path in PATHS:
+        assert_matches_oracle(c.run(path).cpu().numpy(), ref, ab, c.nb)
+
+
+def test_zero_tokens_writes_nothing():
+    c = Case(4, 32, 64, 0, 2)
+    wq, aq, ids = c.gpu()
+    out = torch.full((0, 32), 7.0, device="cuda")
+    ftq.moe(wq, aq, ids, 4, 32, 64, out=out)
+    torch.cuda.synchronize()
+
+
+def test_quantize_q8_1_closed_forms():
+    x = np.zeros((3, 64), np.float32)
+    x[1, :32] = 0.25                           # constant block -> all codes 127
+    x[2, 0] = 127.0                            # d = 1: ties round away from zero
+    x[2, 1:7] = [2.5, -2.5, 0.5, -0.5, 126.5, -3.5]
+    x[2, 40] = -1e-30                          # tiny single value -> -127 with a subnormal-free d
+    got = ftq.quantize_q8_1(torch.from_numpy(x).cuda()).cpu().numpy()
+    import oracle
+    assert np.array_equal(got, oracle.quantize_q8_1(x))
+    q = got.reshape(3, 2, 36)[..., 4:].view(np.int8)
+    assert not got[0].any()
+    assert np.all(q[1, 0] == 127)
+    assert q[2, 0, :7].tolist() == [127, 3, -3, 1, -1, 127, -4]
+
+
+def test_quantize_q8_1_many_rows_and_ragged():
+    for T, K in ((1, 4096), (37, 2816), (1000, 2048), (3, 32)):
+        x = np.random.default_rng(T).standard_normal((T, K)).astype(np.float32) * np.float32(3.0)
+        import oracle
+        got = ftq.quantize_q8_1(torch.from_numpy(x).cuda()).cpu().numpy()
+        assert np.array_equal(got, oracle.quantize_q8_1(x)), (T, K)
+
+
+def test_launch_check_reports_geometry_and_does_not_latch():
+    c = Case(8, 128, 256, 16, 2)
+    wq, aq, ids = c.gpu()
+    good = c.run(ftq.PATH_GEMV)
+    L = ftq.lib()
+    L.ftq_debug_force_block_threads(4096)
+    try:
+        with pytest.raises(ftq.FtqError) as ei:
+            ftq.moe(wq, aq, ids, 8, 128, 256, path=ftq.PATH_GEMV)
+        assert ei.value.status == ftq.ERR_LAUNCH
+        msg = str(ei.value)
+        assert "moe_gemv_kernel" in msg and "block=(4096" in msg and "grid=(" in msg and "lds=" in msg
+    finally:
+        L.ftq_debug_force_block_threads(0)
+    again = c.run(ftq.PATH_GEMV)
+    assert torch.equal(again, good)
+
+
+def test_graph_capture_and_replay():
+    c = Case(16, 256, 512, 96, 4, seed=2)
+    wq, aq, ids = c.gpu()
+    for path in PATHS:
+        eager = c.run(path).clone()
+        out = torch.empty_like(eager)
+        need = ftq.workspace_bytes(16, 256, 512, 96, 4, path)
+        ws = torch.empty(max(need, 1), dtype=torch.uint8, device="cuda")
+        s = torch.cuda.Stream()
+        s.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(s):
+            ftq.moe(wq, aq, ids, 16, 256, 512, path=path, out=out, workspace=ws)   # warm up on the side stream
+        torch.cuda.current_stream().wait_stream(s)
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            ftq.moe(wq, aq, ids, 16, 256, 512, path=path, out=out, workspace=ws)
+        for i in range(4):
+            out.fill_(float("nan"))
+            ws.fill_(0xAB)
+            g.replay()
+            torch.cuda.synchronize()
+            assert torch.equal(out, eager), f"replay {i} differs"
+            _ = (eager * 2).sum().item()      # unrelated eager work between replays
