@@ -26,8 +26,10 @@ BUILD_DIR = os.path.join(ROOT, "_build", "ftq")
 
 ARCH = "gfx950"
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
-# Packed fp32 VALU ops are kept out of generated code on purpose.
-FLAGS = ["-std=c++17", "-O3", "-fPIC", "-Wall", "-Wno-unused-function", f"--offload-arch={ARCH}",
+# Packed fp32 VALU ops are kept out of generated code on purpose.  No implicit
+# contraction: every fused multiply-add in the kernels is written out (fmaf),
+# and a product that feeds an fp16 conversion must round to fp32 first.
+FLAGS = ["-std=c++17", "-O3", "-fPIC", "-ffp-contract=off", "-Wall", "-Wno-unused-function", f"--offload-arch={ARCH}",
          "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops", "-I", INCLUDE]
 
 

@@ -12,9 +12,14 @@ namespace {
 
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 
+// fp32 -> fp16 bits, round to nearest even.  The empty asm pins `f` as an
+// fp32 register value: without it the backend folds a preceding fp32 multiply
+// and this conversion into one v_fma_mix (a single rounding), whereas the
+// format rounds the product to fp32 first and then to fp16.
 __device__ __forceinline__ uint16_t f32_to_f16_bits(float f)
 {
-    _Float16 h = (_Float16)f;   // v_cvt_f16_f32: round to nearest even
+    __asm__ volatile("" : "+v"(f));
+    _Float16 h = (_Float16)f;   // v_cvt_f16_f32
     return __builtin_bit_cast(uint16_t, h);
 }
 

@@ -118,6 +118,31 @@ def test_quantize_q8_1_many_rows_and_ragged():
         assert np.array_equal(got, oracle.quantize_q8_1(x)), (T, K)
 
 
+def _double_rounding_blocks(n=1 << 20, seed=77):
+    """Seeded search (host only) for Q8_1 blocks whose s = d*sum(q) rounds
+    differently when taken to fp16 in one step than via fp32.  The oracle holds
+    the expected bytes; this only finds inputs where a fused conversion would
+    show."""
+    rng = np.random.default_rng(seed)
+    x = (rng.standard_normal((n, 32)) * rng.choice([0.01, 1, 30, 500], size=(n, 1))).astype(np.float32)
+    d = (np.abs(x).max(1) / np.float32(127)).astype(np.float32)
+    r = x / d[:, None]
+    q = np.where(r >= 0, np.floor(r + np.float32(0.5)), np.ceil(r - np.float32(0.5))).astype(np.int64)
+    S = q.sum(1)
+    once = (d.astype(np.float64) * S).astype(np.float16).view(np.uint16)
+    twice = (d * S.astype(np.float32)).astype(np.float16).view(np.uint16)
+    return x[np.nonzero(once != twice)[0]]
+
+
+def test_quantize_q8_1_sum_rounds_via_fp32():
+    import oracle
+    x = _double_rounding_blocks()
+    assert len(x) >= 16
+    x = np.ascontiguousarray(x.reshape(-1, 32))
+    got = ftq.quantize_q8_1(torch.from_numpy(x).cuda()).cpu().numpy()
+    assert np.array_equal(got, oracle.quantize_q8_1(x))
+
+
 def test_launch_check_reports_geometry_and_does_not_latch():
     c = Case(8, 128, 256, 16, 2)
     wq, aq, ids = c.gpu()
