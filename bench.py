@@ -1,0 +1,248 @@
+#!/usr/bin/env python3
+"""Benchmark of the MoE Q4_0 x Q8_1 expert matmul on one MI355X.
+
+One step = the whole hot path over one batch: Q8_1 quantisation of the fp32
+activations, routing (bucketing of the (token, top-k) pairs by expert) and the
+expert matmul, through the C ABI of libftq.  Workload: the FreeToken PR #185
+"Performance" shape (128 experts, nrows N = 1408, hidden K = 2816, top_k = 8)
+at T = 8191 tokens (65528 pairs), seeded synthetic inputs (weights N(0, 0.02),
+activations N(0, 1), uniform distinct routing).  Inputs are resident in HBM
+before timing starts.
+
+    python bench.py [--steps K] [--warmup W] [--T tokens]
+    python bench.py --mode profile         # a short run for rocprofv3
+    python bench.py --summarize-pmc DIR    # HBM traffic from rocprofv3 --pmc runs
+
+Prints one JSON line.  `value` is milliseconds per step (lower is better);
+`roofline` reports the dominant kernel (the grouped MFMA matmul) against the
+int8 MFMA peak using its algorithmic operation count, timed with HIP events
+on the stream it runs on; `cpu_baseline` is the CPU oracle on a bounded
+sample of the same workload.
+"""
+from __future__ import annotations
+
+import argparse
+import glob
+import json
+import os
+import statistics
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "MoE Q4_0xQ8_1 matmul time (ms) + HBM GB/s / int8 MFMA % at T=1..8192, top_k=8"
+WORKLOAD = dict(workload="freetoken_pr185_moe_q4_0", E=128, N=1408, K=2816, top_k=8, routing="uniform", seed=0)
+DEFAULT_T = 8191
+# The pages' own measurement of this workload: the fixed GEMV kernel at 8191
+# tokens on a Tesla T4 (FreeToken PR #185, Performance), the faster of two runs.
+PAGES_MS_T8191 = 705.8
+HBM_PEAK_GBS = 8000.0           # MI355X HBM3E
+INT8_PEAK_TOPS = 5000.0         # MI355X dense int8 MFMA
+DOMINANT = "moe_grouped_kernel"
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "moe_grouped_kernel_page1_T8191_traffic.json")
+
+
+def _lib_hash() -> str:
+    p = os.path.join(ROOT, "quantized_moe_expert_quantize_amd", "libftq.sha256")
+    return open(p).read().strip() if os.path.exists(p) else ""
+
+
+def _algorithmic_bytes(E, N, K, T, k, ids):
+    """Bytes the method must move: the distinct experts' Q4_0 rows, the Q8_1
+    activations, the int32 ids and the fp32 output."""
+    import numpy as np
+    nb = K // 32
+    distinct = len(np.unique(ids[(ids >= 0) & (ids < E)]))
+    return distinct * N * nb * 18 + T * nb * 36 + 4 * T * k + 4 * T * k * N
+
+
+def summarize_pmc(d: str) -> None:
+    """Turn two rocprofv3 --pmc runs (FETCH_SIZE, WRITE_SIZE; KiB per dispatch)
+    into HBM bytes per launch of the dominant kernel, scaled by what the same
+    counters read for a plain copy of known size (bench.py --mode profile runs
+    one: 1 GiB read, 1 GiB written)."""
+    import csv
+    vals = {}
+    for f in glob.glob(os.path.join(d, "**", "*counter_collection.csv"), recursive=True):
+        with open(f) as fh:
+            for row in csv.DictReader(fh):
+                name = row.get("Kernel_Name", "")
+                ctr = row.get("Counter_Name", "")
+                v = float(row.get("Counter_Value", "nan"))
+                kind = "dominant" if DOMINANT in name else ("copy" if "ftq_copy_probe" in name or "copy" in name.lower() else None)
+                if kind is None:
+                    continue
+                vals.setdefault((kind, ctr), []).append(v)
+    out = {}
+    for ctr in ("FETCH_SIZE", "WRITE_SIZE"):
+        dom = vals.get(("dominant", ctr))
+        cp = vals.get(("copy", ctr))
+        if not dom or not cp:
+            continue
+        copy_kib = statistics.median(cp)
+        factor = (1 << 30) / (copy_kib * 1024.0)
+        out[ctr] = dict(kib_per_dispatch=statistics.median(dom), copy_kib=copy_kib, factor=factor,
+                        bytes_per_launch=statistics.median(dom) * 1024.0 * factor)
+    print(json.dumps(out, indent=1))
+
+
+def main() -> None:
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--T", type=int, default=DEFAULT_T)
+    ap.add_argument("--mode", choices=["bench", "profile"], default="bench")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-sample-tokens", type=int, default=2048)
+    ap.add_argument("--summarize-pmc", metavar="DIR")
+    args = ap.parse_args()
+
+    if args.summarize_pmc:
+        summarize_pmc(args.summarize_pmc)
+        return
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print("bench.py: this build measures one GPU only; --gpus N with N > 1 is not supported "
+              "(the pairs shard by expert or by weight rows across GPUs, but no multi-GPU path is built)",
+              file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    from quantized_moe_expert_quantize_amd import ftq, inputs
+
+    E, N, K, k = WORKLOAD["E"], WORKLOAD["N"], WORKLOAD["K"], WORKLOAD["top_k"]
+    T = args.T
+    seed = WORKLOAD["seed"]
+    torch.cuda.set_device(0)
+    dev = torch.device("cuda", 0)
+
+    # ---- inputs, resident in HBM --------------------------------------------
+    w32 = inputs.weights(E, N, K, seed=seed)
+    x32 = inputs.activations(T, K, seed=seed)
+    ids = inputs.routing(T, E, k, seed=seed, kind=WORKLOAD["routing"])
+    wdev = torch.from_numpy(w32).to(dev)
+    wq = ftq.quantize_q4_0(wdev)
+    del wdev
+    x = torch.from_numpy(x32).to(dev)
+    ids_d = torch.from_numpy(ids).to(dev)
+    path = ftq.select_path(E, N, K, T, k)
+    aq = torch.empty((T, K // 32 * 36), dtype=torch.uint8, device=dev)
+    out = torch.empty((T * k, N), dtype=torch.float32, device=dev)
+    need = ftq.workspace_bytes(E, N, K, T, k, path)
+    ws = torch.empty(max(need, 256), dtype=torch.uint8, device=dev) if need else None
+    torch.cuda.synchronize()
+
+    ev = lambda: torch.cuda.Event(enable_timing=True)
+
+    def step(marks=None):
+        if marks:
+            marks[0].record()
+        ftq.quantize_q8_1(x, out=aq)
+        if marks:
+            marks[1].record()
+        ftq.moe_route(ids_d, E, ws, path)
+        if marks:
+            marks[2].record()
+        ftq.moe_routed(wq, aq, ids_d, E, N, K, out, ws, path)
+        if marks:
+            marks[3].record()
+
+    steps = 3 if args.mode == "profile" else args.steps
+    warmup = 2 if args.mode == "profile" else args.warmup
+    for _ in range(warmup):
+        step()
+    torch.cuda.synchronize()
+
+    # ---- timed region: exactly `steps` steps --------------------------------
+    marks = [[ev() for _ in range(4)] for _ in range(steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(steps):
+        step(marks[i])
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    ms_per_step = (t1 - t0) * 1e3 / steps
+    q_ms = statistics.mean(m[0].elapsed_time(m[1]) for m in marks)
+    r_ms = statistics.mean(m[1].elapsed_time(m[2]) for m in marks)
+    mm_ms = statistics.mean(m[2].elapsed_time(m[3]) for m in marks)
+
+    if args.mode == "profile":
+        # plain copy of known size for counter calibration: 1 GiB read, 1 GiB written
+        src = torch.ones(1 << 28, dtype=torch.float32, device=dev)
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            torch.mul(src, 1.0, out=dst)
+        torch.cuda.synchronize()
+        print(json.dumps({"mode": "profile", "ms_per_step": ms_per_step, "matmul_ms": mm_ms, "path": path}))
+        return
+
+    # ---- roofline of the dominant kernel ------------------------------------
+    pairs = T * k
+    ops = 2.0 * pairs * N * K
+    alg_bytes = _algorithmic_bytes(E, N, K, T, k, ids)
+    kern_s = mm_ms / 1e3
+    tops = ops / kern_s / 1e12
+    gbs = alg_bytes / kern_s / 1e9
+    traffic = None
+    if os.path.exists(TRAFFIC_FILE):
+        rec = json.load(open(TRAFFIC_FILE))
+        if rec.get("lib_sha256") == _lib_hash() and rec.get("T") == T:
+            traffic = rec.get("bytes_per_launch")
+    if path == ftq.PATH_GROUPED:
+        roofline = {"bound": "mfma", "achieved": round(tops, 2), "peak": INT8_PEAK_TOPS, "unit": "TOP/s",
+                    "frac": round(tops / INT8_PEAK_TOPS, 4), "traffic": traffic,
+                    "kernel": "moe_grouped_kernel (int8 MFMA)", "kernel_ms": round(mm_ms, 4),
+                    "ops_per_launch": ops, "alg_bytes_per_launch": alg_bytes,
+                    "hbm_gbs": round(gbs, 1), "hbm_frac": round(gbs / HBM_PEAK_GBS, 4)}
+    else:
+        roofline = {"bound": "hbm", "achieved": round(gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                    "frac": round(gbs / HBM_PEAK_GBS, 4), "traffic": traffic,
+                    "kernel": "moe_gemv_kernel", "kernel_ms": round(mm_ms, 4),
+                    "alg_bytes_per_launch": alg_bytes, "ops_per_launch": ops}
+
+    # ---- CPU oracle on a bounded sample of the same workload ----------------
+    cpu = None
+    if not args.no_cpu_baseline:
+        import oracle
+        ts = min(args.cpu_sample_tokens, T)
+        ow = oracle.quantize_q4_0(w32).reshape(-1)       # weight preparation: not part of a step
+        c0 = time.perf_counter()
+        oa = oracle.quantize_q8_1(x32[:ts]).reshape(-1)
+        oracle.moe(ow, oa, np.ascontiguousarray(ids[:ts]), E, N, K, ts, k)
+        c1 = time.perf_counter()
+        cpu = {"value": round((c1 - c0) * 1e3 * T / ts, 1), "unit": "ms", "cores": oracle.num_threads(),
+               "kind": "oracle",
+               "sample": f"Q8_1 quantisation + matmul of the first {ts} of {T} tokens ({ts * k} of {pairs} pairs), "
+                         f"{(c1 - c0):.1f} s measured, scaled by {T}/{ts} to one step"}
+
+    result = {
+        "metric": METRIC,
+        "value": round(ms_per_step, 4),
+        "unit": "ms",
+        "n_gpus": 1,
+        "steps": steps,
+        "warmup": warmup,
+        "ms_per_step": round(ms_per_step, 4),
+        "higher_is_better": False,
+        "scaling": "weak",
+        "vs_baseline": round(ms_per_step / PAGES_MS_T8191, 6) if T == DEFAULT_T else None,
+        "dtype": "q4_0 x q8_1 (int8 MFMA, fp32 accumulate)",
+        "data": "synthetic",
+        "config": dict(WORKLOAD, T=T, pairs=pairs, path={1: "gemv", 2: "grouped"}[path]),
+        "breakdown_ms": {"quantize_q8_1": round(q_ms, 4), "route": round(r_ms, 4), "matmul": round(mm_ms, 4)},
+        "throughput": {"tokens_per_s": round(T / (ms_per_step / 1e3), 1), "matmul_TOPS": round(tops, 2),
+                       "matmul_alg_GBps": round(gbs, 1)},
+        "roofline": roofline,
+        "cpu_baseline": cpu,
+        "lib_sha256": _lib_hash()[:16],
+    }
+    print(json.dumps(result))
+
+
+if __name__ == "__main__":
+    main()

@@ -130,6 +130,29 @@ int ftq_moe_q4_0_q8_1(const void* w, const void* a, const int32_t* topk_ids, flo
                       void* workspace, size_t workspace_bytes, int path, hipStream_t stream);
 
 /*
+ * The same matmul split in two, so that one routing can serve several matmuls
+ * over the same (token, top-k) pairs (e.g. an expert FFN's up- and
+ * down-projections) and each half can be timed on its own.
+ *
+ * ftq_moe_route: groups the pairs by routed expert into `workspace` (per-expert
+ *   counts, segment offsets, tile table and the sorted pair list: the
+ *   expert-sorted layout of "Current Bug: CuTeDSLMoERunner", Key Architecture,
+ *   built on the device without any host readback).  The workspace size and
+ *   path are those of ftq_moe_workspace_bytes / ftq_moe_q4_0_q8_1 for the same
+ *   E, T, top_k (they do not depend on N or K).  A path that needs no
+ *   workspace makes this a no-op.
+ * ftq_moe_q4_0_q8_1_routed: the matmul on pairs routed by ftq_moe_route with
+ *   the same topk_ids, E, T, top_k, path and workspace, enqueued after it.
+ *   Arguments and results are exactly those of ftq_moe_q4_0_q8_1.
+ */
+int ftq_moe_route(const int32_t* topk_ids, int64_t E, int64_t T, int64_t top_k, void* workspace,
+                  size_t workspace_bytes, int path, hipStream_t stream);
+
+int ftq_moe_q4_0_q8_1_routed(const void* w, const void* a, const int32_t* topk_ids, float* out,
+                             int64_t E, int64_t N, int64_t K, int64_t T, int64_t top_k,
+                             void* workspace, size_t workspace_bytes, int path, hipStream_t stream);
+
+/*
  * Checking aid: the same computation, but instead of the fp32 outputs it
  * writes the exact integer block partials
  *   partials: int32 [T*top_k][N][K/32], P[p][n][b] as defined above

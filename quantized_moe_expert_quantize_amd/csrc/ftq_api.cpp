@@ -131,9 +131,22 @@ int resolve_path(int path, int64_t E, int64_t T, int64_t top_k)
     return -1;
 }
 
+int check_workspace(const BucketPlan& plan, const void* ws, size_t ws_bytes)
+{
+    if (!ws || (int64_t)ws_bytes < plan.bytes) {
+        set_error("workspace of %zu bytes is smaller than the %lld bytes needed", ws_bytes, (long long)plan.bytes);
+        return FTQ_ERR_WORKSPACE;
+    }
+    if (!aligned(ws, 256)) { set_error("workspace must be 256-byte aligned"); return FTQ_ERR_INVALID_ARG; }
+    return FTQ_OK;
+}
+
+// kRoute: bucketing only; kMatmul: matmul only (pairs already routed); both: the full call.
+enum Phase { kRoute = 1, kMatmul = 2 };
+
 int moe_common(const void* w, const void* a, const int32_t* ids, float* out, int32_t* partials,
                int64_t E, int64_t N, int64_t K, int64_t T, int64_t top_k, void* ws, size_t ws_bytes,
-               int path, hipStream_t stream)
+               int path, hipStream_t stream, int phases)
 {
     clear_error();
     int st = check_sizes(E, N, K, T, top_k);
@@ -141,22 +154,26 @@ int moe_common(const void* w, const void* a, const int32_t* ids, float* out, int
     const int rp = resolve_path(path, E, T, top_k);
     if (rp < 0) { set_error("unknown path %d", path); return FTQ_ERR_INVALID_ARG; }
     if (T == 0) return FTQ_OK;
-    if (!w || !a || !ids || (!out && !partials)) { set_error("null pointer argument (w, a, topk_ids or the output)"); return FTQ_ERR_INVALID_ARG; }
-    if (!aligned(w, 2) || !aligned(a, 4) || !aligned(ids, 4) || !aligned(out ? (const void*)out : (const void*)partials, 4)) {
+    if (!ids || ((phases & kMatmul) && (!w || !a || (!out && !partials)))) {
+        set_error("null pointer argument (w, a, topk_ids or the output)");
+        return FTQ_ERR_INVALID_ARG;
+    }
+    if (!aligned(ids, 4) || ((phases & kMatmul) &&
+        (!aligned(w, 2) || !aligned(a, 4) || !aligned(out ? (const void*)out : (const void*)partials, 4)))) {
         set_error("misaligned pointer (w needs 2-byte, a/topk_ids/out 4-byte alignment)");
         return FTQ_ERR_INVALID_ARG;
     }
     bool bucketed = false;
     const BucketPlan plan = plan_for(rp, E, N, K, T, top_k, &bucketed);
     if (bucketed) {
-        if (!ws || (int64_t)ws_bytes < plan.bytes) {
-            set_error("workspace of %zu bytes is smaller than the %lld bytes needed", ws_bytes, (long long)plan.bytes);
-            return FTQ_ERR_WORKSPACE;
-        }
-        if (!aligned(ws, 256)) { set_error("workspace must be 256-byte aligned"); return FTQ_ERR_INVALID_ARG; }
-        st = run_bucket(ids, E, plan, ws, stream);
+        st = check_workspace(plan, ws, ws_bytes);
         if (st != FTQ_OK) return st;
+        if (phases & kRoute) {
+            st = run_bucket(ids, E, plan, ws, stream);
+            if (st != FTQ_OK) return st;
+        }
     }
+    if (!(phases & kMatmul)) return FTQ_OK;
     MoeArgs m{w, a, ids, out, partials, E, N, K, T, top_k};
     if (rp == FTQ_PATH_GEMV) return run_gemv(m, bucketed ? &plan : nullptr, ws, stream);
     return run_grouped(m, plan, ws, stream);
@@ -215,14 +232,32 @@ int ftq_moe_q4_0_q8_1(const void* w, const void* a, const int32_t* topk_ids, flo
                       int64_t N, int64_t K, int64_t T, int64_t top_k, void* workspace,
                       size_t workspace_bytes, int path, hipStream_t stream)
 {
-    return moe_common(w, a, topk_ids, out, nullptr, E, N, K, T, top_k, workspace, workspace_bytes, path, stream);
+    return moe_common(w, a, topk_ids, out, nullptr, E, N, K, T, top_k, workspace, workspace_bytes, path, stream,
+                      kRoute | kMatmul);
+}
+
+int ftq_moe_route(const int32_t* topk_ids, int64_t E, int64_t T, int64_t top_k, void* workspace,
+                  size_t workspace_bytes, int path, hipStream_t stream)
+{
+    // N and K do not enter the routing; any valid values pass the size checks
+    return moe_common(nullptr, nullptr, topk_ids, nullptr, nullptr, E, 1, kQK, T, top_k, workspace,
+                      workspace_bytes, path, stream, kRoute);
+}
+
+int ftq_moe_q4_0_q8_1_routed(const void* w, const void* a, const int32_t* topk_ids, float* out, int64_t E,
+                             int64_t N, int64_t K, int64_t T, int64_t top_k, void* workspace,
+                             size_t workspace_bytes, int path, hipStream_t stream)
+{
+    return moe_common(w, a, topk_ids, out, nullptr, E, N, K, T, top_k, workspace, workspace_bytes, path, stream,
+                      kMatmul);
 }
 
 int ftq_moe_q4_0_q8_1_partials(const void* w, const void* a, const int32_t* topk_ids, int32_t* partials,
                                int64_t E, int64_t N, int64_t K, int64_t T, int64_t top_k,
                                void* workspace, size_t workspace_bytes, int path, hipStream_t stream)
 {
-    return moe_common(w, a, topk_ids, nullptr, partials, E, N, K, T, top_k, workspace, workspace_bytes, path, stream);
+    return moe_common(w, a, topk_ids, nullptr, partials, E, N, K, T, top_k, workspace, workspace_bytes, path, stream,
+                      kRoute | kMatmul);
 }
 
 const char* ftq_last_error(void) { return g_error.c_str(); }

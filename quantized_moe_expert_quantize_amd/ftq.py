@@ -21,7 +21,8 @@ QK, Q4_0_BYTES, Q8_1_BYTES = 32, 18, 36
 
 EXPORTS = (
     "ftq_quantize_q8_1", "ftq_quantize_q4_0", "ftq_moe_select_path", "ftq_moe_workspace_bytes",
-    "ftq_moe_q4_0_q8_1", "ftq_moe_q4_0_q8_1_partials", "ftq_last_error", "ftq_version",
+    "ftq_moe_q4_0_q8_1", "ftq_moe_route", "ftq_moe_q4_0_q8_1_routed", "ftq_moe_q4_0_q8_1_partials",
+    "ftq_last_error", "ftq_version",
     "ftq_debug_force_block_threads",
 )
 
@@ -54,6 +55,10 @@ def lib() -> ctypes.CDLL:
     L.ftq_moe_workspace_bytes.restype = I64
     L.ftq_moe_q4_0_q8_1.argtypes = [P, P, P, P, I64, I64, I64, I64, I64, P, SZ, I32, P]
     L.ftq_moe_q4_0_q8_1.restype = I32
+    L.ftq_moe_route.argtypes = [P, I64, I64, I64, P, SZ, I32, P]
+    L.ftq_moe_route.restype = I32
+    L.ftq_moe_q4_0_q8_1_routed.argtypes = [P, P, P, P, I64, I64, I64, I64, I64, P, SZ, I32, P]
+    L.ftq_moe_q4_0_q8_1_routed.restype = I32
     L.ftq_moe_q4_0_q8_1_partials.argtypes = [P, P, P, P, I64, I64, I64, I64, I64, P, SZ, I32, P]
     L.ftq_moe_q4_0_q8_1_partials.restype = I32
     L.ftq_last_error.restype = ctypes.c_char_p
@@ -158,6 +163,28 @@ def moe(w: torch.Tensor, a: torch.Tensor, topk_ids: torch.Tensor, E: int, N: int
         _dev(w, "w", torch.uint8), _dev(a, "a", torch.uint8), _dev(topk_ids, "topk_ids", torch.int32),
         _dev(out, "out", torch.float32), E, N, K, T, top_k,
         ws.data_ptr() if ws is not None else None, ws_n, path, _stream(stream)))
+    return out
+
+
+def moe_route(topk_ids: torch.Tensor, E: int, workspace: torch.Tensor | None, path: int = PATH_AUTO,
+              stream=None) -> None:
+    """Group the pairs by expert into `workspace` (see ftq_moe_route)."""
+    T, top_k = topk_ids.shape
+    ws_n = workspace.numel() if workspace is not None else 0
+    _check(lib().ftq_moe_route(_dev(topk_ids, "topk_ids", torch.int32), E, T, top_k,
+                               workspace.data_ptr() if workspace is not None else None, ws_n, path,
+                               _stream(stream)))
+
+
+def moe_routed(w: torch.Tensor, a: torch.Tensor, topk_ids: torch.Tensor, E: int, N: int, K: int,
+               out: torch.Tensor, workspace: torch.Tensor | None, path: int = PATH_AUTO, stream=None) -> torch.Tensor:
+    """The matmul on pairs already routed into `workspace` by moe_route."""
+    T, top_k = _moe_args(w, a, topk_ids, E, N, K)
+    ws_n = workspace.numel() if workspace is not None else 0
+    _check(lib().ftq_moe_q4_0_q8_1_routed(
+        _dev(w, "w", torch.uint8), _dev(a, "a", torch.uint8), _dev(topk_ids, "topk_ids", torch.int32),
+        _dev(out, "out", torch.float32), E, N, K, T, top_k,
+        workspace.data_ptr() if workspace is not None else None, ws_n, path, _stream(stream)))
     return out
 
 

@@ -184,3 +184,22 @@ def test_graph_capture_and_replay():
             torch.cuda.synchronize()
             assert torch.equal(out, eager), f"replay {i} differs"
             _ = (eager * 2).sum().item()      # unrelated eager work between replays
+
+
+@pytest.mark.parametrize("path", PATHS + [ftq.PATH_AUTO], ids=lambda p: PATH_NAMES[p])
+def test_route_then_routed_equals_one_call(path):
+    c = Case(16, 200, 512, 150, 4, seed=8, kind="zipf")
+    wq, aq, ids = c.gpu()
+    one = c.run(path)
+    need = ftq.workspace_bytes(16, 200, 512, 150, 4, path)
+    ws = torch.empty(max(need, 1), dtype=torch.uint8, device="cuda") if need else None
+    ftq.moe_route(ids, 16, ws, path)
+    out = torch.empty_like(one)
+    ftq.moe_routed(wq, aq, ids, 16, 200, 512, out, ws, path)
+    # a second matmul over the same routing (another weight set, same pairs)
+    w2 = ftq.quantize_q4_0(torch.from_numpy(c.w32[::-1].copy()).cuda())
+    out2 = torch.empty_like(one)
+    ftq.moe_routed(w2, aq, ids, 16, 200, 512, out2, ws, path)
+    ref2 = ftq.moe(w2, aq, ids, 16, 200, 512, path=path)
+    torch.cuda.synchronize()
+    assert torch.equal(out, one) and torch.equal(out2, ref2)
