@@ -71,7 +71,8 @@ def summarize_pmc(d: str) -> None:
                 name = row.get("Kernel_Name", "")
                 ctr = row.get("Counter_Name", "")
                 v = float(row.get("Counter_Value", "nan"))
-                kind = "dominant" if DOMINANT in name else ("copy" if "ftq_copy_probe" in name or "copy" in name.lower() else None)
+                # the calibration kernel is torch's x * 1.0 over 1 GiB (bench.py --mode profile)
+                kind = "dominant" if DOMINANT in name else ("copy" if "AUnaryFunctor" in name else None)
                 if kind is None:
                     continue
                 vals.setdefault((kind, ctr), []).append(v)
@@ -85,6 +86,9 @@ def summarize_pmc(d: str) -> None:
         factor = (1 << 30) / (copy_kib * 1024.0)
         out[ctr] = dict(kib_per_dispatch=statistics.median(dom), copy_kib=copy_kib, factor=factor,
                         bytes_per_launch=statistics.median(dom) * 1024.0 * factor)
+    fetch, write = out.get("FETCH_SIZE"), out.get("WRITE_SIZE")
+    if fetch and write:
+        out["bytes_per_launch"] = fetch["bytes_per_launch"] + write["bytes_per_launch"]
     print(json.dumps(out, indent=1))
 
 
