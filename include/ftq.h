@@ -137,10 +137,10 @@ int ftq_moe_q4_0_q8_1(const void* w, const void* a, const int32_t* topk_ids, flo
  * ftq_moe_route: groups the pairs by routed expert into `workspace` (per-expert
  *   counts, segment offsets, tile table and the sorted pair list: the
  *   expert-sorted layout of "Current Bug: CuTeDSLMoERunner", Key Architecture,
- *   built on the device without any host readback).  The workspace size and
- *   path are those of ftq_moe_workspace_bytes / ftq_moe_q4_0_q8_1 for the same
- *   E, T, top_k (they do not depend on N or K).  A path that needs no
- *   workspace makes this a no-op.
+ *   built on the device without any host readback).  Pass the workspace and
+ *   path that the matmul will use (ftq_moe_workspace_bytes with the matmul's
+ *   N and K; the routing itself uses only its leading part, which depends on
+ *   E, T and top_k alone).  A path that needs no workspace makes this a no-op.
  * ftq_moe_q4_0_q8_1_routed: the matmul on pairs routed by ftq_moe_route with
  *   the same topk_ids, E, T, top_k, path and workspace, enqueued after it.
  *   Arguments and results are exactly those of ftq_moe_q4_0_q8_1.

@@ -131,10 +131,10 @@ int resolve_path(int path, int64_t E, int64_t T, int64_t top_k)
     return -1;
 }
 
-int check_workspace(const BucketPlan& plan, const void* ws, size_t ws_bytes)
+int check_workspace(int64_t need, const void* ws, size_t ws_bytes)
 {
-    if (!ws || (int64_t)ws_bytes < plan.bytes) {
-        set_error("workspace of %zu bytes is smaller than the %lld bytes needed", ws_bytes, (long long)plan.bytes);
+    if (!ws || (int64_t)ws_bytes < need) {
+        set_error("workspace of %zu bytes is smaller than the %lld bytes needed", ws_bytes, (long long)need);
         return FTQ_ERR_WORKSPACE;
     }
     if (!aligned(ws, 256)) { set_error("workspace must be 256-byte aligned"); return FTQ_ERR_INVALID_ARG; }
@@ -166,7 +166,9 @@ int moe_common(const void* w, const void* a, const int32_t* ids, float* out, int
     bool bucketed = false;
     const BucketPlan plan = plan_for(rp, E, N, K, T, top_k, &bucketed);
     if (bucketed) {
-        st = check_workspace(plan, ws, ws_bytes);
+        // routing alone needs the bucket tables; the grouped matmul also stages activations
+        const int64_t need = plan.bytes + ((phases & kMatmul) && rp == FTQ_PATH_GROUPED ? grouped_prep_bytes(T, K) : 0);
+        st = check_workspace(need, ws, ws_bytes);
         if (st != FTQ_OK) return st;
         if (phases & kRoute) {
             st = run_bucket(ids, E, plan, ws, stream);
@@ -225,7 +227,8 @@ int64_t ftq_moe_workspace_bytes(int64_t E, int64_t N, int64_t K, int64_t T, int6
     if (T == 0) return 0;
     bool bucketed = false;
     const BucketPlan plan = plan_for(rp, E, N, K, T, top_k, &bucketed);
-    return bucketed ? plan.bytes : 0;
+    if (!bucketed) return 0;
+    return plan.bytes + (rp == FTQ_PATH_GROUPED ? grouped_prep_bytes(T, K) : 0);
 }
 
 int ftq_moe_q4_0_q8_1(const void* w, const void* a, const int32_t* topk_ids, float* out, int64_t E,

@@ -9,7 +9,7 @@
 #include <cstdio>
 #include <string>
 
-#include "../../include/ftq.h"
+#include "ftq.h"
 
 namespace ftq {
 
@@ -106,8 +106,10 @@ struct MoeArgs {
 int run_gemv(const MoeArgs& m, const BucketPlan* plan, const void* ws, hipStream_t s);
 constexpr int64_t kGemvScanMaxPairs = 4096;
 
-// Grouped MFMA path.
-int run_grouped(const MoeArgs& m, const BucketPlan& plan, const void* ws, hipStream_t s);
+// Grouped MFMA path.  Its workspace is the bucket plan's bytes followed by
+// grouped_prep_bytes(T, K) of per-call activation staging.
+int run_grouped(const MoeArgs& m, const BucketPlan& plan, void* ws, hipStream_t s);
 int64_t grouped_tile_m(const MoeArgs& m);
+int64_t grouped_prep_bytes(int64_t T, int64_t K);
 
 }  // namespace ftq

@@ -1,46 +1,71 @@
-// Grouped path of the MoE expert matmul: expert-sorted tiles on int8 MFMA.
+// Grouped path of the MoE expert matmul: expert-sorted tiles on the matrix cores.
 //
 // After bucketing, the pairs routed to expert e occupy one contiguous segment
-// of the sorted pair list.  Each workgroup computes one BM x BN output tile:
+// of the sorted pair list.  Each workgroup computes one BM x 128 output tile:
 // BM pairs of one expert (a tile never straddles two experts; the last tile of
 // an expert is ragged and its missing rows are masked, not padded in memory)
-// against BN weight rows of that expert.  Prior art for this layout is the
+// against 128 weight rows of that expert.  Prior art for this layout is the
 // expert-sorted grouped GEMM of "Current Bug: CuTeDSLMoERunner" (Key
 // Architecture: Fixed-Layout Padding; Bugs 2 and 4 for the tile -> expert
-// lookup, done here as an upper-bound search over per-expert tile offsets);
-// the tiles themselves are gfx950-native:
-//   * K advances one 32-value quantisation block per v_mfma_i32_32x32x32_i8,
-//     so each MFMA produces exactly the integer block partials P (exact int32);
-//   * the Q4_0 nibbles are unpacked to signed bytes (q - 8) in registers while
-//     the tile is staged to LDS; Q8_1 codes are gathered per pair row;
-//   * per block the fp32 accumulator takes one FMA with the exact product of
-//     the two fp16 scales: acc = fma(float(P), d4*d8, acc), blocks ascending.
-//     The arithmetic per output element depends only on K, never on where the
-//     pair sits in a tile, so results are batch invariant.
-// The grid is a flat x axis over (M tile, N tile) with a grid-stride loop and
-// 64-bit offsets; tiles past the device-side tile count exit at once.
+// lookup, done here as an upper-bound search over per-expert tile offsets).
+//
+// Arithmetic, exact at every step.  Per output element and quantisation block b
+// the result needs the integer partial P_b = sum_i (q4-8)*q8 and the scale
+// product d4*d8.  On gfx950 both come from the matrix cores:
+//   * P_b: two v_mfma_f32_32x32x16_f16 over the block's 32 values.  The Q8_1
+//     codes (|q| <= 127) and the Q4_0 values (q-8 in [-8, 7]) are exact in
+//     fp16, every product is an exact small integer and every partial sum stays
+//     below 2^24, so the fp32 result is P_b exactly, in any summation order;
+//   * d4*d8: one more f16 MFMA used as an outer product (only k = 0 non-zero);
+//     a product of two fp16 values is exact in fp32;
+//   * the vector ALUs then do a single fp32 FMA per element and block:
+//     acc = fma(P_b, d4*d8, acc), blocks in ascending order.
+// Doing the products on the MFMA units leaves one VALU op per element-block,
+// instead of three (int->float convert, scale multiply, FMA) after an int8 MFMA.
+// The per-element arithmetic does not depend on where a pair sits in a tile,
+// so results are batch invariant.
+//
+// Operands.  The activations are converted once per call by
+// prep_activations_kernel into fp16 codes (64 B per block) plus fp16 scales;
+// the weight nibbles are unpacked to fp16 while a tile is staged into LDS, in a
+// block-internal k order chosen so that each 32-bit word of nibbles yields
+// four packed fp16 pairs with one mask-or and one packed add each; the
+// activation codes are written in that same order, so the dot products match.
+// Tiles are double buffered in LDS (loads for block pair s+1 are in flight while
+// block pair s is multiplied).  Workgroups are mapped to tiles XCD by XCD: each
+// of the 8 XCDs takes a contiguous range of tiles, walked in groups of kGroupM
+// M tiles with the N tiles inner, so a gathered activation tile and an expert's
+// weight tiles are reused from that XCD's L2.
+#include <type_traits>
+
 #include "ftq_internal.h"
 
 namespace ftq {
 namespace {
 
-typedef int v4i __attribute__((ext_vector_type(4)));
-typedef int v16i __attribute__((ext_vector_type(16)));
+typedef _Float16 v8h __attribute__((ext_vector_type(8)));
+typedef _Float16 h2 __attribute__((ext_vector_type(2)));
+typedef float v16f __attribute__((ext_vector_type(16)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
 constexpr int kThreads = 256;
-constexpr int kBN = 128;        // weight rows per tile
-constexpr int kKB = 4;          // quantisation blocks staged per pass
-constexpr int kCodeStride = kKB * 32 + 16;   // LDS bytes per staged row of codes
+constexpr int kBN = 128;          // weight rows per tile
+constexpr int kKB = 2;            // quantisation blocks per staged pass
+constexpr int kBlockF16 = 64;     // bytes of one block's 32 fp16 codes
+constexpr int kRowBytes = kKB * kBlockF16 + 16;   // LDS bytes per staged row (+16: bank skew)
+constexpr int kXcds = 8;
+constexpr int kGroupM = 4;
 
 struct GroupedParams {
     const uint8_t* w;
-    const uint8_t* a;
+    const uint8_t* a16;       // [T][nb][64 B] fp16 codes in the block-internal order
+    const uint16_t* d8;       // [T][nb] fp16 scale bits
     float* out;
     int32_t* partials;
     const int32_t* offsets;   // [E+2]
     const int32_t* tiles;     // [E+2]
     const int32_t* sorted;
-    int64_t E, N, nb, top_k, nbuckets, n_tiles_n, work;   // work = max M tiles * N tiles
+    int64_t E, N, nb, top_k, nbuckets, n_tiles_n, max_mt;
 };
 
 template <int BM>
@@ -52,57 +77,104 @@ struct Shape {
     static_assert(SM >= 1 && SN >= 1, "tile shape");
 };
 
-__device__ __forceinline__ float half_bits_to_float(uint32_t bits)
+template <int BM>
+struct Smem {
+    uint8_t a[2][BM * kRowBytes];
+    uint8_t b[2][kBN * kRowBytes];
+    uint32_t as[2][kKB][BM];    // fp16 scale bits of A rows (upper half zero)
+    uint32_t bs[2][kKB][kBN + 1];   // fp16 scale bits of weight rows; entry kBN stays 0
+    int32_t row_pair[BM];
+    int32_t row_tok[BM];
+};
+
+// Four packed fp16 pairs (q - 8) from one word of eight Q4_0 nibbles.  Word j of
+// a block holds elements 4j..4j+3 in its low nibbles and 16+4j..16+4j+3 in its
+// high nibbles; the outputs are the pairs (4j, 4j+2), (4j+1, 4j+3),
+// (16+4j, 16+4j+2), (16+4j+1, 16+4j+3).  0x6400 | q is the fp16 1024 + q.
+__device__ __forceinline__ void nibbles_to_f16(uint32_t x, uint32_t o[4])
 {
-    return (float)__builtin_bit_cast(_Float16, (uint16_t)bits);
+    const h2 bias = {(_Float16)-1032.0f, (_Float16)-1032.0f};
+    const uint32_t t0 = (x & 0x000f000fu) | 0x64006400u;
+    const uint32_t t1 = ((x >> 8) & 0x000f000fu) | 0x64006400u;
+    const uint32_t t2 = ((x >> 4) & 0x000f000fu) | 0x64006400u;
+    const uint32_t t3 = ((x >> 12) & 0x000f000fu) | 0x64006400u;
+    o[0] = __builtin_bit_cast(uint32_t, __builtin_bit_cast(h2, t0) + bias);
+    o[1] = __builtin_bit_cast(uint32_t, __builtin_bit_cast(h2, t1) + bias);
+    o[2] = __builtin_bit_cast(uint32_t, __builtin_bit_cast(h2, t2) + bias);
+    o[3] = __builtin_bit_cast(uint32_t, __builtin_bit_cast(h2, t3) + bias);
 }
 
-// Signed codes q - 8 for four nibbles held one per byte (values 0..15): set the
-// top bit so the byte-wise subtract cannot borrow, then clear it again.
-__device__ __forceinline__ uint32_t nibbles_minus_8(uint32_t x)
+// ---- per-call activation preparation ------------------------------------------
+
+// One lane per Q8_1 block: 32 int8 codes -> 32 fp16 codes in the order of
+// nibbles_to_f16 (pairs (4j, 4j+2), (4j+1, 4j+3), (16+4j, 16+4j+2),
+// (16+4j+1, 16+4j+3) for j = 0..3), and the fp16 scale.
+__global__ __launch_bounds__(kThreads) void prep_activations_kernel(
+    const uint8_t* __restrict__ a, int64_t nblocks, uint8_t* __restrict__ a16, uint16_t* __restrict__ d8)
 {
-    return ((x | 0x80808080u) - 0x08080808u) ^ 0x80808080u;
+    const int64_t stride = (int64_t)gridDim.x * kThreads;
+    for (int64_t blk = (int64_t)blockIdx.x * kThreads + threadIdx.x; blk < nblocks; blk += stride) {
+        const uint32_t* src = reinterpret_cast<const uint32_t*>(a + blk * kQ8Bytes);
+        uint32_t c[8];
+        const uint32_t head = src[0];
+#pragma unroll
+        for (int i = 0; i < 8; ++i) c[i] = src[1 + i];
+        auto f = [](uint32_t word, int byte) -> uint32_t {
+            const _Float16 h = (_Float16)(int)(int8_t)(word >> (8 * byte));   // exact
+            return (uint32_t)__builtin_bit_cast(uint16_t, h);
+        };
+        uint32_t o[16];
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            o[4 * j + 0] = f(c[j], 0) | (f(c[j], 2) << 16);
+            o[4 * j + 1] = f(c[j], 1) | (f(c[j], 3) << 16);
+            o[4 * j + 2] = f(c[4 + j], 0) | (f(c[4 + j], 2) << 16);
+            o[4 * j + 3] = f(c[4 + j], 1) | (f(c[4 + j], 3) << 16);
+        }
+        u32x4* dst = reinterpret_cast<u32x4*>(a16 + blk * kBlockF16);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) dst[i] = u32x4{o[4 * i], o[4 * i + 1], o[4 * i + 2], o[4 * i + 3]};
+        d8[blk] = (uint16_t)(head & 0xffffu);
+    }
 }
 
-// Unpack one Q4_0 block given as fp16 scale bits and four words of nibbles.
-__device__ __forceinline__ void store_block(uint8_t* codes, float* d4s, uint32_t dbits, const uint32_t qs[4])
+// ---- the tile kernel ------------------------------------------------------------
+
+// Map a flat workgroup index to the logical tile index so that each XCD (which
+// receives workgroups i with i % 8 == xcd) gets one contiguous range of tiles.
+__device__ __forceinline__ int64_t xcd_remap(int64_t bid, int64_t G)
 {
-    uint4 lo, hi;
-    lo.x = nibbles_minus_8(qs[0] & 0x0f0f0f0fu);
-    lo.y = nibbles_minus_8(qs[1] & 0x0f0f0f0fu);
-    lo.z = nibbles_minus_8(qs[2] & 0x0f0f0f0fu);
-    lo.w = nibbles_minus_8(qs[3] & 0x0f0f0f0fu);
-    hi.x = nibbles_minus_8((qs[0] >> 4) & 0x0f0f0f0fu);
-    hi.y = nibbles_minus_8((qs[1] >> 4) & 0x0f0f0f0fu);
-    hi.z = nibbles_minus_8((qs[2] >> 4) & 0x0f0f0f0fu);
-    hi.w = nibbles_minus_8((qs[3] >> 4) & 0x0f0f0f0fu);
-    reinterpret_cast<uint4*>(codes)[0] = lo;
-    reinterpret_cast<uint4*>(codes)[1] = hi;
-    *d4s = half_bits_to_float(dbits);
+    const int64_t xcd = bid % kXcds, local = bid / kXcds;
+    const int64_t q = G / kXcds, r = G % kXcds;
+    return xcd * q + min<int64_t>(xcd, r) + local;
 }
 
-template <int BM, int VEC, bool kPartials>
-__global__ __launch_bounds__(kThreads) void moe_grouped_kernel(GroupedParams p)
+template <int BM, int VEC, bool kWide, bool kPartials>
+__global__ __launch_bounds__(kThreads, 2) void moe_grouped_kernel(GroupedParams p)
 {
     using S = Shape<BM>;
-    __shared__ __align__(16) uint8_t a_codes[BM * kCodeStride];
-    __shared__ __align__(16) uint8_t b_codes[kBN * kCodeStride];
-    __shared__ __align__(16) float a_scale[kKB][BM];
-    __shared__ __align__(16) float b_scale[kKB][kBN];
-    __shared__ int32_t row_pair[BM];
-    __shared__ int32_t row_tok[BM];
+    __shared__ __align__(16) Smem<BM> sm;
 
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int wm = wave / S::WN, wn = wave % S::WN;
-    const int32_t total_tiles = p.tiles[p.nbuckets];
+    const int half = lane >> 5, l32 = lane & 31;
+    const int64_t total_tiles = p.tiles[p.nbuckets];
+    const int64_t work = total_tiles * p.n_tiles_n;
+    const bool direct = (int64_t)gridDim.x >= work;   // one workgroup per tile: remap by XCD
+    const int64_t nb = p.nb;
 
-    for (int64_t work = blockIdx.x; work < p.work; work += gridDim.x) {
-        const int64_t mt = work / p.n_tiles_n;
-        const int64_t nt = work - mt * p.n_tiles_n;
-        if (mt >= total_tiles) break;   // tiles are visited in increasing mt order
+    for (int64_t w = blockIdx.x; w < work; w += gridDim.x) {
+        const int64_t L = direct ? xcd_remap(w, work) : w;
+        // groups of kGroupM M tiles, N tiles inner
+        const int64_t grp = L / (kGroupM * p.n_tiles_n);
+        const int64_t rem = L - grp * (kGroupM * p.n_tiles_n);
+        const int64_t mt0 = grp * kGroupM;
+        const int64_t gsz = min<int64_t>(kGroupM, total_tiles - mt0);
+        const int64_t nt = rem / gsz;
+        const int64_t mt = mt0 + (rem - nt * gsz);
 
         // bucket of this M tile: the last b with tiles[b] <= mt
-        int lo = 0, hi = (int)p.nbuckets;   // tiles[nbuckets] = total > mt
+        int lo = 0, hi = (int)p.nbuckets;
         while (hi - lo > 1) {
             const int mid = (lo + hi) >> 1;
             if (p.tiles[mid] <= mt) lo = mid; else hi = mid;
@@ -112,21 +184,22 @@ __global__ __launch_bounds__(kThreads) void moe_grouped_kernel(GroupedParams p)
         const int rows = (int)min<int64_t>(BM, p.offsets[bucket + 1] - slot0);
         const int64_t n0 = nt * kBN;
 
-        __syncthreads();   // previous tile is done with the LDS row tables
+        __syncthreads();   // the previous tile is done with LDS
         for (int m = tid; m < BM; m += kThreads) {
             const int32_t pid = m < rows ? p.sorted[slot0 + m] : 0;
-            row_pair[m] = pid;
-            row_tok[m] = (int32_t)(pid / p.top_k);
+            sm.row_pair[m] = pid;
+            sm.row_tok[m] = (int32_t)(pid / p.top_k);
         }
+        if (tid < 2 * kKB) sm.bs[tid / kKB][tid % kKB][kBN] = 0u;
         __syncthreads();
 
         if (bucket == p.E) {   // masked pairs: zero rows
             for (int i = tid; i < rows * kBN; i += kThreads) {
                 const int m = i / kBN, n = i - m * kBN;
                 if (n0 + n >= p.N) continue;
-                const int64_t o = (int64_t)row_pair[m] * p.N + n0 + n;
+                const int64_t o = (int64_t)sm.row_pair[m] * p.N + n0 + n;
                 if constexpr (kPartials) {
-                    for (int64_t b = 0; b < p.nb; ++b) p.partials[o * p.nb + b] = 0;
+                    for (int64_t b = 0; b < nb; ++b) p.partials[o * nb + b] = 0;
                 } else {
                     p.out[o] = 0.0f;
                 }
@@ -134,119 +207,191 @@ __global__ __launch_bounds__(kThreads) void moe_grouped_kernel(GroupedParams p)
             continue;
         }
 
-        float acc[S::SM][S::SN][16];
+        // ---- per-tile staging plan ------------------------------------------
+        // Offsets are relative to bases that advance by a constant per stage;
+        // loads are never predicated: a row past the tile (A) or past N (B) is
+        // computed but never stored, and a block past K/32 is read from block
+        // K/32-1 with its weight scale set to 0, so it adds fma(P, 0, acc) =
+        // acc exactly.
+        // A: BM rows x kKB blocks x 64 B = BM*8 units of 16 B (unit c of a row: block c/4, piece c%4)
+        constexpr int kAUnits = BM * kKB * 4;
+        constexpr int kAPer = (kAUnits + kThreads - 1) / kThreads;
+        static_assert(kAUnits % kThreads == 0, "whole A units per thread");
+        using AOff = typename std::conditional<kWide, int64_t, uint32_t>::type;
+        AOff a_off_g[kAPer];
+        int a_blk[kAPer];
+#pragma unroll
+        for (int i = 0; i < kAPer; ++i) {
+            const int u = tid + i * kThreads;
+            const int m = u >> 3, c = u & 7;
+            a_blk[i] = c >> 2;
+            a_off_g[i] = (AOff)(((int64_t)sm.row_tok[m < rows ? m : 0] * nb + (c >> 2)) * kBlockF16 + (c & 3) * 16);
+        }
+        // A scales: thread < BM*kKB owns (row tid % BM, block tid / BM)
+        const int d_m = tid % BM, d_blk = tid / BM;
+        const AOff d_off = (AOff)((int64_t)sm.row_tok[d_m < rows ? d_m : 0] * nb + d_blk);
+        // B: one block (18 B) of one weight row per thread
+        static_assert(kBN * kKB == kThreads, "one weight block per thread");
+        const int bn = tid % kBN, bh = tid / kBN;
+        const uint8_t* wtile = p.w + (bucket * p.N + n0) * nb * kQ4Bytes;   // uniform per tile
+        const uint32_t bg_off = (uint32_t)(((n0 + bn < p.N ? bn : 0) * nb + bh) * kQ4Bytes);
+
+        u32x4 ra[kAPer];
+        uint32_t rb[5];
+        uint32_t rd8;
+        bool rb_ok;
+
+        auto issue = [&](int64_t kb0) {
+            // the last block stands in for blocks past K/32 (kb0 + c < nb fails only in the last stage)
+            const int64_t kl = nb - 1;
+#pragma unroll
+            for (int i = 0; i < kAPer; ++i) {
+                const int64_t shift = (kb0 + a_blk[i] < nb ? kb0 : kl - a_blk[i]) * kBlockF16;
+                ra[i] = *reinterpret_cast<const u32x4*>(p.a16 + shift + a_off_g[i]);
+            }
+            if (tid < BM * kKB) {
+                const int64_t shift = kb0 + d_blk < nb ? kb0 : kl - d_blk;
+                rd8 = p.d8[shift + d_off];
+            }
+            rb_ok = kb0 + bh < nb;
+            const int64_t kbs = rb_ok ? kb0 : kl - bh;
+            const uint8_t* bp = wtile + kbs * kQ4Bytes + bg_off;
+            if constexpr (VEC == 4) {
+                // a pair of blocks starts 4-byte aligned (K/32 even, kb0 even):
+                // block kb0 is words 0..4 of the pair, block kb0+1 words 4..8
+                const uint32_t* wp = reinterpret_cast<const uint32_t*>(bp - 18 * bh) + 4 * bh;
+#pragma unroll
+                for (int i = 0; i < 5; ++i) rb[i] = wp[i];
+            } else {
+                const uint16_t* hp = reinterpret_cast<const uint16_t*>(bp);
+                rb[0] = hp[0];
+#pragma unroll
+                for (int i = 0; i < 4; ++i) rb[1 + i] = (uint32_t)hp[1 + 2 * i] | ((uint32_t)hp[2 + 2 * i] << 16);
+            }
+        };
+        auto commit = [&](int buf) {
+#pragma unroll
+            for (int i = 0; i < kAPer; ++i) {
+                const int u = tid + i * kThreads;
+                *reinterpret_cast<u32x4*>(&sm.a[buf][(u >> 3) * kRowBytes + (u & 7) * 16]) = ra[i];
+            }
+            if (tid < BM * kKB) sm.as[buf][d_blk][d_m] = rd8;
+            // weight block -> 32 fp16 values (q - 8) and its scale
+            uint32_t dbits, qs[4];
+            if constexpr (VEC == 4) {
+                if (bh == 0) {
+                    dbits = rb[0] & 0xffffu;
+                    qs[0] = __builtin_amdgcn_alignbit(rb[1], rb[0], 16);
+                    qs[1] = __builtin_amdgcn_alignbit(rb[2], rb[1], 16);
+                    qs[2] = __builtin_amdgcn_alignbit(rb[3], rb[2], 16);
+                    qs[3] = __builtin_amdgcn_alignbit(rb[4], rb[3], 16);
+                } else {
+                    dbits = rb[0] >> 16;
+                    qs[0] = rb[1]; qs[1] = rb[2]; qs[2] = rb[3]; qs[3] = rb[4];
+                }
+            } else {
+                dbits = rb[0];
+                qs[0] = rb[1]; qs[1] = rb[2]; qs[2] = rb[3]; qs[3] = rb[4];
+            }
+            uint32_t o[16];
+#pragma unroll
+            for (int j = 0; j < 4; ++j) nibbles_to_f16(qs[j], &o[4 * j]);
+            u32x4* dst = reinterpret_cast<u32x4*>(&sm.b[buf][bn * kRowBytes + bh * kBlockF16]);
+#pragma unroll
+            for (int i = 0; i < 4; ++i) dst[i] = u32x4{o[4 * i], o[4 * i + 1], o[4 * i + 2], o[4 * i + 3]};
+            sm.bs[buf][bh][bn] = rb_ok ? dbits : 0u;
+        };
+
+        // LDS read offsets of this lane's fragments (constant over the K loop)
+        int a_off[S::SM], b_off[S::SN], as_off[S::SM], bs_off[S::SN];
+#pragma unroll
+        for (int i = 0; i < S::SM; ++i) {
+            const int m = (wm * S::SM + i) * 32 + l32;
+            a_off[i] = m * kRowBytes + 32 * half;
+            as_off[i] = m;
+        }
+#pragma unroll
+        for (int j = 0; j < S::SN; ++j) {
+            const int n = (wn * S::SN + j) * 32 + l32;
+            b_off[j] = n * kRowBytes + 32 * half;
+            bs_off[j] = half ? kBN : n;   // upper-half lanes read the zero slot
+        }
+
+        v16f acc[S::SM][S::SN];
 #pragma unroll
         for (int i = 0; i < S::SM; ++i)
 #pragma unroll
             for (int j = 0; j < S::SN; ++j)
 #pragma unroll
                 for (int k = 0; k < 16; ++k) acc[i][j][k] = 0.0f;
+        // scale operands of the outer product d8 (x) d4: one fp16 in k slot 0, zeros elsewhere
+        u32x4 as_v[S::SM], bs_v[S::SN];
+#pragma unroll
+        for (int i = 0; i < S::SM; ++i) as_v[i] = u32x4{0, 0, 0, 0};
+#pragma unroll
+        for (int j = 0; j < S::SN; ++j) bs_v[j] = u32x4{0, 0, 0, 0};
 
-        const uint8_t* wexp = p.w + (bucket * p.N) * p.nb * kQ4Bytes;
-
-        for (int64_t kb0 = 0; kb0 < p.nb; kb0 += kKB) {
-            __syncthreads();   // previous pass consumed
-            // ---- stage A: BM pair rows x kKB blocks of Q8_1 -----------------
-            for (int u = tid; u < BM * kKB; u += kThreads) {
-                const int m = u / kKB, blk = u - m * kKB;
-                const int64_t b = kb0 + blk;
-                uint4 q0 = make_uint4(0, 0, 0, 0), q1 = q0;
-                float d8 = 0.0f;
-                if (m < rows && b < p.nb) {
-                    const uint32_t* src = reinterpret_cast<const uint32_t*>(p.a + ((int64_t)row_tok[m] * p.nb + b) * kQ8Bytes);
-                    const uint32_t h = src[0];
-                    q0 = make_uint4(src[1], src[2], src[3], src[4]);
-                    q1 = make_uint4(src[5], src[6], src[7], src[8]);
-                    d8 = half_bits_to_float(h & 0xffffu);
-                }
-                uint4* dst = reinterpret_cast<uint4*>(a_codes + m * kCodeStride + blk * 32);
-                dst[0] = q0;
-                dst[1] = q1;
-                a_scale[blk][m] = d8;
-            }
-            // ---- stage B: kBN weight rows x kKB blocks of Q4_0 --------------
-            if constexpr (VEC == 4) {
-                // pairs of blocks: 36 bytes, 4-byte aligned (K/32 even, kb0 even)
-                for (int u = tid; u < kBN * (kKB / 2); u += kThreads) {
-                    const int n = u / (kKB / 2), bp = u - n * (kKB / 2);
-                    const int64_t b = kb0 + 2 * bp;
-                    uint32_t v[9] = {0, 0, 0, 0, 0, 0, 0, 0, 0};
-                    const bool ok_row = n0 + n < p.N;
-                    if (ok_row && b < p.nb) {
-                        const uint32_t* src = reinterpret_cast<const uint32_t*>(wexp + ((n0 + n) * p.nb + b) * kQ4Bytes);
+        // One staged pass: kKB blocks from LDS buffer `buf`.  A block past K/32
+        // has weight scale 0 and adds fma(P, 0, acc) = acc exactly.
+        auto compute = [&](int buf, int64_t kb0) {
+#pragma unroll 1
+            for (int blk = 0; blk < kKB; ++blk) {
+                v8h alo[S::SM], ahi[S::SM], blo[S::SN], bhi[S::SN];
 #pragma unroll
-                        for (int i = 0; i < 9; ++i) v[i] = src[i];
-                    }
-                    uint32_t qs[4];
-                    qs[0] = __builtin_amdgcn_alignbit(v[1], v[0], 16);
-                    qs[1] = __builtin_amdgcn_alignbit(v[2], v[1], 16);
-                    qs[2] = __builtin_amdgcn_alignbit(v[3], v[2], 16);
-                    qs[3] = __builtin_amdgcn_alignbit(v[4], v[3], 16);
-                    if (!(ok_row && b < p.nb)) { qs[0] = qs[1] = qs[2] = qs[3] = 0x88888888u; }
-                    store_block(b_codes + n * kCodeStride + (2 * bp) * 32, &b_scale[2 * bp][n], v[0] & 0xffffu, qs);
-                    uint32_t qs1[4] = {v[5], v[6], v[7], v[8]};
-                    if (!(ok_row && b + 1 < p.nb)) { qs1[0] = qs1[1] = qs1[2] = qs1[3] = 0x88888888u; v[4] = 0; }
-                    store_block(b_codes + n * kCodeStride + (2 * bp + 1) * 32, &b_scale[2 * bp + 1][n], v[4] >> 16, qs1);
-                }
-            } else {
-                // single blocks through 2-byte loads (odd K/32 or 2-byte aligned weights)
-                for (int u = tid; u < kBN * kKB; u += kThreads) {
-                    const int n = u / kKB, blk = u - n * kKB;
-                    const int64_t b = kb0 + blk;
-                    uint32_t dbits = 0, qs[4] = {0x88888888u, 0x88888888u, 0x88888888u, 0x88888888u};
-                    if (n0 + n < p.N && b < p.nb) {
-                        const uint16_t* src = reinterpret_cast<const uint16_t*>(wexp + ((n0 + n) * p.nb + b) * kQ4Bytes);
-                        dbits = src[0];
-#pragma unroll
-                        for (int i = 0; i < 4; ++i) qs[i] = (uint32_t)src[1 + 2 * i] | ((uint32_t)src[2 + 2 * i] << 16);
-                    }
-                    store_block(b_codes + n * kCodeStride + blk * 32, &b_scale[blk][n], dbits, qs);
-                }
-            }
-            __syncthreads();
-
-            // ---- MFMA + exact per-block rescale ----------------------------
-            const int kblocks = (int)min<int64_t>(kKB, p.nb - kb0);
-            for (int blk = 0; blk < kblocks; ++blk) {
-                v4i af[S::SM], bf[S::SN];
-#pragma unroll
-                for (int i = 0; i < S::SM; ++i) {
-                    const int m = (wm * S::SM + i) * 32 + (lane & 31);
-                    af[i] = *reinterpret_cast<const v4i*>(a_codes + m * kCodeStride + blk * 32 + 16 * (lane >> 5));
+                for (int ii = 0; ii < S::SM; ++ii) {
+                    const uint8_t* src = &sm.a[buf][a_off[ii] + blk * kBlockF16];
+                    alo[ii] = *reinterpret_cast<const v8h*>(src);
+                    ahi[ii] = *reinterpret_cast<const v8h*>(src + 16);
+                    as_v[ii].x = sm.as[buf][blk][as_off[ii]];
                 }
 #pragma unroll
-                for (int j = 0; j < S::SN; ++j) {
-                    const int n = (wn * S::SN + j) * 32 + (lane & 31);
-                    bf[j] = *reinterpret_cast<const v4i*>(b_codes + n * kCodeStride + blk * 32 + 16 * (lane >> 5));
+                for (int jj = 0; jj < S::SN; ++jj) {
+                    const uint8_t* src = &sm.b[buf][b_off[jj] + blk * kBlockF16];
+                    blo[jj] = *reinterpret_cast<const v8h*>(src);
+                    bhi[jj] = *reinterpret_cast<const v8h*>(src + 16);
+                    bs_v[jj].x = sm.bs[buf][blk][bs_off[jj]];
                 }
 #pragma unroll
                 for (int i = 0; i < S::SM; ++i) {
 #pragma unroll
                     for (int j = 0; j < S::SN; ++j) {
-                        v16i zero = {0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0};
-                        const v16i P = __builtin_amdgcn_mfma_i32_32x32x32_i8(af[i], bf[j], zero, 0, 0, 0);
-                        const int nl = (wn * S::SN + j) * 32 + (lane & 31);
-                        const float d4 = b_scale[blk][nl];
+                        v16f P = __builtin_amdgcn_mfma_f32_32x32x16_f16(alo[i], blo[j], v16f{}, 0, 0, 0);
+                        P = __builtin_amdgcn_mfma_f32_32x32x16_f16(ahi[i], bhi[j], P, 0, 0, 0);
+                        if constexpr (kPartials) {
+                            const int64_t n = n0 + (wn * S::SN + j) * 32 + l32;
+                            const int64_t b = kb0 + blk;
 #pragma unroll
-                        for (int g = 0; g < 4; ++g) {
-                            const int ml = (wm * S::SM + i) * 32 + 8 * g + 4 * (lane >> 5);
-                            const float4 d8 = *reinterpret_cast<const float4*>(&a_scale[blk][ml]);
-                            const float d8v[4] = {d8.x, d8.y, d8.z, d8.w};
-#pragma unroll
-                            for (int r = 0; r < 4; ++r) {
-                                if constexpr (kPartials) {
-                                    const int m = ml + r;
-                                    const int64_t n = n0 + nl;
-                                    if (m < rows && n < p.N)
-                                        p.partials[((int64_t)row_pair[m] * p.N + n) * p.nb + kb0 + blk] = P[4 * g + r];
-                                } else {
-                                    acc[i][j][4 * g + r] = __builtin_fmaf((float)P[4 * g + r], d4 * d8v[r], acc[i][j][4 * g + r]);
-                                }
+                            for (int r = 0; r < 16; ++r) {
+                                const int m = (wm * S::SM + i) * 32 + 8 * (r / 4) + 4 * half + (r % 4);
+                                if (m < rows && n < p.N && b < nb)
+                                    p.partials[((int64_t)sm.row_pair[m] * p.N + n) * nb + b] = (int32_t)P[r];
                             }
+                        } else {
+                            const v16f Sc = __builtin_amdgcn_mfma_f32_32x32x16_f16(
+                                __builtin_bit_cast(v8h, as_v[i]), __builtin_bit_cast(v8h, bs_v[j]), v16f{}, 0, 0, 0);
+#pragma unroll
+                            for (int r = 0; r < 16; ++r) acc[i][j][r] = __builtin_fmaf(P[r], Sc[r], acc[i][j][r]);
                         }
                     }
                 }
             }
+        };
+
+        // ---- K loop: double-buffered, unrolled by two so buffers are constants
+        const int64_t nstages = (nb + kKB - 1) / kKB;
+        issue(0);
+        commit(0);
+        __syncthreads();
+        for (int64_t s = 0; s < nstages; s += 2) {
+            if (s + 1 < nstages) issue((s + 1) * kKB);
+            compute(0, s * kKB);
+            if (s + 1 < nstages) commit(1);
+            __syncthreads();
+            if (s + 1 >= nstages) break;
+            if (s + 2 < nstages) issue((s + 2) * kKB);
+            compute(1, (s + 1) * kKB);
+            if (s + 2 < nstages) commit(0);
+            __syncthreads();
         }
 
         if constexpr (!kPartials) {
@@ -254,14 +399,12 @@ __global__ __launch_bounds__(kThreads) void moe_grouped_kernel(GroupedParams p)
             for (int i = 0; i < S::SM; ++i) {
 #pragma unroll
                 for (int j = 0; j < S::SN; ++j) {
-                    const int64_t n = n0 + (wn * S::SN + j) * 32 + (lane & 31);
+                    const int64_t n = n0 + (wn * S::SN + j) * 32 + l32;
 #pragma unroll
-                    for (int g = 0; g < 4; ++g) {
-#pragma unroll
-                        for (int r = 0; r < 4; ++r) {
-                            const int m = (wm * S::SM + i) * 32 + 8 * g + 4 * (lane >> 5) + r;
-                            if (m < rows && n < p.N) p.out[(int64_t)row_pair[m] * p.N + n] = acc[i][j][4 * g + r];
-                        }
+                    for (int r = 0; r < 16; ++r) {
+                        const int m = (wm * S::SM + i) * 32 + 8 * (r / 4) + 4 * half + (r % 4);
+                        if (m < rows && n < p.N)
+                            __builtin_nontemporal_store(acc[i][j][r], &p.out[(int64_t)sm.row_pair[m] * p.N + n]);
                     }
                 }
             }
@@ -270,17 +413,27 @@ __global__ __launch_bounds__(kThreads) void moe_grouped_kernel(GroupedParams p)
 }
 
 template <int BM, bool kPartials>
-int launch_grouped(int vec, const GroupedParams& gp, int64_t grid, hipStream_t s)
+int launch_grouped(int vec, bool wide, const GroupedParams& gp, int64_t grid, hipStream_t s)
 {
-    if (vec == 4)
-        return launch("moe_grouped_kernel<4>", moe_grouped_kernel<BM, 4, kPartials>, grid, kThreads, 0, s, gp);
-    return launch("moe_grouped_kernel<2>", moe_grouped_kernel<BM, 2, kPartials>, grid, kThreads, 0, s, gp);
+    if (vec == 4) {
+        return wide ? launch("moe_grouped_kernel<4,wide>", moe_grouped_kernel<BM, 4, true, kPartials>, grid, kThreads, 0, s, gp)
+                    : launch("moe_grouped_kernel<4>", moe_grouped_kernel<BM, 4, false, kPartials>, grid, kThreads, 0, s, gp);
+    }
+    return wide ? launch("moe_grouped_kernel<2,wide>", moe_grouped_kernel<BM, 2, true, kPartials>, grid, kThreads, 0, s, gp)
+                : launch("moe_grouped_kernel<2>", moe_grouped_kernel<BM, 2, false, kPartials>, grid, kThreads, 0, s, gp);
 }
 
 }  // namespace
 
 int64_t grouped_tile_m(const MoeArgs& m)
 {
+    // FTQ_TILE_M=32|64|128 pins the tile height (tuning and tests); read once
+    static const int64_t forced = [] {
+        const char* v = getenv("FTQ_TILE_M");
+        const int64_t t = v ? atoll(v) : 0;
+        return (t == 32 || t == 64 || t == 128) ? t : 0;
+    }();
+    if (forced) return forced;
     // rows per M tile from the average pairs per expert (host arithmetic only)
     const int64_t per_expert = (m.T * m.top_k) / (m.E > 0 ? m.E : 1);
     if (per_expert >= 96) return 128;
@@ -288,16 +441,36 @@ int64_t grouped_tile_m(const MoeArgs& m)
     return 32;
 }
 
-int run_grouped(const MoeArgs& m, const BucketPlan& plan, const void* ws, hipStream_t s)
+int64_t grouped_prep_bytes(int64_t T, int64_t K)
+{
+    const int64_t nb = K / kQK;
+    auto align = [](int64_t v) { return (v + 255) / 256 * 256; };
+    return align(T * nb * kBlockF16) + align(T * nb * 2);
+}
+
+int run_grouped(const MoeArgs& m, const BucketPlan& plan, void* ws, hipStream_t s)
 {
     if (plan.pairs == 0) return FTQ_OK;
     DeviceLimits lim;
     int st = device_limits(&lim);
     if (st != FTQ_OK) return st;
-    const uint8_t* base = static_cast<const uint8_t*>(ws);
+    uint8_t* base = static_cast<uint8_t*>(ws);
+    const int64_t nb = m.K / kQK;
+    auto align = [](int64_t v) { return (v + 255) / 256 * 256; };
+    uint8_t* a16 = base + plan.bytes;
+    uint16_t* d8 = reinterpret_cast<uint16_t*>(a16 + align(m.T * nb * kBlockF16));
+
+    // activations -> fp16 codes + scales (once per call)
+    const int64_t nblocks = m.T * nb;
+    st = launch("prep_activations_kernel", prep_activations_kernel,
+                stride_grid((nblocks + kThreads - 1) / kThreads, lim), kThreads, 0, s,
+                static_cast<const uint8_t*>(m.a), nblocks, a16, d8);
+    if (st != FTQ_OK) return st;
+
     GroupedParams gp{};
     gp.w = static_cast<const uint8_t*>(m.w);
-    gp.a = static_cast<const uint8_t*>(m.a);
+    gp.a16 = a16;
+    gp.d8 = d8;
     gp.out = m.out;
     gp.partials = m.partials;
     gp.offsets = reinterpret_cast<const int32_t*>(base + plan.off_offsets);
@@ -305,22 +478,25 @@ int run_grouped(const MoeArgs& m, const BucketPlan& plan, const void* ws, hipStr
     gp.sorted = reinterpret_cast<const int32_t*>(base + plan.off_sorted);
     gp.E = m.E;
     gp.N = m.N;
-    gp.nb = m.K / kQK;
+    gp.nb = nb;
     gp.top_k = m.top_k;
     gp.nbuckets = plan.buckets;
     gp.n_tiles_n = (m.N + kBN - 1) / kBN;
     const int64_t bm = plan.tile_m;
     // sum over buckets of ceil(count/BM) <= (pairs + buckets*(BM-1)) / BM
-    const int64_t max_mt = (plan.pairs + plan.buckets * (bm - 1)) / bm;
-    gp.work = max_mt * gp.n_tiles_n;
-    const int64_t grid = std::min<int64_t>(gp.work, lim.max_grid_x);
+    gp.max_mt = (plan.pairs + plan.buckets * (bm - 1)) / bm;
+    const int64_t grid = std::min<int64_t>(gp.max_mt * gp.n_tiles_n, std::min<int64_t>(lim.max_grid_x, UINT32_MAX / kThreads));
     const uintptr_t wa = reinterpret_cast<uintptr_t>(m.w);
-    const int vec = (gp.nb % 2 == 0 && wa % 4 == 0) ? 4 : 2;
+    const int vec = (nb % 2 == 0 && wa % 4 == 0) ? 4 : 2;
     const bool part = m.partials != nullptr;
+    // activation offsets fit 32 bits unless the staged activations reach 4 GiB;
+    // FTQ_FORCE_WIDE=1 selects the 64-bit variant at any size (tests)
+    static const bool force_wide = [] { const char* v = getenv("FTQ_FORCE_WIDE"); return v && v[0] == '1'; }();
+    const bool wide = force_wide || m.T * nb * kBlockF16 >= ((int64_t)1 << 32);
     switch (bm) {
-    case 128: return part ? launch_grouped<128, true>(vec, gp, grid, s) : launch_grouped<128, false>(vec, gp, grid, s);
-    case 64: return part ? launch_grouped<64, true>(vec, gp, grid, s) : launch_grouped<64, false>(vec, gp, grid, s);
-    default: return part ? launch_grouped<32, true>(vec, gp, grid, s) : launch_grouped<32, false>(vec, gp, grid, s);
+    case 128: return part ? launch_grouped<128, true>(vec, wide, gp, grid, s) : launch_grouped<128, false>(vec, wide, gp, grid, s);
+    case 64: return part ? launch_grouped<64, true>(vec, wide, gp, grid, s) : launch_grouped<64, false>(vec, wide, gp, grid, s);
+    default: return part ? launch_grouped<32, true>(vec, wide, gp, grid, s) : launch_grouped<32, false>(vec, wide, gp, grid, s);
     }
 }
 

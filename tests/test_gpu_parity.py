@@ -203,3 +203,24 @@ def test_route_then_routed_equals_one_call(path):
     ref2 = ftq.moe(w2, aq, ids, 16, 200, 512, path=path)
     torch.cuda.synchronize()
     assert torch.equal(out, one) and torch.equal(out2, ref2)
+
+
+def test_wide_offset_variant_matches():
+    """The 64-bit-offset tile kernel (used past 4 GiB of staged activations) is
+    forced on a small case in a child process and must match the oracle."""
+    import os
+    import subprocess
+    import sys
+    code = (
+        "import numpy as np\n"
+        "from tests._cases import Case, assert_matches_oracle\n"
+        "from quantized_moe_expert_quantize_amd import ftq\n"
+        "c = Case(8, 200, 640, 120, 4, seed=6)\n"
+        "ref, ab = c.oracle_out()\n"
+        "assert_matches_oracle(c.run(ftq.PATH_GROUPED).cpu().numpy(), ref, ab, c.nb)\n"
+        "assert np.array_equal(c.partials(ftq.PATH_GROUPED), c.oracle_partials())\n"
+        "print('wide ok')\n")
+    root = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+    env = dict(os.environ, FTQ_FORCE_WIDE="1")
+    r = subprocess.run([sys.executable, "-c", code], cwd=root, env=env, capture_output=True, text=True, timeout=300)
+    assert r.returncode == 0 and "wide ok" in r.stdout, r.stdout + r.stderr
