@@ -28,8 +28,12 @@ ARCH = "gfx950"
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 # Packed fp32 VALU ops are kept out of generated code on purpose.  No implicit
 # contraction: every fused multiply-add in the kernels is written out (fmaf),
-# and a product that feeds an fp16 conversion must round to fp32 first.
-FLAGS = ["-std=c++17", "-O3", "-fPIC", "-ffp-contract=off", "-Wall", "-Wno-unused-function", f"--offload-arch={ARCH}",
+# and a product that feeds an fp16 conversion must round to fp32 first.  No
+# type-based alias analysis: the kernels write LDS and global staging buffers
+# as 16-byte vectors and read them back as words (and the other way round), and
+# with strict aliasing the compiler may move such a read above the write.
+FLAGS = ["-std=c++17", "-O3", "-fPIC", "-ffp-contract=off", "-fno-strict-aliasing", "-Wall", "-Wno-unused-function",
+         "-Wno-cuda-compat", f"--offload-arch={ARCH}",
          "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops", "-I", INCLUDE]
 
 

@@ -2,25 +2,37 @@
 //
 // The same operation as the per-pair MoE GEMV of FreeToken PR #185 ("fix(kernel):
 // launch GGUF MoE GEMV token axis on grid.x, not grid.z", Problem/Fix), laid out
-// for gfx950 instead of one block per pair: a workgroup owns one expert and a
-// tile of kRows weight rows, streams that tile from HBM exactly once, and serves
-// every pair routed to the expert from it.  The weight stream is >97% of the
-// bytes at decode sizes, so this is an HBM-bound kernel:
-//   * the weight tile (kRows whole rows x kSeg blocks, contiguous in HBM) is
-//     copied to LDS with the widest aligned vector loads the layout allows
-//     (16 B when K/32 % 8 == 0), so HBM sees fully coalesced bursts even though
-//     Q4_0 blocks are 18 bytes;
-//   * the routed tokens' Q8_1 blocks are staged in LDS once per workgroup,
-//     re-laid out as 16-byte aligned codes plus (d, -8*sum(q)) per block;
-//   * 16 lanes share a row, each taking block pairs (36 bytes, 4-byte aligned in
-//     LDS) in a fixed stride; per block the integer partial is 8 v_dot4_i32_i8
-//     on the raw nibbles started from -8*sum(q8) (exact), then one fp32 FMA with
-//     the exact scale product d4*d8; the 16 partial sums are combined with a
-//     fixed xor-shuffle tree.  Nothing depends on the batch size, so a row's
+// for gfx950 instead of one block per pair: each weight row of each routed
+// expert is streamed from HBM exactly once and serves every pair routed to that
+// expert.  At decode sizes the weight stream is >97% of the bytes, so this is an
+// HBM-streaming kernel:
+//   * work items are (routed expert, tile of 16 rows); the grid is what fits
+//     on the device at once and each workgroup takes a contiguous share of the
+//     items (at most one item more than any other), so no workgroup waits for
+//     a second round and every routed expert's rows are spread over all CUs;
+//   * 16 lanes share a row and walk it in steps of 16 groups of 8 Q4_0 blocks
+//     (2304 bytes).  A step is loaded coalesced: each load instruction of the
+//     16 lanes covers 256 contiguous bytes of the row (16 bytes per lane when
+//     K/32 % 8 == 0), which the memory system serves at full rate, whereas
+//     one 144-byte group per lane (lanes 144 bytes apart) reaches only about a
+//     third of it.  The step then passes through a wave-private LDS buffer so
+//     that lane l reads back its own group of 8 whole blocks; no workgroup
+//     barrier is involved, and each wave issues the loads of its next step
+//     before it computes the current one;
+//   * the routed tokens' Q8_1 blocks are staged once per (expert, K segment) in
+//     LDS as aligned codes plus (d, -8 * sum(q)), padded so that the 16 lanes
+//     of a row (reading blocks 8 apart) hit distinct banks;
+//   * per block the integer partial is 8 v_dot4_i32_i8 on the raw nibbles
+//     started from -8*sum(q8) (exact), then one fp32 FMA with the exact scale
+//     product d4*d8; the 16 lane sums are combined with a fixed xor-shuffle
+//     tree, and K segments (only for rows longer than the staging budget) are
+//     added in order.  Nothing depends on the batch or the grid, so a row's
 //     bits do not change when the batch is split.
-// The grid is one flat x axis over (expert bucket, row tile) with 64-bit
-// index math; the pair list is either scanned from topk_ids by each
-// workgroup (small batches) or read from the bucketed list.
+// The pair list of an expert is either scanned from topk_ids (small batches)
+// or read from the bucketed list.  Masked pairs (ids outside [0, E)) form one
+// more "expert" whose items write zero rows.
+#include <type_traits>
+
 #include "ftq_internal.h"
 
 namespace ftq {
@@ -29,11 +41,20 @@ namespace {
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
 constexpr int kThreads = 256;
-constexpr int kRows = 16;                         // weight rows per workgroup
-constexpr int kLanesPerRow = kThreads / kRows;    // 16
-constexpr int kSeg = 64;                          // K blocks staged per pass
-constexpr int kPairChunk = 8;                     // pairs served per pass
-constexpr int kRowStride = (kSeg * kQ4Bytes + 15) / 16 * 16 + 16;   // LDS bytes per staged row
+constexpr int kWaves = kThreads / 64;
+constexpr int kLPR = 16;                                        // lanes per row
+constexpr int kRowsPerWave = 64 / kLPR;                         // 4
+constexpr int kRowsPerTile = kRowsPerWave * kWaves;             // 16
+constexpr int kGroup = 8;                                       // blocks per lane group (144 bytes)
+constexpr int kPairChunk = 8;                                   // pairs served per pass
+constexpr int kStepGroups = kLPR;                               // groups per row per step
+constexpr int kStepBlocks = kStepGroups * kGroup;               // 128
+constexpr int kStepBytes = kStepBlocks * kQ4Bytes;              // 2304
+constexpr int kWRowPitch = kStepBytes + 16;                     // LDS bytes per row of a step
+constexpr int kWaveW = kRowsPerWave * kWRowPitch;               // LDS bytes per wave for weights
+constexpr int kWavesPerSimd = 3;                                // register budget: 3 waves per SIMD
+constexpr int64_t kLdsPerCU = 160 * 1024;
+constexpr int64_t kTargetWGPerCU = 2;                           // LDS is sized so that 2 workgroups fit
 
 struct GemvParams {
     const uint8_t* w;
@@ -44,204 +65,262 @@ struct GemvParams {
     const int32_t* offsets;   // bucketed mode: [E+2] segment starts
     const int32_t* sorted;    // bucketed mode: pair ids grouped by bucket
     int64_t E, N, nb, top_k, pairs, row_tiles;
+    int64_t grid;             // workgroups launched
+    int64_t seg;              // K blocks staged per pass (a multiple of 8)
+    int pc_cap;               // activation rows staged per pass (<= kPairChunk)
+    int list_cap;             // scan mode: LDS slots for the pair list
 };
+
+// Activation staging in LDS, block-major so that a lane's pairs sit at fixed
+// offsets from one address: for block b of the segment and chunk row j (pc rows
+// staged), 32 code bytes at code_off(b) + 32 j and an 8-byte entry (d8 as fp32,
+// -8 * sum(q) as int32) at ent_off(b) + 8 j.  One 16-byte pad per 8 blocks
+// (codes) and one 8-byte pad per 8 blocks (entries) put the blocks 8l+jb read
+// by lanes l = 0..15 on distinct banks for any pc.
+__host__ __device__ constexpr int64_t code_bytes(int64_t seg, int64_t pc) { return 32 * pc * seg + 16 * ((seg + 7) / 8) + 16; }
+__host__ __device__ constexpr int64_t ent_bytes(int64_t seg, int64_t pc) { return 8 * pc * seg + 8 * ((seg + 7) / 8) + 8; }
+__device__ __forceinline__ int code_off(int b, int pc) { return 32 * pc * b + 16 * (b >> 3); }
+__device__ __forceinline__ int ent_off(int b, int pc) { return 8 * pc * b + 8 * (b >> 3); }
 
 struct LdsLayout {
-    int wt, aq, ad, plist, scan, bytes;
+    int64_t wt, codes, ds, bits, prefix, plist, misc, list, bytes;
 };
 
-__host__ __device__ constexpr LdsLayout lds_layout(int scan_cap)
+__host__ __device__ constexpr LdsLayout lds_layout(int64_t E, int64_t seg, int64_t pc_cap, int64_t list_cap)
 {
     LdsLayout l{};
+    const int64_t words = (E + 1 + 31) / 32;
     l.wt = 0;
-    l.aq = l.wt + kRows * kRowStride;
-    l.ad = l.aq + kPairChunk * kSeg * 32;
-    l.plist = l.ad + kPairChunk * kSeg * 8;
-    l.scan = l.plist + 2 * kPairChunk * 4 + 64;
-    l.bytes = l.scan + scan_cap * 4;
+    l.codes = l.wt + kWaves * kWaveW;
+    l.ds = l.codes + code_bytes(seg, pc_cap);
+    l.bits = (l.ds + ent_bytes(seg, pc_cap) + 15) / 16 * 16;
+    l.prefix = l.bits + 4 * words;
+    l.plist = l.prefix + 4 * (words + 1);
+    l.misc = l.plist + 4 * 2 * kPairChunk;
+    l.list = l.misc + 4 * 16;
+    l.bytes = l.list + 4 * list_cap;
     return l;
 }
 
-__device__ __forceinline__ int bucket_of(int32_t id, int64_t E) { return (id >= 0 && id < E) ? id : (int)E; }
+__device__ __forceinline__ int64_t bucket_of(int32_t id, int64_t E) { return (id >= 0 && id < E) ? id : E; }
+
+// Values every lane holds the same copy of (read from LDS or from global memory
+// at a uniform address): moved to scalar registers so that loops over them are
+// scalar loops.
+__device__ __forceinline__ int32_t uniform(int32_t v) { return __builtin_amdgcn_readfirstlane(v); }
+__device__ __forceinline__ int64_t uniform(int64_t v)
+{
+    const uint64_t u = (uint64_t)v;
+    const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)u), hi = __builtin_amdgcn_readfirstlane((uint32_t)(u >> 32));
+    return (int64_t)(((uint64_t)hi << 32) | lo);
+}
 
 __device__ __forceinline__ float half_bits_to_float(uint32_t bits)
 {
     return (float)__builtin_bit_cast(_Float16, (uint16_t)bits);
 }
 
-// Copy rows [n0, n0+rows) x blocks [sb, sb+len) of expert e into LDS.
-template <int VEC>
-__device__ __forceinline__ void stage_weights(const GemvParams& p, int64_t e, int64_t n0, int rows,
-                                              int64_t sb, int len, uint8_t* wt)
-{
-    const int row_bytes = len * kQ4Bytes;
-    const int upr = row_bytes / VEC;   // VEC divides row_bytes by construction
-    for (int u = threadIdx.x; u < rows * upr; u += kThreads) {
-        const int r = u / upr, col = u - r * upr;
-        const uint8_t* src = p.w + ((e * p.N + n0 + r) * p.nb + sb) * kQ4Bytes + col * VEC;
-        uint8_t* dst = wt + r * kRowStride + col * VEC;
-        if constexpr (VEC == 16) {
-            *reinterpret_cast<u32x4*>(dst) = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(src));
-        } else if constexpr (VEC == 4) {
-            *reinterpret_cast<uint32_t*>(dst) = __builtin_nontemporal_load(reinterpret_cast<const uint32_t*>(src));
-        } else {
-            *reinterpret_cast<uint16_t*>(dst) = *reinterpret_cast<const uint16_t*>(src);
-        }
-    }
-}
-
-// Stage the Q8_1 blocks [sb, sb+len) of the chunk's tokens: codes as 32
-// aligned bytes, and per block (d8 as float, -8 * sum of the codes).
-__device__ __forceinline__ void stage_acts(const GemvParams& p, const int32_t* tok, int npc, int64_t sb,
-                                           int len, uint8_t* aq, uint8_t* ad)
+// Stage the Q8_1 blocks [sb, sb+len) of the chunk's tokens.
+__device__ __forceinline__ void stage_acts(const GemvParams& p, const int32_t* tok, int npc, int64_t sb, int len,
+                                           uint8_t* codes, uint8_t* ds)
 {
     for (int u = threadIdx.x; u < npc * len; u += kThreads) {
-        const int j = u / len, blk = u - j * len;
-        const uint32_t* src = reinterpret_cast<const uint32_t*>(p.a + ((int64_t)tok[j] * p.nb + sb + blk) * kQ8Bytes);
+        const int j = u / len, b = u - j * len;
+        const uint32_t* src = reinterpret_cast<const uint32_t*>(p.a + ((int64_t)tok[j] * p.nb + sb + b) * kQ8Bytes);
         uint32_t v[9];
 #pragma unroll
         for (int i = 0; i < 9; ++i) v[i] = src[i];
         int sum = 0;
 #pragma unroll
         for (int i = 1; i < 9; ++i) sum = __builtin_amdgcn_sdot4((int)v[i], 0x01010101, sum, false);
-        uint4* q = reinterpret_cast<uint4*>(aq + (j * kSeg + blk) * 32);
-        q[0] = make_uint4(v[1], v[2], v[3], v[4]);
-        q[1] = make_uint4(v[5], v[6], v[7], v[8]);
-        float2* dc = reinterpret_cast<float2*>(ad + (j * kSeg + blk) * 8);
-        *dc = make_float2(half_bits_to_float(v[0] & 0xffffu), __int_as_float(-8 * sum));
+        u32x4* q = reinterpret_cast<u32x4*>(codes + code_off(b, p.pc_cap) + 32 * j);
+        q[0] = u32x4{v[1], v[2], v[3], v[4]};
+        q[1] = u32x4{v[5], v[6], v[7], v[8]};
+        *reinterpret_cast<float2*>(ds + ent_off(b, p.pc_cap) + 8 * j) =
+            make_float2(half_bits_to_float(v[0] & 0xffffu), __int_as_float(-8 * sum));
     }
 }
 
 // Integer partial of one block: P = sum (nib - 8) * q8 = sum nib*q8 - 8*sum q8.
-__device__ __forceinline__ int block_dot(const uint32_t qs[4], const uint4 a0, const uint4 a1, int neg8sum)
+// lo/hi hold the low and high nibbles of the block's 16 bytes, one per byte.
+__device__ __forceinline__ int block_dot(const uint32_t lo[4], const uint32_t hi[4], const u32x4 a0,
+                                         const u32x4 a1, int neg8sum)
 {
     int acc = neg8sum;
-    acc = __builtin_amdgcn_sdot4((int)(qs[0] & 0x0f0f0f0fu), (int)a0.x, acc, false);
-    acc = __builtin_amdgcn_sdot4((int)(qs[1] & 0x0f0f0f0fu), (int)a0.y, acc, false);
-    acc = __builtin_amdgcn_sdot4((int)(qs[2] & 0x0f0f0f0fu), (int)a0.z, acc, false);
-    acc = __builtin_amdgcn_sdot4((int)(qs[3] & 0x0f0f0f0fu), (int)a0.w, acc, false);
-    acc = __builtin_amdgcn_sdot4((int)((qs[0] >> 4) & 0x0f0f0f0fu), (int)a1.x, acc, false);
-    acc = __builtin_amdgcn_sdot4((int)((qs[1] >> 4) & 0x0f0f0f0fu), (int)a1.y, acc, false);
-    acc = __builtin_amdgcn_sdot4((int)((qs[2] >> 4) & 0x0f0f0f0fu), (int)a1.z, acc, false);
-    acc = __builtin_amdgcn_sdot4((int)((qs[3] >> 4) & 0x0f0f0f0fu), (int)a1.w, acc, false);
+    acc = __builtin_amdgcn_sdot4((int)lo[0], (int)a0.x, acc, false);
+    acc = __builtin_amdgcn_sdot4((int)lo[1], (int)a0.y, acc, false);
+    acc = __builtin_amdgcn_sdot4((int)lo[2], (int)a0.z, acc, false);
+    acc = __builtin_amdgcn_sdot4((int)lo[3], (int)a0.w, acc, false);
+    acc = __builtin_amdgcn_sdot4((int)hi[0], (int)a1.x, acc, false);
+    acc = __builtin_amdgcn_sdot4((int)hi[1], (int)a1.y, acc, false);
+    acc = __builtin_amdgcn_sdot4((int)hi[2], (int)a1.z, acc, false);
+    acc = __builtin_amdgcn_sdot4((int)hi[3], (int)a1.w, acc, false);
     return acc;
 }
 
-template <int VEC, bool kBucketed, bool kPartials>
-__global__ __launch_bounds__(kThreads) void moe_gemv_kernel(GemvParams p, int scan_cap)
+// One lane's group of up to 8 blocks (144 bytes) as 36 words.
+struct Group {
+    uint32_t w[36];
+};
+
+// Block jb (0..7) of a group: fp16 scale bits and its low / high nibbles.
+__device__ __forceinline__ void group_block(const Group& G, int jb, uint32_t& dbits, uint32_t lo[4], uint32_t hi[4])
 {
-    extern __shared__ __align__(16) uint8_t lds[];
-    const LdsLayout L = lds_layout(scan_cap);
-    uint8_t* wt = lds + L.wt;
-    uint8_t* aq = lds + L.aq;
-    uint8_t* ad = lds + L.ad;
-    int32_t* plist = reinterpret_cast<int32_t*>(lds + L.plist);   // [kPairChunk] pair ids
-    int32_t* ptok = plist + kPairChunk;                             // [kPairChunk] tokens
-    int32_t* misc = ptok + kPairChunk;                              // counters
-    int32_t* scan = reinterpret_cast<int32_t*>(lds + L.scan);
-
-    const int64_t bid = blockIdx.x;
-    const int64_t e = bid / p.row_tiles;               // bucket; e == E is the masked bucket
-    const int64_t n0 = (bid - e * p.row_tiles) * kRows;
-    const int rows = (int)min<int64_t>(kRows, p.N - n0);
-    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-
-    // ---- the pair list of this bucket --------------------------------------
-    const int32_t* list;
-    int64_t count;
-    if constexpr (kBucketed) {
-        const int64_t beg = p.offsets[e];
-        count = p.offsets[e + 1] - beg;
-        list = p.sorted + beg;
-    } else {
-        if (tid == 0) misc[0] = 0;
-        __syncthreads();
-        for (int64_t base = 0; base < p.pairs; base += kThreads) {
-            const int64_t q = base + tid;
-            const bool match = q < p.pairs && bucket_of(p.ids[q], p.E) == e;
-            const uint64_t m = __ballot(match);
-            const int below = __builtin_amdgcn_mbcnt_hi((uint32_t)(m >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)m, 0));
-            if (lane == 0) misc[2 + wave] = __popcll(m);
-            __syncthreads();
-            int off = misc[0];
-            for (int w = 0; w < wave; ++w) off += misc[2 + w];
-            if (match) scan[off + below] = (int32_t)q;
-            __syncthreads();
-            if (tid == 0) misc[0] += misc[2] + misc[3] + misc[4] + misc[5];
-            __syncthreads();
-        }
-        count = misc[0];
-        list = scan;
+    const int k = 9 * (jb >> 1);
+    uint32_t qs[4];
+    if ((jb & 1) == 0) {   // the block starts at word k
+        dbits = G.w[k] & 0xffffu;
+        qs[0] = __builtin_amdgcn_alignbit(G.w[k + 1], G.w[k], 16);
+        qs[1] = __builtin_amdgcn_alignbit(G.w[k + 2], G.w[k + 1], 16);
+        qs[2] = __builtin_amdgcn_alignbit(G.w[k + 3], G.w[k + 2], 16);
+        qs[3] = __builtin_amdgcn_alignbit(G.w[k + 4], G.w[k + 3], 16);
+    } else {               // the block starts in the upper half of word k+4
+        dbits = G.w[k + 4] >> 16;
+        qs[0] = G.w[k + 5];
+        qs[1] = G.w[k + 6];
+        qs[2] = G.w[k + 7];
+        qs[3] = G.w[k + 8];
     }
-    if (count == 0) return;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        lo[i] = qs[i] & 0x0f0f0f0fu;
+        hi[i] = (qs[i] >> 4) & 0x0f0f0f0fu;
+    }
+}
 
-    const int r = tid / kLanesPerRow, l = tid % kLanesPerRow;
-    const bool row_ok = r < rows;
-    const int64_t n = n0 + r;
+// One lane's share of a step as loaded: VEC-byte units 16*i + l of the step.
+template <int VEC>
+struct Raw {
+    static constexpr int kUnits = kStepBytes / VEC / kLPR;   // 9, 36 or 72
+    using Unit = typename std::conditional<VEC == 16, u32x4, typename std::conditional<VEC == 4, uint32_t, uint16_t>::type>::type;
+    Unit u[kUnits];
+};
 
-    for (int64_t c0 = 0; c0 < count; c0 += kPairChunk) {
-        const int npc = (int)min<int64_t>(kPairChunk, count - c0);
-        __syncthreads();   // the previous chunk is done with plist / LDS tiles
-        if (tid < npc) {
-            const int32_t pid = list[c0 + tid];
-            plist[tid] = pid;
-            ptok[tid] = (int32_t)(pid / p.top_k);
+// Load the step of `len` bytes at `src` (VEC-aligned, len a positive multiple
+// of VEC).  Units past `len` re-read the last unit instead of branching, so the
+// nine (or more) loads issue back to back with no wait between them.
+template <int VEC>
+__device__ __forceinline__ void load_step(const uint8_t* src, int len, int l, Raw<VEC>& R)
+{
+    using Unit = typename Raw<VEC>::Unit;
+    const Unit* s = reinterpret_cast<const Unit*>(src);
+    const int last = len / VEC - 1;
+#pragma unroll
+    for (int i = 0; i < Raw<VEC>::kUnits; ++i) R.u[i] = __builtin_nontemporal_load(s + min(kLPR * i + l, last));
+}
+
+// Lanes of a wave exchange data through its private LDS step buffer.  The
+// hardware keeps one wave's LDS accesses in order, but the compiler reasons per
+// lane (a lane's own writes never overlap its own reads) and would move reads
+// across the writes; a wave-scope fence orders them and costs no instruction
+// beyond a wait for the LDS counter.
+__device__ __forceinline__ void wave_lds_fence() { __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront"); }
+
+// Write the loaded units to the row's LDS step buffer in memory order.  Units
+// past the step's length land in the buffer's unused tail, which no lane reads
+// as a block.
+template <int VEC>
+__device__ __forceinline__ void store_step(uint8_t* wrow, int l, const Raw<VEC>& R)
+{
+    using Unit = typename Raw<VEC>::Unit;
+    Unit* d = reinterpret_cast<Unit*>(wrow);
+#pragma unroll
+    for (int i = 0; i < Raw<VEC>::kUnits; ++i) d[kLPR * i + l] = R.u[i];
+}
+
+// Rows of tiles [t0, t1) of expert e, K blocks [sb, sb+len), for the staged chunk.
+// kMultiSeg: rows span several K segments, so later segments add to the sums
+// already written (a global load inside the loop; kept out of the single
+// segment case so that the weight loads are the only loads in flight there).
+// NPC > 0: exactly NPC pairs are staged (no per-pair guards); NPC == 0: npc
+// (1..8) pairs, guarded at run time.
+template <int VEC, bool kPartials, bool kMultiSeg, int NPC>
+__device__ __forceinline__ void stream_tiles(const GemvParams& p, int64_t e, int64_t t0, int64_t t1, int64_t sb, int len,
+                                             int npc, const int32_t* plist, uint8_t* wrow, const uint8_t* codes,
+                                             const uint8_t* ds, int l, int rw, int wave)
+{
+    constexpr int kJ = NPC > 0 ? NPC : kPairChunk;
+    const int pc = p.pc_cap;
+    const int64_t nb = p.nb;
+    const int64_t row_bytes = nb * kQ4Bytes;
+    const uint8_t* wexp = p.w + e * p.N * row_bytes;
+    const int64_t gbeg = sb / kGroup, gend = (sb + len + kGroup - 1) / kGroup;
+    const int64_t seg_end = (sb + len) * kQ4Bytes;   // row bytes up to the segment's end
+    auto step_len = [&](int64_t ws) { return (int)min<int64_t>(kStepBytes, seg_end - ws * kGroup * kQ4Bytes); };
+    auto row_of = [&](int64_t t) { return t * kRowsPerTile + wave * kRowsPerWave + rw; };
+    // rows past N (last tile only) load row N-1; their sums are never written
+    auto src_of = [&](int64_t t, int64_t ws) {
+        return wexp + min<int64_t>(row_of(t), p.N - 1) * row_bytes + ws * kGroup * kQ4Bytes;
+    };
+    // steps are (tile t, first group ws of the step), tile-major
+    auto advance = [&](int64_t& t, int64_t& ws) {
+        ws += kStepGroups;
+        if (ws >= gend) {
+            ws = gbeg;
+            ++t;
         }
-        __syncthreads();
+    };
 
-        if (e == p.E) {   // masked bucket: zero rows
-            if (row_ok && l == 0) {
-                for (int j = 0; j < npc; ++j) {
-                    if constexpr (kPartials) {
-                        for (int64_t b = 0; b < p.nb; ++b) p.partials[((int64_t)plist[j] * p.N + n) * p.nb + b] = 0;
-                    } else {
-                        p.out[(int64_t)plist[j] * p.N + n] = 0.0f;
-                    }
-                }
-            }
-            continue;
+    float acc[kJ];
+#pragma unroll
+    for (int j = 0; j < kJ; ++j) acc[j] = 0.0f;
+
+    // Steps: (tile t, first group ws of the step); the loads of the next step
+    // are in flight while the current one is computed.  Past the range the
+    // load re-reads the last tile's first step (an L2 hit, never used): an
+    // unconditional load keeps the loads in flight the same on every path.
+    Raw<VEC> R;
+    int64_t t = t0, ws = gbeg;
+    load_step<VEC>(src_of(t, ws), step_len(ws), l, R);
+    while (t < t1) {
+        const int64_t n = row_of(t);
+        wave_lds_fence();   // the previous step's reads of the buffer come first
+        store_step<VEC>(wrow, l, R);
+        wave_lds_fence();   // and this step's writes before its reads
+        int64_t t2 = t, ws2 = ws;
+        advance(t2, ws2);
+        {
+            const bool in = t2 < t1;
+            load_step<VEC>(src_of(in ? t2 : t1 - 1, in ? ws2 : gbeg), step_len(in ? ws2 : gbeg), l, R);
         }
-
-        float acc[kPairChunk];
+        // lanes whose group is past the segment (partial steps) compute on a
+        // valid group with scale 0 (fma(P, 0, acc) == acc); rows past N are
+        // never written
+        const int64_t g = ws + l;
+        const bool valid = g < gend;
+        const int64_t gl = (valid ? g : gend - 1) - gbeg;   // group within the segment
+        {
+            // 16-byte loads imply K/32 % 8 == 0: every group is whole
+            const int nblk = VEC == 16 ? kGroup : (int)min<int64_t>(kGroup, nb - (gbeg + gl) * kGroup);
+            const int bl0 = (int)(gl * kGroup);   // first block of the group in the segment
+            const uint32_t* gw = reinterpret_cast<const uint32_t*>(wrow + l * kGroup * kQ4Bytes);
+            // block pairs are read from the step buffer one at a time, which
+            // bounds what is live at once to two blocks
 #pragma unroll
-        for (int j = 0; j < kPairChunk; ++j) acc[j] = 0.0f;
-
-        for (int64_t sb = 0; sb < p.nb; sb += kSeg) {
-            const int len = (int)min<int64_t>(kSeg, p.nb - sb);
-            if (sb > 0) __syncthreads();   // previous segment consumed
-            stage_weights<VEC>(p, e, n0, rows, sb, len, wt);
-            stage_acts(p, ptok, npc, sb, len, aq, ad);
-            __syncthreads();
-            if (row_ok) {
-                const uint8_t* wrow = wt + r * kRowStride;
-                for (int bp = l; 2 * bp < len; bp += kLanesPerRow) {
-                    // two 18-byte blocks = nine 4-byte words, 4-byte aligned in LDS
-                    const uint32_t* src = reinterpret_cast<const uint32_t*>(wrow + 36 * bp);
-                    uint32_t v[9];
+            for (int jp = 0; jp < kGroup / 2; ++jp) {
+                Group bp;   // two blocks = 9 words, dword aligned in LDS
 #pragma unroll
-                    for (int i = 0; i < 9; ++i) v[i] = src[i];
-                    uint32_t qs[2][4];
-                    float d4[2];
-                    d4[0] = half_bits_to_float(v[0] & 0xffffu);
-                    qs[0][0] = __builtin_amdgcn_alignbit(v[1], v[0], 16);
-                    qs[0][1] = __builtin_amdgcn_alignbit(v[2], v[1], 16);
-                    qs[0][2] = __builtin_amdgcn_alignbit(v[3], v[2], 16);
-                    qs[0][3] = __builtin_amdgcn_alignbit(v[4], v[3], 16);
-                    d4[1] = half_bits_to_float(v[4] >> 16);
-                    qs[1][0] = v[5]; qs[1][1] = v[6]; qs[1][2] = v[7]; qs[1][3] = v[8];
-                    const int nblk = min(2, len - 2 * bp);
-                    for (int h = 0; h < nblk; ++h) {
-                        const int blk = 2 * bp + h;
+                for (int i = 0; i < 9; ++i) bp.w[i] = gw[9 * jp + i];
 #pragma unroll
-                        for (int j = 0; j < kPairChunk; ++j) {
-                            if (j < npc) {
-                                const uint4* aqb = reinterpret_cast<const uint4*>(aq + (j * kSeg + blk) * 32);
-                                const float2 dc = *reinterpret_cast<const float2*>(ad + (j * kSeg + blk) * 8);
-                                const int P = block_dot(qs[h], aqb[0], aqb[1], __float_as_int(dc.y));
+                for (int h = 0; h < 2; ++h) {
+                    const int jb = 2 * jp + h;
+                    if (VEC == 16 || jb < nblk) {
+                        uint32_t dbits, lo[4], hi[4];
+                        group_block(bp, h, dbits, lo, hi);
+                        const float d4 = valid ? half_bits_to_float(dbits) : 0.0f;
+                        const uint8_t* cbj = codes + code_off(bl0 + jb, pc);
+                        const uint8_t* ebj = ds + ent_off(bl0 + jb, pc);
+#pragma unroll
+                        for (int j = 0; j < kJ; ++j) {
+                            if (NPC > 0 || j < npc) {
+                                const u32x4* aqb = reinterpret_cast<const u32x4*>(cbj + 32 * j);
+                                const float2 en = *reinterpret_cast<const float2*>(ebj + 8 * j);
+                                const int P = block_dot(lo, hi, aqb[0], aqb[1], __float_as_int(en.y));
                                 if constexpr (kPartials) {
-                                    p.partials[((int64_t)plist[j] * p.N + n) * p.nb + sb + blk] = P;
+                                    if (valid && n < p.N)
+                                        p.partials[((int64_t)plist[j] * p.N + n) * nb + sb + bl0 + jb] = P;
                                 } else {
-                                    acc[j] = __builtin_fmaf((float)P, d4[h] * dc.x, acc[j]);
+                                    acc[j] = __builtin_fmaf((float)P, d4 * en.x, acc[j]);
                                 }
                             }
                         }
@@ -249,30 +328,193 @@ __global__ __launch_bounds__(kThreads) void moe_gemv_kernel(GemvParams p, int sc
                 }
             }
         }
-        if constexpr (!kPartials) {
+        if (t2 != t) {   // the tile's rows are complete (wave-uniform)
+            if constexpr (!kPartials) {
 #pragma unroll
-            for (int j = 0; j < kPairChunk; ++j) {
-                float v = acc[j];
-                v += __shfl_xor(v, 8);
-                v += __shfl_xor(v, 4);
-                v += __shfl_xor(v, 2);
-                v += __shfl_xor(v, 1);
-                acc[j] = v;
+                for (int j = 0; j < kJ; ++j) {
+                    float v = acc[j];
+                    v += __shfl_xor(v, 8);
+                    v += __shfl_xor(v, 4);
+                    v += __shfl_xor(v, 2);
+                    v += __shfl_xor(v, 1);
+                    acc[j] = 0.0f;
+                    if (n < p.N && l == 0 && (NPC > 0 || j < npc)) {
+                        float* o = p.out + (int64_t)plist[j] * p.N + n;
+                        if constexpr (kMultiSeg) {
+                            *o = sb == 0 ? v : *o + v;
+                        } else {
+                            *o = v;
+                        }
+                    }
+                }
             }
-            if (row_ok && l == 0) {
-                for (int j = 0; j < npc; ++j) p.out[(int64_t)plist[j] * p.N + n] = acc[j];
+        }
+        t = t2;
+        ws = ws2;
+    }
+}
+
+template <int VEC, bool kBucketed, bool kPartials, bool kMultiSeg>
+__global__ __launch_bounds__(kThreads, kWavesPerSimd) void moe_gemv_kernel(GemvParams p)
+{
+    extern __shared__ __align__(16) uint8_t lds[];
+    const int64_t nb = p.nb;
+    const LdsLayout L = lds_layout(p.E, p.seg, p.pc_cap, p.list_cap);
+    uint8_t* codes = lds + L.codes;
+    uint8_t* ds = lds + L.ds;
+    uint32_t* bits = reinterpret_cast<uint32_t*>(lds + L.bits);     // routed buckets (E+1 bits)
+    int32_t* prefix = reinterpret_cast<int32_t*>(lds + L.prefix);   // set bits before each word
+    int32_t* plist = reinterpret_cast<int32_t*>(lds + L.plist);     // [kPairChunk] pair ids
+    int32_t* ptok = plist + kPairChunk;                               // [kPairChunk] tokens
+    int32_t* misc = reinterpret_cast<int32_t*>(lds + L.misc);
+    int32_t* slist = reinterpret_cast<int32_t*>(lds + L.list);      // scan mode: the expert's pairs
+
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int l = lane % kLPR, rw = lane / kLPR;   // lane within the row, row within the wave
+    const int words = (int)((p.E + 1 + 31) / 32);
+
+    // ---- the routed buckets (experts with pairs, and E for masked pairs) -------
+    if constexpr (kBucketed) {
+        for (int w = tid; w < words; w += kThreads) {
+            uint32_t m = 0;
+            for (int i = 0; i < 32; ++i) {
+                const int64_t b = 32 * (int64_t)w + i;
+                if (b <= p.E && p.offsets[b + 1] > p.offsets[b]) m |= 1u << i;
+            }
+            bits[w] = m;
+        }
+    } else {
+        for (int w = tid; w < words; w += kThreads) bits[w] = 0;
+        __syncthreads();
+        for (int64_t q = tid; q < p.pairs; q += kThreads) {
+            const int64_t b = bucket_of(p.ids[q], p.E);
+            atomicOr(&bits[b >> 5], 1u << (b & 31));
+        }
+    }
+    __syncthreads();
+    if (tid == 0) {
+        int run = 0;
+        for (int w = 0; w < words; ++w) {
+            prefix[w] = run;
+            run += __popc(bits[w]);
+        }
+        prefix[words] = run;
+    }
+    __syncthreads();
+    const int64_t D = uniform((int32_t)prefix[words]);
+    const int64_t items = D * p.row_tiles;
+    const int64_t i0 = (int64_t)blockIdx.x * items / p.grid, i1 = ((int64_t)blockIdx.x + 1) * items / p.grid;
+    if (i0 >= i1) return;
+
+    for (int64_t d = i0 / p.row_tiles; d * p.row_tiles < i1; ++d) {
+        const int64_t t0 = max<int64_t>(i0 - d * p.row_tiles, 0);
+        const int64_t t1 = min<int64_t>(i1 - d * p.row_tiles, p.row_tiles);
+        // the d-th routed bucket
+        int64_t e = 0;
+        {
+            int lo = 0, hi = words - 1;   // last word with prefix <= d
+            while (lo < hi) {
+                const int mid = (lo + hi + 1) / 2;
+                if (prefix[mid] <= d) lo = mid; else hi = mid - 1;
+            }
+            uint32_t m = bits[lo];
+            for (int64_t k = prefix[lo]; k < d; ++k) m &= m - 1;   // drop the lower set bits
+            e = uniform((int32_t)(32 * lo + __ffs(m) - 1));
+        }
+
+        // ---- the pair list of this bucket ----------------------------------
+        const int32_t* list;
+        int64_t count;
+        __syncthreads();   // the previous bucket is done with the list and the staged rows
+        if constexpr (kBucketed) {
+            const int64_t beg = uniform(p.offsets[e]);
+            count = uniform(p.offsets[e + 1]) - beg;
+            list = p.sorted + beg;
+        } else {
+            if (tid == 0) misc[0] = 0;
+            __syncthreads();
+            for (int64_t base = 0; base < p.pairs; base += kThreads) {
+                const int64_t q = base + tid;
+                const bool match = q < p.pairs && bucket_of(p.ids[q], p.E) == e;
+                const uint64_t mb = __ballot(match);
+                const int below = __builtin_amdgcn_mbcnt_hi((uint32_t)(mb >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)mb, 0));
+                if (lane == 0) misc[2 + wave] = __popcll(mb);
+                __syncthreads();
+                int off = misc[0];
+                for (int w = 0; w < wave; ++w) off += misc[2 + w];
+                if (match) slist[off + below] = (int32_t)q;
+                __syncthreads();
+                if (tid == 0) misc[0] += misc[2] + misc[3] + misc[4] + misc[5];
+                __syncthreads();
+            }
+            count = uniform(misc[0]);
+            list = slist;
+        }
+
+        for (int64_t c0 = 0; c0 < count; c0 += p.pc_cap) {
+            const int npc = (int)min<int64_t>(p.pc_cap, count - c0);
+            __syncthreads();   // the previous chunk is done with plist and the staged rows
+            if (tid < npc) {
+                const int32_t pid = list[c0 + tid];
+                plist[tid] = pid;
+                ptok[tid] = (int32_t)(pid / p.top_k);
+            }
+            __syncthreads();
+
+            if (e == p.E) {   // masked bucket: zero rows of tiles [t0, t1)
+                const int64_t r0 = t0 * kRowsPerTile, r1 = min<int64_t>(t1 * kRowsPerTile, p.N);
+                for (int64_t i = tid; i < (int64_t)npc * (r1 - r0); i += kThreads) {
+                    const int j = (int)(i / (r1 - r0));
+                    const int64_t n = r0 + (i - (int64_t)j * (r1 - r0));
+                    if constexpr (kPartials) {
+                        for (int64_t b = 0; b < nb; ++b) p.partials[((int64_t)plist[j] * p.N + n) * nb + b] = 0;
+                    } else {
+                        p.out[(int64_t)plist[j] * p.N + n] = 0.0f;
+                    }
+                }
+                continue;
+            }
+
+            // K segments: one unless the staged rows would not fit the budget.
+            for (int64_t sb = 0; sb < nb; sb += p.seg) {
+                const int len = (int)min<int64_t>(p.seg, nb - sb);
+                if (sb > 0) __syncthreads();   // the previous segment's activations are consumed
+                stage_acts(p, ptok, npc, sb, len, codes, ds);
+                __syncthreads();
+                uint8_t* wrow = lds + L.wt + wave * kWaveW + rw * kWRowPitch;
+#define FTQ_STREAM(NPC) stream_tiles<VEC, kPartials, kMultiSeg, NPC>(p, e, t0, t1, sb, len, npc, plist, wrow, codes, ds, l, rw, wave)
+                // one or two pairs per expert (decode) without per-pair guards;
+                // more pairs keep the guarded loop, whose guards also stop the
+                // scheduler from interleaving all 8 blocks (which would need
+                // 8 * 10 * npc registers)
+                if (VEC == 16 && npc == 1) {
+                    FTQ_STREAM(1);
+                } else if (VEC == 16 && npc == 2) {
+                    FTQ_STREAM(2);
+                } else {
+                    FTQ_STREAM(0);
+                }
+#undef FTQ_STREAM
             }
         }
     }
 }
 
-template <bool kBucketed, bool kPartials>
-int launch_gemv(int vec, const GemvParams& gp, int scan_cap, int64_t grid, size_t lds, hipStream_t s)
+template <int VEC, bool kBucketed, bool kPartials>
+int launch_seg(bool multi, const GemvParams& gp, size_t lds, hipStream_t s)
 {
+    if (multi) return launch("moe_gemv_kernel", moe_gemv_kernel<VEC, kBucketed, kPartials, true>, gp.grid, kThreads, lds, s, gp);
+    return launch("moe_gemv_kernel", moe_gemv_kernel<VEC, kBucketed, kPartials, false>, gp.grid, kThreads, lds, s, gp);
+}
+
+template <bool kBucketed, bool kPartials>
+int launch_gemv(int vec, const GemvParams& gp, size_t lds, hipStream_t s)
+{
+    const bool multi = gp.seg < gp.nb;
     switch (vec) {
-    case 16: return launch("moe_gemv_kernel<16>", moe_gemv_kernel<16, kBucketed, kPartials>, grid, kThreads, lds, s, gp, scan_cap);
-    case 4: return launch("moe_gemv_kernel<4>", moe_gemv_kernel<4, kBucketed, kPartials>, grid, kThreads, lds, s, gp, scan_cap);
-    default: return launch("moe_gemv_kernel<2>", moe_gemv_kernel<2, kBucketed, kPartials>, grid, kThreads, lds, s, gp, scan_cap);
+    case 16: return launch_seg<16, kBucketed, kPartials>(multi, gp, lds, s);
+    case 4: return launch_seg<4, kBucketed, kPartials>(multi, gp, lds, s);
+    default: return launch_seg<2, kBucketed, kPartials>(multi, gp, lds, s);
     }
 }
 
@@ -291,30 +533,52 @@ int run_gemv(const MoeArgs& m, const BucketPlan* plan, const void* ws, hipStream
     gp.nb = m.K / kQK;
     gp.top_k = m.top_k;
     gp.pairs = m.T * m.top_k;
-    gp.row_tiles = (m.N + kRows - 1) / kRows;
+    gp.row_tiles = (m.N + kRowsPerTile - 1) / kRowsPerTile;
     if (gp.pairs == 0) return FTQ_OK;
+    DeviceLimits lim;
+    int st = device_limits(&lim);
+    if (st != FTQ_OK) return st;
     const bool bucketed = plan != nullptr;
-    int scan_cap = 0;
     if (bucketed) {
         const uint8_t* base = static_cast<const uint8_t*>(ws);
         gp.offsets = reinterpret_cast<const int32_t*>(base + plan->off_offsets);
         gp.sorted = reinterpret_cast<const int32_t*>(base + plan->off_sorted);
+        gp.list_cap = 0;
     } else {
-        scan_cap = (int)gp.pairs;   // caller guarantees pairs <= kGemvScanMaxPairs
+        gp.list_cap = (int)gp.pairs;   // the caller keeps pairs <= kGemvScanMaxPairs
     }
-    // widest copy unit that keeps every staged row segment aligned
+    // a bucket never holds more than T*top_k pairs
+    gp.pc_cap = (int)std::min<int64_t>(kPairChunk, gp.pairs);
+    // K segment: whole rows when the staged activations fit next to the weight
+    // buffers with kTargetWGPerCU workgroups per CU, else the largest multiple
+    // of a step (128 blocks) that fits, so that every step is full
+    const int64_t fixed = lds_layout(m.E, 0, 0, gp.list_cap).bytes;
+    const int64_t budget = std::max<int64_t>(kLdsPerCU / kTargetWGPerCU - fixed, 0);
+    auto act_bytes = [&](int64_t seg) { return code_bytes(seg, gp.pc_cap) + ent_bytes(seg, gp.pc_cap); };
+    if (act_bytes(gp.nb) <= budget) {
+        gp.seg = gp.nb;
+    } else {
+        int64_t seg = kStepBlocks;
+        while (seg + kStepBlocks < gp.nb && act_bytes(seg + kStepBlocks) <= budget) seg += kStepBlocks;
+        gp.seg = seg;
+    }
+    const int64_t lds = lds_layout(m.E, gp.seg, gp.pc_cap, gp.list_cap).bytes;
+    // grid: the workgroups that are resident at once (LDS and registers permitting)
+    const int64_t by_lds = std::max<int64_t>(1, kLdsPerCU / lds);
+    const int64_t per_cu = std::min<int64_t>(by_lds, kWavesPerSimd * 4 / kWaves);
+    const int64_t max_items = (std::min<int64_t>(m.E, gp.pairs) + 1) * gp.row_tiles;
+    gp.grid = std::max<int64_t>(1, std::min<int64_t>((int64_t)lim.cu_count * per_cu, max_items));
+    // widest load unit that keeps every step aligned
     const uintptr_t wa = reinterpret_cast<uintptr_t>(m.w);
     int vec = 2;
     if (gp.nb % 8 == 0 && wa % 16 == 0) vec = 16;
     else if (gp.nb % 2 == 0 && wa % 4 == 0) vec = 4;
-    const int64_t grid = (m.E + 1) * gp.row_tiles;
-    const size_t lds = (size_t)lds_layout(scan_cap).bytes;
     if (bucketed) {
-        return m.partials ? launch_gemv<true, true>(vec, gp, 0, grid, lds, s)
-                          : launch_gemv<true, false>(vec, gp, 0, grid, lds, s);
+        return m.partials ? launch_gemv<true, true>(vec, gp, (size_t)lds, s)
+                          : launch_gemv<true, false>(vec, gp, (size_t)lds, s);
     }
-    return m.partials ? launch_gemv<false, true>(vec, gp, scan_cap, grid, lds, s)
-                      : launch_gemv<false, false>(vec, gp, scan_cap, grid, lds, s);
+    return m.partials ? launch_gemv<false, true>(vec, gp, (size_t)lds, s)
+                      : launch_gemv<false, false>(vec, gp, (size_t)lds, s);
 }
 
 }  // namespace ftq
