@@ -106,19 +106,33 @@ __device__ __forceinline__ void nibbles_to_f16(uint32_t x, uint32_t o[4])
 
 // ---- per-call activation preparation ------------------------------------------
 
-// One lane per Q8_1 block: 32 int8 codes -> 32 fp16 codes in the order of
-// nibbles_to_f16 (pairs (4j, 4j+2), (4j+1, 4j+3), (16+4j, 16+4j+2),
+// Blocks per staged row, padded to whole passes: the padding block has zero
+// codes and zero scale, so the tile loads never need a bounds clamp.
+__host__ __device__ constexpr int64_t padded_blocks(int64_t nb) { return (nb + kKB - 1) / kKB * kKB; }
+
+// One lane per (token, padded block): 32 int8 codes -> 32 fp16 codes in the
+// order of nibbles_to_f16 (pairs (4j, 4j+2), (4j+1, 4j+3), (16+4j, 16+4j+2),
 // (16+4j+1, 16+4j+3) for j = 0..3), and the fp16 scale.
 __global__ __launch_bounds__(kThreads) void prep_activations_kernel(
-    const uint8_t* __restrict__ a, int64_t nblocks, uint8_t* __restrict__ a16, uint16_t* __restrict__ d8)
+    const uint8_t* __restrict__ a, int64_t T, int64_t nb, uint8_t* __restrict__ a16, uint16_t* __restrict__ d8)
 {
+    const int64_t nbp = padded_blocks(nb);
+    const int64_t nblocks = T * nbp;
     const int64_t stride = (int64_t)gridDim.x * kThreads;
-    for (int64_t blk = (int64_t)blockIdx.x * kThreads + threadIdx.x; blk < nblocks; blk += stride) {
-        const uint32_t* src = reinterpret_cast<const uint32_t*>(a + blk * kQ8Bytes);
+    for (int64_t i = (int64_t)blockIdx.x * kThreads + threadIdx.x; i < nblocks; i += stride) {
+        const int64_t t = i / nbp, b = i - t * nbp;
+        u32x4* dst = reinterpret_cast<u32x4*>(a16 + i * kBlockF16);
+        if (b >= nb) {
+#pragma unroll
+            for (int k = 0; k < 4; ++k) dst[k] = u32x4{0, 0, 0, 0};
+            d8[i] = 0;
+            continue;
+        }
+        const uint32_t* src = reinterpret_cast<const uint32_t*>(a + (t * nb + b) * kQ8Bytes);
         uint32_t c[8];
         const uint32_t head = src[0];
 #pragma unroll
-        for (int i = 0; i < 8; ++i) c[i] = src[1 + i];
+        for (int k = 0; k < 8; ++k) c[k] = src[1 + k];
         auto f = [](uint32_t word, int byte) -> uint32_t {
             const _Float16 h = (_Float16)(int)(int8_t)(word >> (8 * byte));   // exact
             return (uint32_t)__builtin_bit_cast(uint16_t, h);
@@ -131,10 +145,9 @@ __global__ __launch_bounds__(kThreads) void prep_activations_kernel(
             o[4 * j + 2] = f(c[4 + j], 0) | (f(c[4 + j], 2) << 16);
             o[4 * j + 3] = f(c[4 + j], 1) | (f(c[4 + j], 3) << 16);
         }
-        u32x4* dst = reinterpret_cast<u32x4*>(a16 + blk * kBlockF16);
 #pragma unroll
-        for (int i = 0; i < 4; ++i) dst[i] = u32x4{o[4 * i], o[4 * i + 1], o[4 * i + 2], o[4 * i + 3]};
-        d8[blk] = (uint16_t)(head & 0xffffu);
+        for (int k = 0; k < 4; ++k) dst[k] = u32x4{o[4 * k], o[4 * k + 1], o[4 * k + 2], o[4 * k + 3]};
+        d8[i] = (uint16_t)(head & 0xffffu);
     }
 }
 
@@ -162,6 +175,7 @@ __global__ __launch_bounds__(kThreads, 2) void moe_grouped_kernel(GroupedParams 
     const int64_t work = total_tiles * p.n_tiles_n;
     const bool direct = (int64_t)gridDim.x >= work;   // one workgroup per tile: remap by XCD
     const int64_t nb = p.nb;
+    const int64_t nbp = padded_blocks(nb);
 
     for (int64_t w = blockIdx.x; w < work; w += gridDim.x) {
         const int64_t L = direct ? xcd_remap(w, work) : w;
@@ -208,62 +222,54 @@ __global__ __launch_bounds__(kThreads, 2) void moe_grouped_kernel(GroupedParams 
         }
 
         // ---- per-tile staging plan ------------------------------------------
-        // Offsets are relative to bases that advance by a constant per stage;
-        // loads are never predicated: a row past the tile (A) or past N (B) is
-        // computed but never stored, and a block past K/32 is read from block
-        // K/32-1 with its weight scale set to 0, so it adds fma(P, 0, acc) =
-        // acc exactly.
+        // Every address is a per-thread offset fixed for the tile plus a base
+        // that is uniform across the workgroup and advances by a constant per
+        // pass.  Rows past the tile (A) or past N (B) read valid memory and are
+        // never stored.  The activations are padded to whole passes; a weight
+        // block past K/32 (odd K/32, last pass only) is read from block K/32-1
+        // with scale 0, so it adds fma(P, 0, acc) = acc exactly.
         // A: BM rows x kKB blocks x 64 B = BM*8 units of 16 B (unit c of a row: block c/4, piece c%4)
         constexpr int kAUnits = BM * kKB * 4;
         constexpr int kAPer = (kAUnits + kThreads - 1) / kThreads;
         static_assert(kAUnits % kThreads == 0, "whole A units per thread");
         using AOff = typename std::conditional<kWide, int64_t, uint32_t>::type;
         AOff a_off_g[kAPer];
-        int a_blk[kAPer];
 #pragma unroll
         for (int i = 0; i < kAPer; ++i) {
             const int u = tid + i * kThreads;
             const int m = u >> 3, c = u & 7;
-            a_blk[i] = c >> 2;
-            a_off_g[i] = (AOff)(((int64_t)sm.row_tok[m < rows ? m : 0] * nb + (c >> 2)) * kBlockF16 + (c & 3) * 16);
+            a_off_g[i] = (AOff)(((int64_t)sm.row_tok[m < rows ? m : 0] * nbp + (c >> 2)) * kBlockF16 + (c & 3) * 16);
         }
         // A scales: thread < BM*kKB owns (row tid % BM, block tid / BM)
         const int d_m = tid % BM, d_blk = tid / BM;
-        const AOff d_off = (AOff)((int64_t)sm.row_tok[d_m < rows ? d_m : 0] * nb + d_blk);
-        // B: one block (18 B) of one weight row per thread
+        const AOff d_off = (AOff)((int64_t)sm.row_tok[d_m < rows ? d_m : 0] * nbp + d_blk);
+        // B: one block (18 B) of one weight row per thread; bh is uniform per wave
         static_assert(kBN * kKB == kThreads, "one weight block per thread");
         const int bn = tid % kBN, bh = tid / kBN;
         const uint8_t* wtile = p.w + (bucket * p.N + n0) * nb * kQ4Bytes;   // uniform per tile
-        const uint32_t bg_off = (uint32_t)(((n0 + bn < p.N ? bn : 0) * nb + bh) * kQ4Bytes);
+        const uint32_t bg_off = (uint32_t)((n0 + bn < p.N ? bn : 0) * nb * kQ4Bytes);
 
         u32x4 ra[kAPer];
         uint32_t rb[5];
-        uint32_t rd8;
+        uint32_t rd8 = 0;
         bool rb_ok;
 
         auto issue = [&](int64_t kb0) {
-            // the last block stands in for blocks past K/32 (kb0 + c < nb fails only in the last stage)
-            const int64_t kl = nb - 1;
+            const uint8_t* abase = p.a16 + kb0 * kBlockF16;
 #pragma unroll
-            for (int i = 0; i < kAPer; ++i) {
-                const int64_t shift = (kb0 + a_blk[i] < nb ? kb0 : kl - a_blk[i]) * kBlockF16;
-                ra[i] = *reinterpret_cast<const u32x4*>(p.a16 + shift + a_off_g[i]);
-            }
-            if (tid < BM * kKB) {
-                const int64_t shift = kb0 + d_blk < nb ? kb0 : kl - d_blk;
-                rd8 = p.d8[shift + d_off];
-            }
+            for (int i = 0; i < kAPer; ++i) ra[i] = *reinterpret_cast<const u32x4*>(abase + a_off_g[i]);
+            if (tid < BM * kKB) rd8 = p.d8[kb0 + d_off];
+            // past K/32 only in the last pass of an odd K/32; uniform per wave
             rb_ok = kb0 + bh < nb;
-            const int64_t kbs = rb_ok ? kb0 : kl - bh;
-            const uint8_t* bp = wtile + kbs * kQ4Bytes + bg_off;
+            const int64_t kb = rb_ok ? kb0 + bh : nb - 1;
             if constexpr (VEC == 4) {
                 // a pair of blocks starts 4-byte aligned (K/32 even, kb0 even):
                 // block kb0 is words 0..4 of the pair, block kb0+1 words 4..8
-                const uint32_t* wp = reinterpret_cast<const uint32_t*>(bp - 18 * bh) + 4 * bh;
+                const uint32_t* wp = reinterpret_cast<const uint32_t*>(wtile + bg_off + kb0 * kQ4Bytes) + 4 * bh;
 #pragma unroll
                 for (int i = 0; i < 5; ++i) rb[i] = wp[i];
             } else {
-                const uint16_t* hp = reinterpret_cast<const uint16_t*>(bp);
+                const uint16_t* hp = reinterpret_cast<const uint16_t*>(wtile + bg_off + kb * kQ4Bytes);
                 rb[0] = hp[0];
 #pragma unroll
                 for (int i = 0; i < 4; ++i) rb[1 + i] = (uint32_t)hp[1 + 2 * i] | ((uint32_t)hp[2 + 2 * i] << 16);
@@ -324,61 +330,65 @@ __global__ __launch_bounds__(kThreads, 2) void moe_grouped_kernel(GroupedParams 
             for (int j = 0; j < S::SN; ++j)
 #pragma unroll
                 for (int k = 0; k < 16; ++k) acc[i][j][k] = 0.0f;
-        // scale operands of the outer product d8 (x) d4: one fp16 in k slot 0, zeros elsewhere
-        u32x4 as_v[S::SM], bs_v[S::SN];
-#pragma unroll
-        for (int i = 0; i < S::SM; ++i) as_v[i] = u32x4{0, 0, 0, 0};
-#pragma unroll
-        for (int j = 0; j < S::SN; ++j) bs_v[j] = u32x4{0, 0, 0, 0};
 
-        // One staged pass: kKB blocks from LDS buffer `buf`.  A block past K/32
-        // has weight scale 0 and adds fma(P, 0, acc) = acc exactly.
+        // One staged pass: kKB blocks from LDS buffer `buf`.  (Issuing the next
+        // sub-tile's MFMAs before the current FMAs needs a second set of result
+        // registers and spills at BM = 128; two waves per SIMD overlap instead.)
         auto compute = [&](int buf, int64_t kb0) {
 #pragma unroll 1
             for (int blk = 0; blk < kKB; ++blk) {
                 v8h alo[S::SM], ahi[S::SM], blo[S::SN], bhi[S::SN];
+                u32x4 as_v[S::SM], bs_v[S::SN];
 #pragma unroll
                 for (int ii = 0; ii < S::SM; ++ii) {
                     const uint8_t* src = &sm.a[buf][a_off[ii] + blk * kBlockF16];
                     alo[ii] = *reinterpret_cast<const v8h*>(src);
                     ahi[ii] = *reinterpret_cast<const v8h*>(src + 16);
-                    as_v[ii].x = sm.as[buf][blk][as_off[ii]];
+                    as_v[ii] = u32x4{sm.as[buf][blk][as_off[ii]], 0, 0, 0};
                 }
 #pragma unroll
                 for (int jj = 0; jj < S::SN; ++jj) {
                     const uint8_t* src = &sm.b[buf][b_off[jj] + blk * kBlockF16];
                     blo[jj] = *reinterpret_cast<const v8h*>(src);
                     bhi[jj] = *reinterpret_cast<const v8h*>(src + 16);
-                    bs_v[jj].x = sm.bs[buf][blk][bs_off[jj]];
+                    bs_v[jj] = u32x4{sm.bs[buf][blk][bs_off[jj]], 0, 0, 0};
                 }
+                constexpr int kSub = S::SM * S::SN;
+                v16f P, Sc;
+                auto mfmas = [&](int t, v16f& Pt, v16f& St) {
+                    const int i = t / S::SN, j = t % S::SN;
+                    Pt = __builtin_amdgcn_mfma_f32_32x32x16_f16(alo[i], blo[j], v16f{}, 0, 0, 0);
+                    Pt = __builtin_amdgcn_mfma_f32_32x32x16_f16(ahi[i], bhi[j], Pt, 0, 0, 0);
+                    if constexpr (!kPartials)
+                        St = __builtin_amdgcn_mfma_f32_32x32x16_f16(
+                            __builtin_bit_cast(v8h, as_v[i]), __builtin_bit_cast(v8h, bs_v[j]), v16f{}, 0, 0, 0);
+                };
+                auto consume = [&](int t, const v16f& Pt, const v16f& St) {
+                    const int i = t / S::SN, j = t % S::SN;
+                    if constexpr (kPartials) {
+                        const int64_t n = n0 + (wn * S::SN + j) * 32 + l32;
+                        const int64_t b = kb0 + blk;
 #pragma unroll
-                for (int i = 0; i < S::SM; ++i) {
-#pragma unroll
-                    for (int j = 0; j < S::SN; ++j) {
-                        v16f P = __builtin_amdgcn_mfma_f32_32x32x16_f16(alo[i], blo[j], v16f{}, 0, 0, 0);
-                        P = __builtin_amdgcn_mfma_f32_32x32x16_f16(ahi[i], bhi[j], P, 0, 0, 0);
-                        if constexpr (kPartials) {
-                            const int64_t n = n0 + (wn * S::SN + j) * 32 + l32;
-                            const int64_t b = kb0 + blk;
-#pragma unroll
-                            for (int r = 0; r < 16; ++r) {
-                                const int m = (wm * S::SM + i) * 32 + 8 * (r / 4) + 4 * half + (r % 4);
-                                if (m < rows && n < p.N && b < nb)
-                                    p.partials[((int64_t)sm.row_pair[m] * p.N + n) * nb + b] = (int32_t)P[r];
-                            }
-                        } else {
-                            const v16f Sc = __builtin_amdgcn_mfma_f32_32x32x16_f16(
-                                __builtin_bit_cast(v8h, as_v[i]), __builtin_bit_cast(v8h, bs_v[j]), v16f{}, 0, 0, 0);
-#pragma unroll
-                            for (int r = 0; r < 16; ++r) acc[i][j][r] = __builtin_fmaf(P[r], Sc[r], acc[i][j][r]);
+                        for (int r = 0; r < 16; ++r) {
+                            const int m = (wm * S::SM + i) * 32 + 8 * (r / 4) + 4 * half + (r % 4);
+                            if (m < rows && n < p.N && b < nb)
+                                p.partials[((int64_t)sm.row_pair[m] * p.N + n) * nb + b] = (int32_t)Pt[r];
                         }
+                    } else {
+#pragma unroll
+                        for (int r = 0; r < 16; ++r) acc[i][j][r] = __builtin_fmaf(Pt[r], St[r], acc[i][j][r]);
                     }
+                };
+#pragma unroll
+                for (int t = 0; t < kSub; ++t) {
+                    mfmas(t, P, Sc);
+                    consume(t, P, Sc);
                 }
             }
         };
 
         // ---- K loop: double-buffered, unrolled by two so buffers are constants
-        const int64_t nstages = (nb + kKB - 1) / kKB;
+        const int64_t nstages = nbp / kKB;
         issue(0);
         commit(0);
         __syncthreads();
@@ -443,9 +453,9 @@ int64_t grouped_tile_m(const MoeArgs& m)
 
 int64_t grouped_prep_bytes(int64_t T, int64_t K)
 {
-    const int64_t nb = K / kQK;
+    const int64_t nbp = padded_blocks(K / kQK);
     auto align = [](int64_t v) { return (v + 255) / 256 * 256; };
-    return align(T * nb * kBlockF16) + align(T * nb * 2);
+    return align(T * nbp * kBlockF16) + align(T * nbp * 2);
 }
 
 int run_grouped(const MoeArgs& m, const BucketPlan& plan, void* ws, hipStream_t s)
@@ -457,14 +467,15 @@ int run_grouped(const MoeArgs& m, const BucketPlan& plan, void* ws, hipStream_t 
     uint8_t* base = static_cast<uint8_t*>(ws);
     const int64_t nb = m.K / kQK;
     auto align = [](int64_t v) { return (v + 255) / 256 * 256; };
+    const int64_t nbp = padded_blocks(nb);
     uint8_t* a16 = base + plan.bytes;
-    uint16_t* d8 = reinterpret_cast<uint16_t*>(a16 + align(m.T * nb * kBlockF16));
+    uint16_t* d8 = reinterpret_cast<uint16_t*>(a16 + align(m.T * nbp * kBlockF16));
 
-    // activations -> fp16 codes + scales (once per call)
-    const int64_t nblocks = m.T * nb;
+    // activations -> fp16 codes + scales, padded to whole passes (once per call)
+    const int64_t nblocks = m.T * nbp;
     st = launch("prep_activations_kernel", prep_activations_kernel,
                 stride_grid((nblocks + kThreads - 1) / kThreads, lim), kThreads, 0, s,
-                static_cast<const uint8_t*>(m.a), nblocks, a16, d8);
+                static_cast<const uint8_t*>(m.a), m.T, nb, a16, d8);
     if (st != FTQ_OK) return st;
 
     GroupedParams gp{};
@@ -492,7 +503,7 @@ int run_grouped(const MoeArgs& m, const BucketPlan& plan, void* ws, hipStream_t 
     // activation offsets fit 32 bits unless the staged activations reach 4 GiB;
     // FTQ_FORCE_WIDE=1 selects the 64-bit variant at any size (tests)
     static const bool force_wide = [] { const char* v = getenv("FTQ_FORCE_WIDE"); return v && v[0] == '1'; }();
-    const bool wide = force_wide || m.T * nb * kBlockF16 >= ((int64_t)1 << 32);
+    const bool wide = force_wide || m.T * nbp * kBlockF16 >= ((int64_t)1 << 32);
     switch (bm) {
     case 128: return part ? launch_grouped<128, true>(vec, wide, gp, grid, s) : launch_grouped<128, false>(vec, wide, gp, grid, s);
     case 64: return part ? launch_grouped<64, true>(vec, wide, gp, grid, s) : launch_grouped<64, false>(vec, wide, gp, grid, s);
