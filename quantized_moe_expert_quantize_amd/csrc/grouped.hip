@@ -68,10 +68,21 @@ struct GroupedParams {
     int64_t E, N, nb, top_k, nbuckets, n_tiles_n, max_mt;
 };
 
+// Waves per workgroup for BM = 128 tiles.  4 waves of 64x64 (two workgroups
+// per CU, two waves per SIMD) measure fastest; 8 waves of 32x64 need 128
+// VGPRs for four waves per SIMD and spill, and at one workgroup per CU they
+// lose the overlap between workgroups.
+constexpr int kWaves128 = 4;
+
 template <int BM>
 struct Shape {
-    static constexpr int WM = BM >= 64 ? 2 : 1;          // waves along M
-    static constexpr int WN = 4 / WM;                    // waves along N
+    static constexpr int kWaves = BM == 128 ? kWaves128 : 4;
+    static constexpr int kThreads = 64 * kWaves;
+    // register budget: two workgroups per CU (HIP reads the second launch
+    // bound as waves per SIMD)
+    static constexpr int kWavesPerSimd = 2 * kWaves / 4;
+    static constexpr int WM = kWaves == 8 ? 4 : (BM >= 64 ? 2 : 1);   // waves along M
+    static constexpr int WN = kWaves / WM;               // waves along N
     static constexpr int SM = BM / (32 * WM);            // 32x32 sub-tiles per wave along M
     static constexpr int SN = kBN / (32 * WN);           // ... along N
     static_assert(SM >= 1 && SN >= 1, "tile shape");
@@ -163,9 +174,10 @@ __device__ __forceinline__ int64_t xcd_remap(int64_t bid, int64_t G)
 }
 
 template <int BM, int VEC, bool kWide, bool kPartials>
-__global__ __launch_bounds__(kThreads, 2) void moe_grouped_kernel(GroupedParams p)
+__global__ __launch_bounds__(Shape<BM>::kThreads, Shape<BM>::kWavesPerSimd) void moe_grouped_kernel(GroupedParams p)
 {
     using S = Shape<BM>;
+    constexpr int kThreads = S::kThreads;
     __shared__ __align__(16) Smem<BM> sm;
 
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -243,9 +255,11 @@ __global__ __launch_bounds__(kThreads, 2) void moe_grouped_kernel(GroupedParams 
         // A scales: thread < BM*kKB owns (row tid % BM, block tid / BM)
         const int d_m = tid % BM, d_blk = tid / BM;
         const AOff d_off = (AOff)((int64_t)sm.row_tok[d_m < rows ? d_m : 0] * nbp + d_blk);
-        // B: one block (18 B) of one weight row per thread; bh is uniform per wave
-        static_assert(kBN * kKB == kThreads, "one weight block per thread");
-        const int bn = tid % kBN, bh = tid / kBN;
+        // B: one block (18 B) of one weight row per thread of the first
+        // kBN * kKB threads; bh is uniform per wave
+        static_assert(kBN * kKB <= kThreads, "one weight block per thread");
+        const bool b_thread = tid < kBN * kKB;
+        const int bn = tid % kBN, bh = (tid / kBN) % kKB;
         const uint8_t* wtile = p.w + (bucket * p.N + n0) * nb * kQ4Bytes;   // uniform per tile
         const uint32_t bg_off = (uint32_t)((n0 + bn < p.N ? bn : 0) * nb * kQ4Bytes);
 
@@ -262,6 +276,7 @@ __global__ __launch_bounds__(kThreads, 2) void moe_grouped_kernel(GroupedParams 
             // past K/32 only in the last pass of an odd K/32; uniform per wave
             rb_ok = kb0 + bh < nb;
             const int64_t kb = rb_ok ? kb0 + bh : nb - 1;
+            if (!b_thread) return;
             if constexpr (VEC == 4) {
                 // a pair of blocks starts 4-byte aligned (K/32 even, kb0 even):
                 // block kb0 is words 0..4 of the pair, block kb0+1 words 4..8
@@ -282,6 +297,7 @@ __global__ __launch_bounds__(kThreads, 2) void moe_grouped_kernel(GroupedParams 
                 *reinterpret_cast<u32x4*>(&sm.a[buf][(u >> 3) * kRowBytes + (u & 7) * 16]) = ra[i];
             }
             if (tid < BM * kKB) sm.as[buf][d_blk][d_m] = rd8;
+            if (!b_thread) return;
             // weight block -> 32 fp16 values (q - 8) and its scale
             uint32_t dbits, qs[4];
             if constexpr (VEC == 4) {
@@ -383,6 +399,9 @@ __global__ __launch_bounds__(kThreads, 2) void moe_grouped_kernel(GroupedParams 
                 for (int t = 0; t < kSub; ++t) {
                     mfmas(t, P, Sc);
                     consume(t, P, Sc);
+                    // one sub-tile's results live at a time (the register budget
+                    // of four waves per SIMD has no room for two)
+                    if constexpr (S::kWaves == 8) __builtin_amdgcn_sched_barrier(0);
                 }
             }
         };
@@ -405,14 +424,19 @@ __global__ __launch_bounds__(kThreads, 2) void moe_grouped_kernel(GroupedParams 
         }
 
         if constexpr (!kPartials) {
+            // row and column of this lane's outputs, made opaque here so that
+            // the compiler does not compute them before the K loop and keep them
+            // live through it
+            int l32e = l32, halfe = half;
+            __asm__ volatile("" : "+v"(l32e), "+v"(halfe));
 #pragma unroll
             for (int i = 0; i < S::SM; ++i) {
 #pragma unroll
                 for (int j = 0; j < S::SN; ++j) {
-                    const int64_t n = n0 + (wn * S::SN + j) * 32 + l32;
+                    const int64_t n = n0 + (wn * S::SN + j) * 32 + l32e;
 #pragma unroll
                     for (int r = 0; r < 16; ++r) {
-                        const int m = (wm * S::SM + i) * 32 + 8 * (r / 4) + 4 * half + (r % 4);
+                        const int m = (wm * S::SM + i) * 32 + 8 * (r / 4) + 4 * halfe + (r % 4);
                         if (m < rows && n < p.N)
                             __builtin_nontemporal_store(acc[i][j][r], &p.out[(int64_t)sm.row_pair[m] * p.N + n]);
                     }
@@ -425,12 +449,13 @@ __global__ __launch_bounds__(kThreads, 2) void moe_grouped_kernel(GroupedParams 
 template <int BM, bool kPartials>
 int launch_grouped(int vec, bool wide, const GroupedParams& gp, int64_t grid, hipStream_t s)
 {
+    constexpr int kT = Shape<BM>::kThreads;
     if (vec == 4) {
-        return wide ? launch("moe_grouped_kernel<4,wide>", moe_grouped_kernel<BM, 4, true, kPartials>, grid, kThreads, 0, s, gp)
-                    : launch("moe_grouped_kernel<4>", moe_grouped_kernel<BM, 4, false, kPartials>, grid, kThreads, 0, s, gp);
+        return wide ? launch("moe_grouped_kernel<4,wide>", moe_grouped_kernel<BM, 4, true, kPartials>, grid, kT, 0, s, gp)
+                    : launch("moe_grouped_kernel<4>", moe_grouped_kernel<BM, 4, false, kPartials>, grid, kT, 0, s, gp);
     }
-    return wide ? launch("moe_grouped_kernel<2,wide>", moe_grouped_kernel<BM, 2, true, kPartials>, grid, kThreads, 0, s, gp)
-                : launch("moe_grouped_kernel<2>", moe_grouped_kernel<BM, 2, false, kPartials>, grid, kThreads, 0, s, gp);
+    return wide ? launch("moe_grouped_kernel<2,wide>", moe_grouped_kernel<BM, 2, true, kPartials>, grid, kT, 0, s, gp)
+                : launch("moe_grouped_kernel<2>", moe_grouped_kernel<BM, 2, false, kPartials>, grid, kT, 0, s, gp);
 }
 
 }  // namespace
