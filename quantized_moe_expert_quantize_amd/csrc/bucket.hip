@@ -1,16 +1,23 @@
 // Bucketing of the flat (token, top-k) pairs by routed expert, for the
-// expert-sorted paths: per-chunk expert histogram -> exclusive scan into
-// per-expert segment offsets (the "expert_offsets" of "Current Bug:
-// CuTeDSLMoERunner", Bug 4, kept here WITH the leading 0 and the total) and a
-// per-expert tile count scan -> stable scatter of pair ids into their expert's
-// segment.  Ids outside [0, E) go to one extra bucket E, whose rows the matmul
-// writes as zeros (that page's Bug 8: non-local experts are masked).
+// expert-sorted paths: per-chunk expert histogram -> one exclusive scan that
+// yields the per-expert segment offsets (the "expert_offsets" of "Current
+// Bug: CuTeDSLMoERunner", Bug 4, kept here WITH the leading 0 and the total),
+// every chunk's base inside its expert's segment, and the per-expert tile
+// table -> stable scatter of pair ids into their expert's segment.  Ids
+// outside [0, E) go to one extra bucket E, whose rows the matmul writes as
+// zeros (that page's Bug 8: non-local experts are masked).
+//
+// The counts are stored bucket-major, counts[b][c] for bucket b and chunk c,
+// so a single flat exclusive scan over them gives, at [b][c], the sorted
+// position of chunk c's first pair of bucket b: the pairs of lower buckets,
+// then those of bucket b in earlier chunks.
 //
 // Every pass is deterministic: counts do not depend on the order of LDS
-// atomics, and the scatter orders each chunk with a bitonic sort on the unique
-// key (bucket, position), so a bucket's segment lists its pairs in ascending
-// pair order.  Nothing is read back to the host, so the whole sequence can be
-// captured in a HIP graph ("Cudagraph Constraints" on the same page).
+// atomics, and the scatter walks each chunk in pair order (one wave per chunk,
+// 64 pairs per step, ranks within a step from ballots), so a bucket's segment
+// lists its pairs in ascending pair order.  Nothing is read back to the host,
+// so the whole sequence can be captured in a HIP graph ("Cudagraph
+// Constraints" on the same page).
 #include "ftq_internal.h"
 
 namespace ftq {
@@ -18,16 +25,15 @@ namespace {
 
 constexpr int kCountThreads = 256;
 constexpr int kScanThreads = 1024;
-constexpr int kSortThreads = 256;
-constexpr uint32_t kPadKey = 0xffffffffu;
-constexpr int kPosBits = 10;   // kBucketChunk == 1 << kPosBits
-static_assert(kBucketChunk == (1 << kPosBits), "chunk size must match the key layout");
+constexpr int kScanPer = 8;                  // elements per thread and pass of the flat scan
+constexpr int kScatterWaves = 4;             // chunks per scatter workgroup (one wave each)
+constexpr int kKeyBits = 12;                 // bucket ids < 4096
 
 __device__ __forceinline__ int bucket_of(int32_t id, int32_t E) { return (id >= 0 && id < E) ? id : E; }
 
-// Pass 1: counts[c][b] = number of pairs of chunk c in bucket b.
+// Pass 1: counts[b][c] = number of pairs of chunk c in bucket b.
 __global__ __launch_bounds__(kCountThreads) void bucket_count_kernel(
-    const int32_t* __restrict__ ids, int64_t pairs, int32_t E, int32_t nbuckets,
+    const int32_t* __restrict__ ids, int64_t pairs, int32_t E, int32_t nbuckets, int64_t nchunks,
     int32_t* __restrict__ counts)
 {
     extern __shared__ int32_t hist[];
@@ -40,119 +46,129 @@ __global__ __launch_bounds__(kCountThreads) void bucket_count_kernel(
         if (p < pairs) atomicAdd(&hist[bucket_of(ids[p], E)], 1);
     }
     __syncthreads();
-    int32_t* row = counts + c * (int64_t)nbuckets;
-    for (int b = threadIdx.x; b < nbuckets; b += kCountThreads) row[b] = hist[b];
+    for (int b = threadIdx.x; b < nbuckets; b += kCountThreads) counts[(int64_t)b * nchunks + c] = hist[b];
 }
 
-// Exclusive block-wide scan of v[0..n) in LDS (n <= kMaxScan), result in place;
-// returns the total.  All threads of the block must call it.
-__device__ int32_t block_exclusive_scan(int32_t* v, int n, int32_t* warp_tmp)
-{
-    // Each thread owns a contiguous run of ceil(n / blockDim) entries.
-    const int per = (n + kScanThreads - 1) / kScanThreads;
-    const int beg = min(n, (int)threadIdx.x * per), end = min(n, beg + per);
-    int32_t local = 0;
-    for (int i = beg; i < end; ++i) local += v[i];
-    // inclusive scan of `local` across the block: wave scan, then over waves
-    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-    int32_t x = local;
-#pragma unroll
-    for (int o = 1; o < 64; o <<= 1) {
-        int32_t y = __shfl_up(x, o);
-        if (lane >= o) x += y;
-    }
-    if (lane == 63) warp_tmp[wave] = x;
-    __syncthreads();
-    if (threadIdx.x == 0) {
-        int32_t run = 0;
-        for (int w = 0; w < kScanThreads / 64; ++w) { int32_t t = warp_tmp[w]; warp_tmp[w] = run; run += t; }
-        warp_tmp[kScanThreads / 64] = run;
-    }
-    __syncthreads();
-    int32_t run = warp_tmp[wave] + x - local;   // exclusive prefix of this thread's run
-    for (int i = beg; i < end; ++i) { int32_t t = v[i]; v[i] = run; run += t; }
-    const int32_t total = warp_tmp[kScanThreads / 64];
-    __syncthreads();
-    return total;
-}
-
-// Pass 2 (one block): bucket offsets, per-chunk bases (in place over counts),
-// and the per-bucket first-tile table.
+// Pass 2 (one block): flat exclusive scan of counts[nbuckets][nchunks] in
+// place, the bucket offsets (offsets[b] = scanned[b][0], offsets[nbuckets] =
+// pairs) and the exclusive scan of per-bucket tile counts.
 __global__ __launch_bounds__(kScanThreads) void bucket_scan_kernel(
     int32_t* __restrict__ counts, int64_t nchunks, int32_t nbuckets, int32_t tile_m,
     int32_t* __restrict__ offsets, int32_t* __restrict__ tiles)
 {
-    extern __shared__ int32_t lds[];
-    int32_t* tot = lds;                       // [nbuckets]
-    int32_t* ntile = lds + nbuckets;          // [nbuckets]
-    __shared__ int32_t warp_tmp[kScanThreads / 64 + 1];
+    extern __shared__ int32_t off_lds[];          // [nbuckets + 1] bucket offsets
+    __shared__ int32_t wsum[kScanThreads / 64 + 1];
+    __shared__ int32_t carry_s;
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int64_t len = (int64_t)nbuckets * nchunks;
+    if (threadIdx.x == 0) carry_s = 0;
+    __syncthreads();
+    for (int64_t base = 0; base < len; base += (int64_t)kScanThreads * kScanPer) {
+        const int64_t i0 = base + (int64_t)threadIdx.x * kScanPer;
+        int32_t v[kScanPer];
+        int32_t local = 0;
+#pragma unroll
+        for (int k = 0; k < kScanPer; ++k) {
+            v[k] = i0 + k < len ? counts[i0 + k] : 0;
+            local += v[k];
+        }
+        // inclusive scan of the per-thread totals: within the wave, then over waves
+        int32_t x = local;
+#pragma unroll
+        for (int o = 1; o < 64; o <<= 1) {
+            const int32_t y = __shfl_up(x, o);
+            if (lane >= o) x += y;
+        }
+        if (lane == 63) wsum[wave] = x;
+        __syncthreads();
+        if (threadIdx.x == 0) {
+            int32_t run = carry_s;
+            for (int w = 0; w < kScanThreads / 64; ++w) {
+                const int32_t t = wsum[w];
+                wsum[w] = run;
+                run += t;
+            }
+            wsum[kScanThreads / 64] = run;
+        }
+        __syncthreads();
+        int32_t run = wsum[wave] + x - local;   // exclusive prefix of this thread's run
+#pragma unroll
+        for (int k = 0; k < kScanPer; ++k) {
+            const int64_t i = i0 + k;
+            if (i < len) {
+                counts[i] = run;
+                if (i % nchunks == 0) off_lds[i / nchunks] = run;   // first chunk of bucket i / nchunks
+            }
+            run += v[k];
+        }
+        __syncthreads();
+        if (threadIdx.x == 0) carry_s = wsum[kScanThreads / 64];
+        __syncthreads();
+    }
+    if (threadIdx.x == 0) off_lds[nbuckets] = carry_s;
+    __syncthreads();
+    // bucket offsets, and the tile table from the per-bucket totals
+    int32_t* ntile = off_lds + nbuckets + 1;       // [nbuckets] scratch
+    for (int b = threadIdx.x; b <= nbuckets; b += kScanThreads) offsets[b] = off_lds[b];
     for (int b = threadIdx.x; b < nbuckets; b += kScanThreads) {
-        int32_t s = 0;
-        for (int64_t c = 0; c < nchunks; ++c) s += counts[c * nbuckets + b];
-        tot[b] = s;
-        ntile[b] = tile_m > 0 ? (s + tile_m - 1) / tile_m : 0;
+        const int32_t n = off_lds[b + 1] - off_lds[b];
+        ntile[b] = tile_m > 0 ? (n + tile_m - 1) / tile_m : 0;
     }
     __syncthreads();
-    // tot -> exclusive offsets
-    const int32_t total = block_exclusive_scan(tot, nbuckets, warp_tmp);
-    const int32_t total_tiles = block_exclusive_scan(ntile, nbuckets, warp_tmp);
-    for (int b = threadIdx.x; b < nbuckets; b += kScanThreads) {
-        offsets[b] = tot[b];
-        tiles[b] = ntile[b];
-        int32_t run = tot[b];
-        for (int64_t c = 0; c < nchunks; ++c) {
-            int32_t n = counts[c * nbuckets + b];
-            counts[c * nbuckets + b] = run;
-            run += n;
-        }
-    }
     if (threadIdx.x == 0) {
-        offsets[nbuckets] = total;
-        tiles[nbuckets] = total_tiles;
+        int32_t run = 0;
+        for (int b = 0; b < nbuckets; ++b) {
+            const int32_t t = ntile[b];
+            ntile[b] = run;
+            run += t;
+        }
+        ntile[nbuckets] = run;
     }
+    __syncthreads();
+    for (int b = threadIdx.x; b <= nbuckets; b += kScanThreads) tiles[b] = ntile[b];
 }
 
-// Pass 3: sort each chunk by (bucket, position) and scatter pair ids to
-// bases[c][b] + (rank within the chunk's run of bucket b).
-__global__ __launch_bounds__(kSortThreads) void bucket_scatter_kernel(
-    const int32_t* __restrict__ ids, int64_t pairs, int32_t E, int32_t nbuckets,
+// Lanes of a wave share the per-bucket counters in LDS; the hardware keeps a
+// wave's LDS accesses in order and the fence keeps the compiler from moving
+// one lane's access across another lane's.
+__device__ __forceinline__ void wave_lds_fence() { __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront"); }
+
+// Pass 3: one wave per chunk walks its pairs in order, 64 at a time.  A pair's
+// slot is bases[b][c] + (pairs of bucket b earlier in the chunk): the count
+// from earlier steps (an LDS counter per bucket) plus the lanes below it in
+// this step with the same bucket (found with one ballot per key bit).
+__global__ __launch_bounds__(64 * kScatterWaves) void bucket_scatter_kernel(
+    const int32_t* __restrict__ ids, int64_t pairs, int32_t E, int32_t nbuckets, int64_t nchunks,
     const int32_t* __restrict__ bases, int32_t* __restrict__ sorted)
 {
-    __shared__ uint32_t key[kBucketChunk];
-    const int64_t c = blockIdx.x;
+    extern __shared__ int32_t seen_all[];        // [kScatterWaves][nbuckets]
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int64_t c = (int64_t)blockIdx.x * kScatterWaves + wave;
+    if (c >= nchunks) return;                    // whole waves only: no barrier follows
+    int32_t* seen = seen_all + wave * nbuckets;
+    for (int b = lane; b < nbuckets; b += 64) seen[b] = 0;
+    wave_lds_fence();
+    const uint64_t below = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
     const int64_t base = c * kBucketChunk;
-    for (int i = threadIdx.x; i < kBucketChunk; i += kSortThreads) {
-        const int64_t p = base + i;
-        key[i] = (p < pairs) ? (((uint32_t)bucket_of(ids[p], E) << kPosBits) | (uint32_t)i) : kPadKey;
-    }
-    __syncthreads();
-    // bitonic sort, ascending; keys are unique (the position is part of the key)
-    for (int k = 2; k <= kBucketChunk; k <<= 1) {
-        for (int j = k >> 1; j > 0; j >>= 1) {
-            for (int i = threadIdx.x; i < kBucketChunk; i += kSortThreads) {
-                const int ixj = i ^ j;
-                if (ixj > i) {
-                    const uint32_t a = key[i], b = key[ixj];
-                    const bool ascending = (i & k) == 0;
-                    if ((a > b) == ascending) { key[i] = b; key[ixj] = a; }
-                }
-            }
-            __syncthreads();
+    for (int i = 0; i < kBucketChunk; i += 64) {
+        const int64_t p = base + i + lane;
+        const bool live = p < pairs;
+        const int32_t b = live ? bucket_of(ids[p], E) : -1;
+        // lanes holding the same bucket: agree on every key bit (and are live)
+        uint64_t same = __ballot(live);
+#pragma unroll
+        for (int k = 0; k < kKeyBits; ++k) {
+            const uint64_t ones = __ballot(live && ((b >> k) & 1));
+            same &= ((b >> k) & 1) ? ones : ~ones;
         }
-    }
-    const int32_t* crow = bases + c * (int64_t)nbuckets;
-    for (int s = threadIdx.x; s < kBucketChunk; s += kSortThreads) {
-        const uint32_t k = key[s];
-        if (k == kPadKey) continue;
-        const uint32_t b = k >> kPosBits;
-        // first sorted slot holding bucket b (lower bound of b << kPosBits)
-        int lo = 0, hi = s;
-        const uint32_t first = b << kPosBits;
-        while (lo < hi) {
-            const int mid = (lo + hi) >> 1;
-            if (key[mid] < first) lo = mid + 1; else hi = mid;
+        if (live) {
+            const int rank = __popcll(same & below);
+            const int32_t prev = seen[b];
+            sorted[bases[(int64_t)b * nchunks + c] + prev + rank] = (int32_t)p;
+            wave_lds_fence();   // every lane has read seen[] before the leaders update it
+            if (rank == 0) seen[b] = prev + __popcll(same);
         }
-        sorted[crow[b] + (s - lo)] = (int32_t)(base + (k & ((1u << kPosBits) - 1)));
+        wave_lds_fence();
     }
 }
 
@@ -185,13 +201,14 @@ int run_bucket(const int32_t* ids, int64_t E, const BucketPlan& plan, void* ws, 
     int32_t* sorted = reinterpret_cast<int32_t*>(base + plan.off_sorted);
     const int32_t nb = (int32_t)plan.buckets;
     int st = launch("bucket_count_kernel", bucket_count_kernel, plan.chunks, kCountThreads,
-                    sizeof(int32_t) * nb, s, ids, plan.pairs, (int32_t)E, nb, counts);
+                    sizeof(int32_t) * nb, s, ids, plan.pairs, (int32_t)E, nb, plan.chunks, counts);
     if (st != FTQ_OK) return st;
-    st = launch("bucket_scan_kernel", bucket_scan_kernel, 1, kScanThreads, 2 * sizeof(int32_t) * nb, s,
+    st = launch("bucket_scan_kernel", bucket_scan_kernel, 1, kScanThreads, sizeof(int32_t) * (2 * nb + 2), s,
                 counts, plan.chunks, nb, (int32_t)plan.tile_m, offsets, tiles);
     if (st != FTQ_OK) return st;
-    return launch("bucket_scatter_kernel", bucket_scatter_kernel, plan.chunks, kSortThreads, 0, s, ids,
-                  plan.pairs, (int32_t)E, nb, static_cast<const int32_t*>(counts), sorted);
+    return launch("bucket_scatter_kernel", bucket_scatter_kernel, (plan.chunks + kScatterWaves - 1) / kScatterWaves,
+                  64 * kScatterWaves, sizeof(int32_t) * kScatterWaves * nb, s, ids, plan.pairs, (int32_t)E, nb,
+                  plan.chunks, static_cast<const int32_t*>(counts), sorted);
 }
 
 }  // namespace ftq

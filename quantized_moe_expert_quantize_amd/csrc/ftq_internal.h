@@ -82,7 +82,7 @@ struct BucketPlan {
     int64_t chunks = 0;       // ceil(pairs / kBucketChunk)
     int64_t tile_m = 0;       // rows per grouped tile (0: no tile table needed)
     // byte offsets inside the workspace
-    int64_t off_counts = 0;   // int32 [chunks][buckets]: per-chunk counts, then per-chunk bases
+    int64_t off_counts = 0;   // int32 [buckets][chunks]: per-chunk counts, then sorted base positions
     int64_t off_offsets = 0;  // int32 [buckets + 1]: start slot of each bucket
     int64_t off_tiles = 0;    // int32 [buckets + 1]: first tile of each bucket
     int64_t off_sorted = 0;   // int32 [pairs]: pair ids grouped by bucket, ascending within one
