@@ -36,6 +36,13 @@ sys.path.insert(0, ROOT)
 METRIC = "MoE Q4_0xQ8_1 matmul time (ms) + HBM GB/s / int8 MFMA % at T=1..8192, top_k=8"
 WORKLOAD = dict(workload="freetoken_pr185_moe_q4_0", E=128, N=1408, K=2816, top_k=8, routing="uniform", seed=0)
 DEFAULT_T = 8191
+# Other shapes the paths are checked on, for profiling a path at its real shape
+# (`--workload`); the bench line proper is the page-1 workload above.
+WORKLOADS = {
+    "page1": (WORKLOAD, DEFAULT_T),
+    "mixtral": (dict(workload="mixtral_8x7b_up", E=8, N=14336, K=4096, top_k=2, routing="uniform", seed=0), 8),
+    "qwen": (dict(workload="qwen3_30b_a3b_up", E=128, N=768, K=2048, top_k=8, routing="zipf", seed=0), 8192),
+}
 # The pages' own measurement of this workload: the fixed GEMV kernel at 8191
 # tokens on a Tesla T4 (FreeToken PR #185, Performance), the faster of two runs.
 PAGES_MS_T8191 = 705.8
@@ -43,7 +50,10 @@ HBM_PEAK_GBS = 8000.0           # MI355X HBM3E
 F16_PEAK_TFLOPS = 2500.0        # MI355X dense fp16 MFMA (the grouped kernel's contraction type)
 INT8_PEAK_TOPS = 5000.0         # MI355X dense int8 MFMA (context: an int8 formulation's ceiling)
 DOMINANT = "moe_grouped_kernel"
-TRAFFIC_FILE = os.path.join(ROOT, "profiles", "moe_grouped_kernel_page1_T8191_traffic.json")
+
+
+def traffic_file(kernel: str, workload: str, T: int) -> str:
+    return os.path.join(ROOT, "profiles", f"{kernel}_{workload}_T{T}_traffic.json")
 
 
 def _lib_hash() -> str:
@@ -60,7 +70,7 @@ def _algorithmic_bytes(E, N, K, T, k, ids):
     return distinct * N * nb * 18 + T * nb * 36 + 4 * T * k + 4 * T * k * N
 
 
-def summarize_pmc(d: str) -> None:
+def summarize_pmc(d: str, kernel: str = DOMINANT) -> None:
     """Turn two rocprofv3 --pmc runs (FETCH_SIZE, WRITE_SIZE; KiB per dispatch)
     into HBM bytes per launch of the dominant kernel, scaled by what the same
     counters read for a plain copy of known size (bench.py --mode profile runs
@@ -74,7 +84,7 @@ def summarize_pmc(d: str) -> None:
                 ctr = row.get("Counter_Name", "")
                 v = float(row.get("Counter_Value", "nan"))
                 # the calibration kernel is torch's x * 1.0 over 1 GiB (bench.py --mode profile)
-                kind = "dominant" if DOMINANT in name else ("copy" if "AUnaryFunctor" in name else None)
+                kind = "dominant" if kernel in name else ("copy" if "AUnaryFunctor" in name else None)
                 if kind is None:
                     continue
                 vals.setdefault((kind, ctr), []).append(v)
@@ -99,15 +109,17 @@ def main() -> None:
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--T", type=int, default=DEFAULT_T)
+    ap.add_argument("--workload", choices=sorted(WORKLOADS), default="page1")
+    ap.add_argument("--T", type=int, default=None, help="tokens (default: the workload's own)")
     ap.add_argument("--mode", choices=["bench", "profile"], default="bench")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-sample-tokens", type=int, default=2048)
     ap.add_argument("--summarize-pmc", metavar="DIR")
+    ap.add_argument("--pmc-kernel", default=DOMINANT, help="kernel whose counters --summarize-pmc reports")
     args = ap.parse_args()
 
     if args.summarize_pmc:
-        summarize_pmc(args.summarize_pmc)
+        summarize_pmc(args.summarize_pmc, args.pmc_kernel)
         return
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
@@ -121,16 +133,17 @@ def main() -> None:
 
     from quantized_moe_expert_quantize_amd import ftq, inputs
 
-    E, N, K, k = WORKLOAD["E"], WORKLOAD["N"], WORKLOAD["K"], WORKLOAD["top_k"]
-    T = args.T
-    seed = WORKLOAD["seed"]
+    wl, wl_T = WORKLOADS[args.workload]
+    E, N, K, k = wl["E"], wl["N"], wl["K"], wl["top_k"]
+    T = args.T if args.T is not None else wl_T
+    seed = wl["seed"]
     torch.cuda.set_device(0)
     dev = torch.device("cuda", 0)
 
     # ---- inputs, resident in HBM --------------------------------------------
     w32 = inputs.weights(E, N, K, seed=seed)
     x32 = inputs.activations(T, K, seed=seed)
-    ids = inputs.routing(T, E, k, seed=seed, kind=WORKLOAD["routing"])
+    ids = inputs.routing(T, E, k, seed=seed, kind=wl["routing"])
     wdev = torch.from_numpy(w32).to(dev)
     wq = ftq.quantize_q4_0(wdev)
     del wdev
@@ -195,14 +208,16 @@ def main() -> None:
     tops = ops / kern_s / 1e12
     gbs = alg_bytes / kern_s / 1e9
     traffic = None
-    if os.path.exists(TRAFFIC_FILE):
-        rec = json.load(open(TRAFFIC_FILE))
+    tf = traffic_file("moe_grouped_kernel" if path == ftq.PATH_GROUPED else "moe_gemv_kernel", args.workload, T)
+    if os.path.exists(tf):
+        rec = json.load(open(tf))
         if rec.get("lib_sha256") == _lib_hash() and rec.get("T") == T:
             traffic = rec.get("bytes_per_launch")
     if path == ftq.PATH_GROUPED:
         roofline = {"bound": "mfma", "achieved": round(tops, 2), "peak": F16_PEAK_TFLOPS, "unit": "TFLOP/s",
                     "frac": round(tops / F16_PEAK_TFLOPS, 4), "traffic": traffic,
                     "kernel": "moe_grouped_kernel (f16 MFMA on exact integer codes)", "kernel_ms": round(mm_ms, 4),
+                    "kernel_ms_covers": "one routed matmul call: prep_activations_kernel + moe_grouped_kernel",
                     "frac_of_int8_peak": round(tops / INT8_PEAK_TOPS, 4),
                     "ops_per_launch": ops, "alg_bytes_per_launch": alg_bytes,
                     "hbm_gbs": round(gbs, 1), "hbm_frac": round(gbs / HBM_PEAK_GBS, 4)}
@@ -237,10 +252,11 @@ def main() -> None:
         "ms_per_step": round(ms_per_step, 4),
         "higher_is_better": False,
         "scaling": "weak",
-        "vs_baseline": round(ms_per_step / PAGES_MS_T8191, 6) if T == DEFAULT_T else None,
-        "dtype": "q4_0 x q8_1 (exact integer block dots on f16 MFMA, fp32 scale-accumulate)",
+        "vs_baseline": round(ms_per_step / PAGES_MS_T8191, 6) if args.workload == "page1" and T == DEFAULT_T else None,
+        "dtype": ("q4_0 x q8_1 (exact integer block dots on f16 MFMA, fp32 scale-accumulate)" if path == ftq.PATH_GROUPED
+                  else "q4_0 x q8_1 (int8 dot4 block dots, fp32 scale-accumulate)"),
         "data": "synthetic",
-        "config": dict(WORKLOAD, T=T, pairs=pairs, path={1: "gemv", 2: "grouped"}[path]),
+        "config": dict(wl, T=T, pairs=pairs, path={1: "gemv", 2: "grouped"}[path]),
         "breakdown_ms": {"quantize_q8_1": round(q_ms, 4), "route": round(r_ms, 4), "matmul": round(mm_ms, 4)},
         "throughput": {"tokens_per_s": round(T / (ms_per_step / 1e3), 1), "matmul_TOPS": round(tops, 2),
                        "matmul_alg_GBps": round(gbs, 1)},
