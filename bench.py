@@ -10,6 +10,7 @@ activations N(0, 1), uniform distinct routing).  Inputs are resident in HBM
 before timing starts.
 
     python bench.py [--steps K] [--warmup W] [--T tokens]
+    python bench.py --workload page1_down  # the second layer: per-pair rows + combine
     python bench.py --mode profile         # a short run for rocprofv3
     python bench.py --summarize-pmc DIR    # HBM traffic from rocprofv3 --pmc runs
 
@@ -38,10 +39,19 @@ WORKLOAD = dict(workload="freetoken_pr185_moe_q4_0", E=128, N=1408, K=2816, top_
 DEFAULT_T = 8191
 # Other shapes the paths are checked on, for profiling a path at its real shape
 # (`--workload`); the bench line proper is the page-1 workload above.
+# A "down" workload is the second layer of the expert FFN: one Q8_1 row per
+# (token, slot) pair in, the expert width as K and the hidden size as N, then
+# the per-token router-weighted combine of the k pair outputs.
 WORKLOADS = {
     "page1": (WORKLOAD, DEFAULT_T),
     "mixtral": (dict(workload="mixtral_8x7b_up", E=8, N=14336, K=4096, top_k=2, routing="uniform", seed=0), 8),
     "qwen": (dict(workload="qwen3_30b_a3b_up", E=128, N=768, K=2048, top_k=8, routing="zipf", seed=0), 8192),
+    "page1_down": (dict(workload="freetoken_pr185_moe_q4_0_down", layer="down", E=128, N=2816, K=1408, top_k=8,
+                        routing="uniform", seed=0), DEFAULT_T),
+    "mixtral_down": (dict(workload="mixtral_8x7b_down", layer="down", E=8, N=4096, K=14336, top_k=2,
+                          routing="uniform", seed=0), 8),
+    "qwen_down": (dict(workload="qwen3_30b_a3b_down", layer="down", E=128, N=2048, K=768, top_k=8,
+                       routing="zipf", seed=0), 8192),
 }
 # The pages' own measurement of this workload: the fixed GEMV kernel at 8191
 # tokens on a Tesla T4 (FreeToken PR #185, Performance), the faster of two runs.
@@ -61,13 +71,15 @@ def _lib_hash() -> str:
     return open(p).read().strip() if os.path.exists(p) else ""
 
 
-def _algorithmic_bytes(E, N, K, T, k, ids):
+def _algorithmic_bytes(E, N, K, T, k, ids, act_rows=None):
     """Bytes the method must move: the distinct experts' Q4_0 rows, the Q8_1
-    activations, the int32 ids and the fp32 output."""
+    activations (one row per token, or per pair), the int32 ids and the fp32
+    output."""
     import numpy as np
     nb = K // 32
+    rows = T if act_rows is None else act_rows
     distinct = len(np.unique(ids[(ids >= 0) & (ids < E)]))
-    return distinct * N * nb * 18 + T * nb * 36 + 4 * T * k + 4 * T * k * N
+    return distinct * N * nb * 18 + rows * nb * 36 + 4 * T * k + 4 * T * k * N
 
 
 def summarize_pmc(d: str, kernel: str = DOMINANT) -> None:
@@ -137,26 +149,32 @@ def main() -> None:
     E, N, K, k = wl["E"], wl["N"], wl["K"], wl["top_k"]
     T = args.T if args.T is not None else wl_T
     seed = wl["seed"]
+    down = wl.get("layer") == "down"
+    act_rows = T * k if down else T
     torch.cuda.set_device(0)
     dev = torch.device("cuda", 0)
 
     # ---- inputs, resident in HBM --------------------------------------------
     w32 = inputs.weights(E, N, K, seed=seed)
-    x32 = inputs.activations(T, K, seed=seed)
+    x32 = inputs.activations(act_rows, K, seed=seed)
     ids = inputs.routing(T, E, k, seed=seed, kind=wl["routing"])
+    gates = inputs.gates(T, k, seed=seed)
     wdev = torch.from_numpy(w32).to(dev)
     wq = ftq.quantize_q4_0(wdev)
     del wdev
     x = torch.from_numpy(x32).to(dev)
     ids_d = torch.from_numpy(ids).to(dev)
     path = ftq.select_path(E, N, K, T, k)
-    aq = torch.empty((T, K // 32 * 36), dtype=torch.uint8, device=dev)
+    gates_d = torch.from_numpy(gates).to(dev)
+    aq = torch.empty((act_rows, K // 32 * 36), dtype=torch.uint8, device=dev)
     out = torch.empty((T * k, N), dtype=torch.float32, device=dev)
-    need = ftq.workspace_bytes(E, N, K, T, k, path)
+    comb = torch.empty((T, N), dtype=torch.float32, device=dev) if down else None
+    need = (ftq.pairs_workspace_bytes if down else ftq.workspace_bytes)(E, N, K, T, k, path)
     ws = torch.empty(max(need, 256), dtype=torch.uint8, device=dev) if need else None
     torch.cuda.synchronize()
 
     ev = lambda: torch.cuda.Event(enable_timing=True)
+    n_marks = 5 if down else 4
 
     def step(marks=None):
         if marks:
@@ -167,9 +185,16 @@ def main() -> None:
         ftq.moe_route(ids_d, E, ws, path)
         if marks:
             marks[2].record()
-        ftq.moe_routed(wq, aq, ids_d, E, N, K, out, ws, path)
+        if down:
+            ftq.moe_pairs_routed(wq, aq, ids_d, E, N, K, out, ws, path)
+        else:
+            ftq.moe_routed(wq, aq, ids_d, E, N, K, out, ws, path)
         if marks:
             marks[3].record()
+        if down:
+            ftq.combine_topk(out, gates_d, out=comb)
+            if marks:
+                marks[4].record()
 
     steps = 3 if args.mode == "profile" else args.steps
     warmup = 2 if args.mode == "profile" else args.warmup
@@ -178,7 +203,7 @@ def main() -> None:
     torch.cuda.synchronize()
 
     # ---- timed region: exactly `steps` steps --------------------------------
-    marks = [[ev() for _ in range(4)] for _ in range(steps)]
+    marks = [[ev() for _ in range(n_marks)] for _ in range(steps)]
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for i in range(steps):
@@ -189,6 +214,7 @@ def main() -> None:
     q_ms = statistics.mean(m[0].elapsed_time(m[1]) for m in marks)
     r_ms = statistics.mean(m[1].elapsed_time(m[2]) for m in marks)
     mm_ms = statistics.mean(m[2].elapsed_time(m[3]) for m in marks)
+    cb_ms = statistics.mean(m[3].elapsed_time(m[4]) for m in marks) if down else None
 
     if args.mode == "profile":
         # plain copy of known size for counter calibration: 1 GiB read, 1 GiB written
@@ -203,7 +229,7 @@ def main() -> None:
     # ---- roofline of the dominant kernel ------------------------------------
     pairs = T * k
     ops = 2.0 * pairs * N * K
-    alg_bytes = _algorithmic_bytes(E, N, K, T, k, ids)
+    alg_bytes = _algorithmic_bytes(E, N, K, T, k, ids, act_rows)
     kern_s = mm_ms / 1e3
     tops = ops / kern_s / 1e12
     gbs = alg_bytes / kern_s / 1e9
@@ -234,12 +260,18 @@ def main() -> None:
         ts = min(args.cpu_sample_tokens, T)
         ow = oracle.quantize_q4_0(w32).reshape(-1)       # weight preparation: not part of a step
         c0 = time.perf_counter()
-        oa = oracle.quantize_q8_1(x32[:ts]).reshape(-1)
-        oracle.moe(ow, oa, np.ascontiguousarray(ids[:ts]), E, N, K, ts, k)
+        if down:
+            oa = oracle.quantize_q8_1(x32[:ts * k]).reshape(-1)
+            y = oracle.moe(ow, oa, np.ascontiguousarray(ids[:ts]), E, N, K, ts, k, per_pair=True)
+            oracle.combine_topk(y, gates[:ts])
+        else:
+            oa = oracle.quantize_q8_1(x32[:ts]).reshape(-1)
+            oracle.moe(ow, oa, np.ascontiguousarray(ids[:ts]), E, N, K, ts, k)
         c1 = time.perf_counter()
         cpu = {"value": round((c1 - c0) * 1e3 * T / ts, 1), "unit": "ms", "cores": oracle.num_threads(),
                "kind": "oracle",
-               "sample": f"Q8_1 quantisation + matmul of the first {ts} of {T} tokens ({ts * k} of {pairs} pairs), "
+               "sample": f"Q8_1 quantisation + matmul{' + combine' if down else ''} of the first {ts} of {T} "
+                         f"tokens ({ts * k} of {pairs} pairs), "
                          f"{(c1 - c0):.1f} s measured, scaled by {T}/{ts} to one step"}
 
     result = {
@@ -257,9 +289,13 @@ def main() -> None:
                   else "q4_0 x q8_1 (int8 dot4 block dots, fp32 scale-accumulate)"),
         "data": "synthetic",
         "config": dict(wl, T=T, pairs=pairs, path={1: "gemv", 2: "grouped"}[path]),
-        "breakdown_ms": {"quantize_q8_1": round(q_ms, 4), "route": round(r_ms, 4), "matmul": round(mm_ms, 4)},
-        "throughput": {"tokens_per_s": round(T / (ms_per_step / 1e3), 1), "matmul_TOPS": round(tops, 2),
-                       "matmul_alg_GBps": round(gbs, 1)},
+        "breakdown_ms": dict({"quantize_q8_1": round(q_ms, 4), "route": round(r_ms, 4), "matmul": round(mm_ms, 4)},
+                             **({"combine_topk": round(cb_ms, 4)} if down else {})),
+        "throughput": dict({"tokens_per_s": round(T / (ms_per_step / 1e3), 1), "matmul_TOPS": round(tops, 2),
+                            "matmul_alg_GBps": round(gbs, 1)},
+                           # combine: reads y [T*k, N] and the gates, writes [T, N] (fp32)
+                           **({"combine_alg_GBps": round((4 * T * k * N + 4 * T * k + 4 * T * N) / (cb_ms / 1e3) / 1e9, 1)}
+                              if down else {})),
         "roofline": roofline,
         "cpu_baseline": cpu,
         "lib_sha256": _lib_hash()[:16],

@@ -164,6 +164,58 @@ int ftq_moe_q4_0_q8_1_partials(const void* w, const void* a, const int32_t* topk
                                int64_t top_k, void* workspace, size_t workspace_bytes, int path,
                                hipStream_t stream);
 
+/*
+ * Per-pair activations: the down projection of an expert FFN.  ("Current Bug:
+ * CuTeDSLMoERunner", Bug 6: the second layer consumes what the first produced
+ * for each routed pair, so its input is one row per pair, not per token.)
+ *
+ * Same as ftq_moe_q4_0_q8_1 / _routed / _partials except for the activations:
+ *   a_pairs  Q8_1 blocks [T*top_k][K/32] (row p = t*top_k + j feeds pair p
+ *            only; 4-byte aligned).
+ * Outputs, routing, limits, errors and determinism are as documented above;
+ * a masked pair's row is zero whatever its activation row holds.  The grouped
+ * path stages one row per pair, so these calls need
+ * ftq_moe_pairs_workspace_bytes(...) bytes of workspace (the same as
+ * ftq_moe_workspace_bytes for the GEMV path).  A routing made by ftq_moe_route
+ * serves these calls too, when the workspace has this size.
+ */
+int64_t ftq_moe_pairs_workspace_bytes(int64_t E, int64_t N, int64_t K, int64_t T, int64_t top_k, int path);
+
+int ftq_moe_q4_0_q8_1_pairs(const void* w, const void* a_pairs, const int32_t* topk_ids, float* out,
+                            int64_t E, int64_t N, int64_t K, int64_t T, int64_t top_k,
+                            void* workspace, size_t workspace_bytes, int path, hipStream_t stream);
+
+int ftq_moe_q4_0_q8_1_pairs_routed(const void* w, const void* a_pairs, const int32_t* topk_ids,
+                                   float* out, int64_t E, int64_t N, int64_t K, int64_t T,
+                                   int64_t top_k, void* workspace, size_t workspace_bytes, int path,
+                                   hipStream_t stream);
+
+int ftq_moe_q4_0_q8_1_pairs_partials(const void* w, const void* a_pairs, const int32_t* topk_ids,
+                                     int32_t* partials, int64_t E, int64_t N, int64_t K, int64_t T,
+                                     int64_t top_k, void* workspace, size_t workspace_bytes, int path,
+                                     hipStream_t stream);
+
+/*
+ * Top-k weighted combine: the expert FFN's output per token.
+ *
+ *   out[t][n] = sum_{j < top_k} gates[t][j] * y[t*top_k + j][n]
+ *
+ *   y      fp32 [T*top_k][N], row p = t*top_k + j (the layout every matmul entry
+ *          point writes; masked pairs' rows are zero and add nothing)
+ *   gates  fp32 [T][top_k], the router's weights, any values
+ *   out    fp32 [T][N]; must not overlap y or gates
+ * Evaluated in fp32 as acc = fma(gates[t][j], y[t*top_k+j][n], acc) for
+ * j = 0 .. top_k-1 from acc = +0: a fixed order, so the result is bit-exact
+ * across calls and independent of how the batch is split; with top_k = 1 and
+ * gates = 1 it reproduces y exactly.
+ * All pointers 4-byte aligned device pointers (16-byte alignment and N % 4 == 0
+ * select 16-byte accesses).  T = 0 is a no-op.  Errors: FTQ_ERR_INVALID_ARG
+ * (T < 0, top_k < 1, N < 1, null or misaligned pointers), FTQ_ERR_UNSUPPORTED
+ * (T*top_k*N*8 overflows int64), FTQ_ERR_LAUNCH.
+ */
+int ftq_moe_combine_topk(const float* y, const float* gates, float* out, int64_t T, int64_t top_k,
+                         int64_t N, hipStream_t stream);
+
 /* Message for the last failing call on this thread ("" if none).  The pointer
  * stays valid until the next ftq_* call on the same thread. */
 const char* ftq_last_error(void);

@@ -8,7 +8,11 @@ this module only builds it with gcc and marshals numpy arrays through ctypes.
 Every function follows the definition spelled out at the top of ``oracle.c``:
 per (token, top-k) pair, the routed expert's Q4_0 rows dotted block by block
 with the token's Q8_1 row [FreeToken PR #185, "fix(kernel): launch GGUF MoE
-GEMV token axis on grid.x, not grid.z", sections Problem and Fix].
+GEMV token axis on grid.x, not grid.z", sections Problem and Fix].  With
+``per_pair=True`` each pair reads its own activation row instead (the second
+layer of an expert FFN, whose input is the first layer's per-pair output
+["Current Bug: CuTeDSLMoERunner", Bug 6]); ``combine_topk`` is the per-token
+router-weighted sum of the pair outputs.
 """
 from __future__ import annotations
 
@@ -58,6 +62,10 @@ def _load():
     lib.oracle_moe.argtypes = [P, P, P, I64, I64, I64, I64, I64, P, P]
     lib.oracle_moe_pairs.argtypes = [P, P, P, I64, I64, I64, I64, I64, P, I64, P, P]
     lib.oracle_moe_partials.argtypes = [P, P, P, I64, I64, I64, I64, I64, P]
+    lib.oracle_moe_ex.argtypes = [P, P, P, I64, I64, I64, I64, I64, I64, P, P]
+    lib.oracle_moe_pairs_ex.argtypes = [P, P, P, I64, I64, I64, I64, I64, I64, P, I64, P, P]
+    lib.oracle_moe_partials_ex.argtypes = [P, P, P, I64, I64, I64, I64, I64, I64, P]
+    lib.oracle_combine_topk.argtypes = [P, P, I64, I64, I64, P, P]
     lib.oracle_num_threads.restype = ctypes.c_int
     _lib = lib
     return lib
@@ -106,38 +114,59 @@ def quantize_q4_0(w: np.ndarray) -> np.ndarray:
     return y
 
 
-def _check(w, a, ids, E, N, K, T, top_k):
+def _check(w, a, ids, E, N, K, T, top_k, per_pair=False):
     nb = K // QK
+    rows = T * top_k if per_pair else T
     assert w.dtype == np.uint8 and w.size == E * N * nb * Q4_0_BYTES and w.flags.c_contiguous
-    assert a.dtype == np.uint8 and a.size == T * nb * Q8_1_BYTES and a.flags.c_contiguous
+    assert a.dtype == np.uint8 and a.size == rows * nb * Q8_1_BYTES and a.flags.c_contiguous
     assert ids.dtype == np.int32 and ids.size == T * top_k and ids.flags.c_contiguous
+    return 1 if per_pair else top_k
 
 
-def moe(w, a, ids, E, N, K, T, top_k, want_abssum=False):
-    """fp64 outputs [T*top_k, N] (and sum of |block terms| if asked)."""
-    _check(w, a, ids, E, N, K, T, top_k)
+def moe(w, a, ids, E, N, K, T, top_k, want_abssum=False, per_pair=False):
+    """fp64 outputs [T*top_k, N] (and sum of |block terms| if asked).
+
+    a holds one Q8_1 row per token ([T, K/32] blocks), or one per pair
+    ([T*top_k, K/32]) when per_pair is set."""
+    div = _check(w, a, ids, E, N, K, T, top_k, per_pair)
     out = np.empty((T * top_k, N), np.float64)
     ab = np.empty_like(out) if want_abssum else None
-    _load().oracle_moe(_ptr(w), _ptr(a), _ptr(ids), E, N, K, T, top_k, _ptr(out),
-                       _ptr(ab) if ab is not None else None)
+    _load().oracle_moe_ex(_ptr(w), _ptr(a), _ptr(ids), E, N, K, T, top_k, div, _ptr(out),
+                          _ptr(ab) if ab is not None else None)
     return (out, ab) if want_abssum else out
 
 
-def moe_pairs(w, a, ids, E, N, K, T, top_k, pairs, want_abssum=False):
+def moe_pairs(w, a, ids, E, N, K, T, top_k, pairs, want_abssum=False, per_pair=False):
     """fp64 outputs for the listed flat pair indices only: [len(pairs), N]."""
-    _check(w, a, ids, E, N, K, T, top_k)
+    div = _check(w, a, ids, E, N, K, T, top_k, per_pair)
     pairs = np.ascontiguousarray(pairs, dtype=np.int64)
     assert pairs.size == 0 or (pairs.min() >= 0 and pairs.max() < T * top_k)
     out = np.empty((pairs.size, N), np.float64)
     ab = np.empty_like(out) if want_abssum else None
-    _load().oracle_moe_pairs(_ptr(w), _ptr(a), _ptr(ids), E, N, K, T, top_k, _ptr(pairs),
-                             pairs.size, _ptr(out), _ptr(ab) if ab is not None else None)
+    _load().oracle_moe_pairs_ex(_ptr(w), _ptr(a), _ptr(ids), E, N, K, T, top_k, div, _ptr(pairs),
+                                pairs.size, _ptr(out), _ptr(ab) if ab is not None else None)
     return (out, ab) if want_abssum else out
 
 
-def moe_partials(w, a, ids, E, N, K, T, top_k):
+def moe_partials(w, a, ids, E, N, K, T, top_k, per_pair=False):
     """Exact integer block partials [T*top_k, N, K/32] (int32)."""
-    _check(w, a, ids, E, N, K, T, top_k)
+    div = _check(w, a, ids, E, N, K, T, top_k, per_pair)
     out = np.empty((T * top_k, N, K // QK), np.int32)
-    _load().oracle_moe_partials(_ptr(w), _ptr(a), _ptr(ids), E, N, K, T, top_k, _ptr(out))
+    _load().oracle_moe_partials_ex(_ptr(w), _ptr(a), _ptr(ids), E, N, K, T, top_k, div, _ptr(out))
     return out
+
+
+def combine_topk(y, gates, want_abssum=False):
+    """fp64 [T, N]: out[t] = sum_j gates[t, j] * y[t*top_k + j] (and sum of |terms|).
+
+    y: float [T*top_k, N] (taken as fp64); gates: float32 [T, top_k]."""
+    gates = np.ascontiguousarray(gates, dtype=np.float32)
+    T, top_k = gates.shape
+    y = np.ascontiguousarray(y, dtype=np.float64)
+    assert y.ndim == 2 and y.shape[0] == T * top_k
+    N = y.shape[1]
+    out = np.empty((T, N), np.float64)
+    ab = np.empty_like(out) if want_abssum else None
+    _load().oracle_combine_topk(_ptr(y), _ptr(gates), T, top_k, N, _ptr(out),
+                                _ptr(ab) if ab is not None else None)
+    return (out, ab) if want_abssum else out

@@ -16,6 +16,12 @@
  *      grid entry per flat (token, top-k) index with Q8_1 activations]
  *   - Expert ids outside [0, E) give an all-zero output row (the masking of
  *     non-local experts described in "Current Bug: CuTeDSLMoERunner", Bug 8).
+ *   - The second layer of an expert FFN takes one activation row per pair
+ *     (what the first layer produced for that pair, "Current Bug:
+ *     CuTeDSLMoERunner", Bug 6): the same matmul with activation row p instead
+ *     of t.  Its outputs are combined per token as the router-weighted sum
+ *     out[t][n] = sum_j gates[t][j] * y[t*top_k + j][n] (the usual top-k MoE
+ *     combine; the pages do not print it).
  *   - The byte layouts are the GGUF Q4_0 / Q8_1 blocks the FreeToken page
  *     serves ("Tested on": a Q4_0 .gguf checkpoint).  The pages name the
  *     formats but do not print them; the readings used here are:
@@ -235,47 +241,64 @@ static void one_pair(const uint8_t* w, const uint8_t* a, int64_t e, int64_t t,
     }
 }
 
-/* w: [E][N][K/32] Q4_0; a: [T][K/32] Q8_1; ids: [T][top_k] int32;
- * out: [T*top_k][N] fp64; abssum: same shape or NULL. */
+/* w: [E][N][K/32] Q4_0; ids: [T][top_k] int32; out: [T*top_k][N] fp64;
+ * abssum: same shape or NULL.  a: Q8_1 rows; pair p reads row p / act_div
+ * (act_div = top_k: a is [T][K/32], one row per token; act_div = 1: a is
+ * [T*top_k][K/32], one row per pair). */
+void oracle_moe_ex(const uint8_t* w, const uint8_t* a, const int32_t* ids,
+                   int64_t E, int64_t N, int64_t K, int64_t T, int64_t top_k, int64_t act_div,
+                   double* out, double* abssum)
+{
+    int64_t nb = K / QK;
+    int64_t p;
+#pragma omp parallel for schedule(dynamic, 1)
+    for (p = 0; p < T * top_k; ++p) {
+        int64_t row = p / act_div;
+        one_pair(w, a, (int64_t)ids[p], row, E, N, nb, out + p * N, abssum ? abssum + p * N : NULL);
+    }
+}
+
 void oracle_moe(const uint8_t* w, const uint8_t* a, const int32_t* ids,
                 int64_t E, int64_t N, int64_t K, int64_t T, int64_t top_k,
                 double* out, double* abssum)
 {
-    int64_t nb = K / QK;
-    int64_t p;
-#pragma omp parallel for schedule(dynamic, 1)
-    for (p = 0; p < T * top_k; ++p) {
-        int64_t t = p / top_k;
-        one_pair(w, a, (int64_t)ids[p], t, E, N, nb, out + p * N, abssum ? abssum + p * N : NULL);
-    }
+    oracle_moe_ex(w, a, ids, E, N, K, T, top_k, top_k, out, abssum);
 }
 
 /* The same for a chosen list of pairs: out row i belongs to pair pairs[i]. */
-void oracle_moe_pairs(const uint8_t* w, const uint8_t* a, const int32_t* ids,
-                      int64_t E, int64_t N, int64_t K, int64_t T, int64_t top_k,
-                      const int64_t* pairs, int64_t npairs, double* out, double* abssum)
+void oracle_moe_pairs_ex(const uint8_t* w, const uint8_t* a, const int32_t* ids,
+                         int64_t E, int64_t N, int64_t K, int64_t T, int64_t top_k, int64_t act_div,
+                         const int64_t* pairs, int64_t npairs, double* out, double* abssum)
 {
     int64_t nb = K / QK;
     int64_t i;
     (void)T;
+    (void)top_k;
 #pragma omp parallel for schedule(dynamic, 1)
     for (i = 0; i < npairs; ++i) {
         int64_t p = pairs[i];
-        int64_t t = p / top_k;
-        one_pair(w, a, (int64_t)ids[p], t, E, N, nb, out + i * N, abssum ? abssum + i * N : NULL);
+        one_pair(w, a, (int64_t)ids[p], p / act_div, E, N, nb, out + i * N, abssum ? abssum + i * N : NULL);
     }
 }
 
-/* Integer partials P[p][n][b]; masked pairs give zeros. */
-void oracle_moe_partials(const uint8_t* w, const uint8_t* a, const int32_t* ids,
-                         int64_t E, int64_t N, int64_t K, int64_t T, int64_t top_k,
-                         int32_t* partials)
+void oracle_moe_pairs(const uint8_t* w, const uint8_t* a, const int32_t* ids,
+                      int64_t E, int64_t N, int64_t K, int64_t T, int64_t top_k,
+                      const int64_t* pairs, int64_t npairs, double* out, double* abssum)
+{
+    oracle_moe_pairs_ex(w, a, ids, E, N, K, T, top_k, top_k, pairs, npairs, out, abssum);
+}
+
+/* Integer partials P[p][n][b]; masked pairs give zeros; pair p reads
+ * activation row p / act_div. */
+void oracle_moe_partials_ex(const uint8_t* w, const uint8_t* a, const int32_t* ids,
+                            int64_t E, int64_t N, int64_t K, int64_t T, int64_t top_k, int64_t act_div,
+                            int32_t* partials)
 {
     int64_t nb = K / QK;
     int64_t p;
 #pragma omp parallel for schedule(dynamic, 1)
     for (p = 0; p < T * top_k; ++p) {
-        int64_t t = p / top_k;
+        int64_t t = p / act_div;
         int64_t e = ids[p];
         for (int64_t n = 0; n < N; ++n) {
             for (int64_t b = 0; b < nb; ++b) {
@@ -284,6 +307,35 @@ void oracle_moe_partials(const uint8_t* w, const uint8_t* a, const int32_t* ids,
                     v = block_partial(weight_block(w, e, n, b, N, nb), act_block(a, t, b, nb));
                 partials[(p * N + n) * nb + b] = v;
             }
+        }
+    }
+}
+
+void oracle_moe_partials(const uint8_t* w, const uint8_t* a, const int32_t* ids,
+                         int64_t E, int64_t N, int64_t K, int64_t T, int64_t top_k,
+                         int32_t* partials)
+{
+    oracle_moe_partials_ex(w, a, ids, E, N, K, T, top_k, top_k, partials);
+}
+
+/* Top-k combine in fp64: out[t][n] = sum_j gates[t][j] * y[t*top_k + j][n],
+ * abssum[t][n] = sum_j |gates[t][j] * y[t*top_k + j][n]| (nullable).
+ * y: [T*top_k][N] fp64; gates: [T][top_k] fp32; out: [T][N] fp64. */
+void oracle_combine_topk(const double* y, const float* gates, int64_t T, int64_t top_k, int64_t N,
+                         double* out, double* abssum)
+{
+    int64_t t;
+#pragma omp parallel for schedule(static)
+    for (t = 0; t < T; ++t) {
+        for (int64_t n = 0; n < N; ++n) {
+            double acc = 0.0, aabs = 0.0;
+            for (int64_t j = 0; j < top_k; ++j) {
+                double term = (double)gates[t * top_k + j] * y[(t * top_k + j) * N + n];
+                acc += term;
+                aabs += fabs(term);
+            }
+            out[t * N + n] = acc;
+            if (abssum) abssum[t * N + n] = aabs;
         }
     }
 }

@@ -144,9 +144,13 @@ int check_workspace(int64_t need, const void* ws, size_t ws_bytes)
 // kRoute: bucketing only; kMatmul: matmul only (pairs already routed); both: the full call.
 enum Phase { kRoute = 1, kMatmul = 2 };
 
+// act_per_pair: `a` holds one Q8_1 row per pair ([T*top_k][K/32]) instead of
+// one per token ([T][K/32]).
+int64_t act_rows_of(int64_t T, int64_t top_k, bool act_per_pair) { return act_per_pair ? T * top_k : T; }
+
 int moe_common(const void* w, const void* a, const int32_t* ids, float* out, int32_t* partials,
                int64_t E, int64_t N, int64_t K, int64_t T, int64_t top_k, void* ws, size_t ws_bytes,
-               int path, hipStream_t stream, int phases)
+               int path, hipStream_t stream, int phases, bool act_per_pair = false)
 {
     clear_error();
     int st = check_sizes(E, N, K, T, top_k);
@@ -167,7 +171,8 @@ int moe_common(const void* w, const void* a, const int32_t* ids, float* out, int
     const BucketPlan plan = plan_for(rp, E, N, K, T, top_k, &bucketed);
     if (bucketed) {
         // routing alone needs the bucket tables; the grouped matmul also stages activations
-        const int64_t need = plan.bytes + ((phases & kMatmul) && rp == FTQ_PATH_GROUPED ? grouped_prep_bytes(T, K) : 0);
+        const int64_t need = plan.bytes + ((phases & kMatmul) && rp == FTQ_PATH_GROUPED
+                                               ? grouped_prep_bytes(act_rows_of(T, top_k, act_per_pair), K) : 0);
         st = check_workspace(need, ws, ws_bytes);
         if (st != FTQ_OK) return st;
         if (phases & kRoute) {
@@ -176,9 +181,22 @@ int moe_common(const void* w, const void* a, const int32_t* ids, float* out, int
         }
     }
     if (!(phases & kMatmul)) return FTQ_OK;
-    MoeArgs m{w, a, ids, out, partials, E, N, K, T, top_k};
+    MoeArgs m{w, a, ids, out, partials, E, N, K, T, top_k, act_per_pair ? 1 : top_k};
     if (rp == FTQ_PATH_GEMV) return run_gemv(m, bucketed ? &plan : nullptr, ws, stream);
     return run_grouped(m, plan, ws, stream);
+}
+
+int64_t workspace_bytes(int64_t E, int64_t N, int64_t K, int64_t T, int64_t top_k, int path, bool act_per_pair)
+{
+    clear_error();
+    if (check_sizes(E, N, K, T, top_k) != FTQ_OK) return -1;
+    const int rp = resolve_path(path, E, T, top_k);
+    if (rp < 0) { set_error("unknown path %d", path); return -1; }
+    if (T == 0) return 0;
+    bool bucketed = false;
+    const BucketPlan plan = plan_for(rp, E, N, K, T, top_k, &bucketed);
+    if (!bucketed) return 0;
+    return plan.bytes + (rp == FTQ_PATH_GROUPED ? grouped_prep_bytes(act_rows_of(T, top_k, act_per_pair), K) : 0);
 }
 
 }  // namespace
@@ -218,17 +236,15 @@ int ftq_moe_select_path(int64_t E, int64_t N, int64_t K, int64_t T, int64_t top_
     return select_path(E, T, top_k);
 }
 
+
 int64_t ftq_moe_workspace_bytes(int64_t E, int64_t N, int64_t K, int64_t T, int64_t top_k, int path)
 {
-    clear_error();
-    if (check_sizes(E, N, K, T, top_k) != FTQ_OK) return -1;
-    const int rp = resolve_path(path, E, T, top_k);
-    if (rp < 0) { set_error("unknown path %d", path); return -1; }
-    if (T == 0) return 0;
-    bool bucketed = false;
-    const BucketPlan plan = plan_for(rp, E, N, K, T, top_k, &bucketed);
-    if (!bucketed) return 0;
-    return plan.bytes + (rp == FTQ_PATH_GROUPED ? grouped_prep_bytes(T, K) : 0);
+    return workspace_bytes(E, N, K, T, top_k, path, false);
+}
+
+int64_t ftq_moe_pairs_workspace_bytes(int64_t E, int64_t N, int64_t K, int64_t T, int64_t top_k, int path)
+{
+    return workspace_bytes(E, N, K, T, top_k, path, true);
 }
 
 int ftq_moe_q4_0_q8_1(const void* w, const void* a, const int32_t* topk_ids, float* out, int64_t E,
@@ -261,6 +277,50 @@ int ftq_moe_q4_0_q8_1_partials(const void* w, const void* a, const int32_t* topk
 {
     return moe_common(w, a, topk_ids, nullptr, partials, E, N, K, T, top_k, workspace, workspace_bytes, path, stream,
                       kRoute | kMatmul);
+}
+
+int ftq_moe_q4_0_q8_1_pairs(const void* w, const void* a_pairs, const int32_t* topk_ids, float* out, int64_t E,
+                            int64_t N, int64_t K, int64_t T, int64_t top_k, void* workspace,
+                            size_t workspace_bytes, int path, hipStream_t stream)
+{
+    return moe_common(w, a_pairs, topk_ids, out, nullptr, E, N, K, T, top_k, workspace, workspace_bytes, path,
+                      stream, kRoute | kMatmul, true);
+}
+
+int ftq_moe_q4_0_q8_1_pairs_routed(const void* w, const void* a_pairs, const int32_t* topk_ids, float* out,
+                                   int64_t E, int64_t N, int64_t K, int64_t T, int64_t top_k, void* workspace,
+                                   size_t workspace_bytes, int path, hipStream_t stream)
+{
+    return moe_common(w, a_pairs, topk_ids, out, nullptr, E, N, K, T, top_k, workspace, workspace_bytes, path,
+                      stream, kMatmul, true);
+}
+
+int ftq_moe_q4_0_q8_1_pairs_partials(const void* w, const void* a_pairs, const int32_t* topk_ids,
+                                     int32_t* partials, int64_t E, int64_t N, int64_t K, int64_t T,
+                                     int64_t top_k, void* workspace, size_t workspace_bytes, int path,
+                                     hipStream_t stream)
+{
+    return moe_common(w, a_pairs, topk_ids, nullptr, partials, E, N, K, T, top_k, workspace, workspace_bytes, path,
+                      stream, kRoute | kMatmul, true);
+}
+
+int ftq_moe_combine_topk(const float* y, const float* gates, float* out, int64_t T, int64_t top_k, int64_t N,
+                         hipStream_t stream)
+{
+    clear_error();
+    if (T < 0 || top_k < 1 || N < 1) {
+        set_error("need T >= 0, top_k >= 1, N >= 1 (got T=%lld top_k=%lld N=%lld)", (long long)T, (long long)top_k,
+                  (long long)N);
+        return FTQ_ERR_INVALID_ARG;
+    }
+    if (T > INT64_MAX / 8 / top_k / N) { set_error("T*top_k*N overflows 64-bit byte offsets"); return FTQ_ERR_UNSUPPORTED; }
+    if (T == 0) return FTQ_OK;
+    if (!y || !gates || !out) { set_error("null pointer argument (y, gates or out)"); return FTQ_ERR_INVALID_ARG; }
+    if (!aligned(y, 4) || !aligned(gates, 4) || !aligned(out, 4)) {
+        set_error("misaligned pointer (y, gates and out need 4-byte alignment)");
+        return FTQ_ERR_INVALID_ARG;
+    }
+    return run_combine_topk(y, gates, out, T, top_k, N, stream);
 }
 
 const char* ftq_last_error(void) { return g_error.c_str(); }

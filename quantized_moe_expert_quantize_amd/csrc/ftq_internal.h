@@ -99,6 +99,7 @@ struct MoeArgs {
     float* out;            // fp32 outputs, or
     int32_t* partials;     // integer partials when non-null
     int64_t E, N, K, T, top_k;
+    int64_t act_div;       // activation row of pair p: p / act_div (top_k: per token; 1: per pair)
 };
 
 // GEMV path; `bucketed` selects the pair list from the workspace (else the
@@ -107,9 +108,13 @@ int run_gemv(const MoeArgs& m, const BucketPlan* plan, const void* ws, hipStream
 constexpr int64_t kGemvScanMaxPairs = 4096;
 
 // Grouped MFMA path.  Its workspace is the bucket plan's bytes followed by
-// grouped_prep_bytes(T, K) of per-call activation staging.
+// grouped_prep_bytes(activation rows, K) of per-call activation staging.
 int run_grouped(const MoeArgs& m, const BucketPlan& plan, void* ws, hipStream_t s);
 int64_t grouped_tile_m(const MoeArgs& m);
-int64_t grouped_prep_bytes(int64_t T, int64_t K);
+int64_t grouped_prep_bytes(int64_t act_rows, int64_t K);
+
+// Top-k weighted combine of per-pair rows into per-token rows.
+int run_combine_topk(const float* y, const float* gates, float* out, int64_t T, int64_t top_k, int64_t N,
+                     hipStream_t s);
 
 }  // namespace ftq

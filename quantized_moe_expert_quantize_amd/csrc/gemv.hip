@@ -65,6 +65,7 @@ struct GemvParams {
     const int32_t* offsets;   // bucketed mode: [E+2] segment starts
     const int32_t* sorted;    // bucketed mode: pair ids grouped by bucket
     int64_t E, N, nb, top_k, pairs, row_tiles;
+    int64_t act_div;          // activation row of pair p: p / act_div
     int64_t grid;             // workgroups launched
     int64_t seg;              // K blocks staged per pass (a multiple of 8)
     int pc_cap;               // activation rows staged per pass (<= kPairChunk)
@@ -457,7 +458,7 @@ __global__ __launch_bounds__(kThreads, kWavesPerSimd) void moe_gemv_kernel(GemvP
             if (tid < npc) {
                 const int32_t pid = list[c0 + tid];
                 plist[tid] = pid;
-                ptok[tid] = (int32_t)(pid / p.top_k);
+                ptok[tid] = (int32_t)(pid / p.act_div);
             }
             __syncthreads();
 
@@ -532,6 +533,7 @@ int run_gemv(const MoeArgs& m, const BucketPlan* plan, const void* ws, hipStream
     gp.N = m.N;
     gp.nb = m.K / kQK;
     gp.top_k = m.top_k;
+    gp.act_div = m.act_div;
     gp.pairs = m.T * m.top_k;
     gp.row_tiles = (m.N + kRowsPerTile - 1) / kRowsPerTile;
     if (gp.pairs == 0) return FTQ_OK;

@@ -66,6 +66,7 @@ struct GroupedParams {
     const int32_t* tiles;     // [E+2]
     const int32_t* sorted;
     int64_t E, N, nb, top_k, nbuckets, n_tiles_n, max_mt;
+    int64_t act_div;          // activation row of pair p: p / act_div
 };
 
 // Waves per workgroup for BM = 128 tiles.  4 waves of 64x64 (two workgroups
@@ -214,7 +215,7 @@ __global__ __launch_bounds__(Shape<BM>::kThreads, Shape<BM>::kWavesPerSimd) void
         for (int m = tid; m < BM; m += kThreads) {
             const int32_t pid = m < rows ? p.sorted[slot0 + m] : 0;
             sm.row_pair[m] = pid;
-            sm.row_tok[m] = (int32_t)(pid / p.top_k);
+            sm.row_tok[m] = (int32_t)(pid / p.act_div);
         }
         if (tid < 2 * kKB) sm.bs[tid / kKB][tid % kKB][kBN] = 0u;
         __syncthreads();
@@ -476,11 +477,11 @@ int64_t grouped_tile_m(const MoeArgs& m)
     return 32;
 }
 
-int64_t grouped_prep_bytes(int64_t T, int64_t K)
+int64_t grouped_prep_bytes(int64_t act_rows, int64_t K)
 {
     const int64_t nbp = padded_blocks(K / kQK);
     auto align = [](int64_t v) { return (v + 255) / 256 * 256; };
-    return align(T * nbp * kBlockF16) + align(T * nbp * 2);
+    return align(act_rows * nbp * kBlockF16) + align(act_rows * nbp * 2);
 }
 
 int run_grouped(const MoeArgs& m, const BucketPlan& plan, void* ws, hipStream_t s)
@@ -493,14 +494,15 @@ int run_grouped(const MoeArgs& m, const BucketPlan& plan, void* ws, hipStream_t 
     const int64_t nb = m.K / kQK;
     auto align = [](int64_t v) { return (v + 255) / 256 * 256; };
     const int64_t nbp = padded_blocks(nb);
+    const int64_t act_rows = m.T * m.top_k / m.act_div;   // tokens, or pairs
     uint8_t* a16 = base + plan.bytes;
-    uint16_t* d8 = reinterpret_cast<uint16_t*>(a16 + align(m.T * nbp * kBlockF16));
+    uint16_t* d8 = reinterpret_cast<uint16_t*>(a16 + align(act_rows * nbp * kBlockF16));
 
     // activations -> fp16 codes + scales, padded to whole passes (once per call)
-    const int64_t nblocks = m.T * nbp;
+    const int64_t nblocks = act_rows * nbp;
     st = launch("prep_activations_kernel", prep_activations_kernel,
                 stride_grid((nblocks + kThreads - 1) / kThreads, lim), kThreads, 0, s,
-                static_cast<const uint8_t*>(m.a), m.T, nb, a16, d8);
+                static_cast<const uint8_t*>(m.a), act_rows, nb, a16, d8);
     if (st != FTQ_OK) return st;
 
     GroupedParams gp{};
@@ -516,6 +518,7 @@ int run_grouped(const MoeArgs& m, const BucketPlan& plan, void* ws, hipStream_t 
     gp.N = m.N;
     gp.nb = nb;
     gp.top_k = m.top_k;
+    gp.act_div = m.act_div;
     gp.nbuckets = plan.buckets;
     gp.n_tiles_n = (m.N + kBN - 1) / kBN;
     const int64_t bm = plan.tile_m;
@@ -528,7 +531,7 @@ int run_grouped(const MoeArgs& m, const BucketPlan& plan, void* ws, hipStream_t 
     // activation offsets fit 32 bits unless the staged activations reach 4 GiB;
     // FTQ_FORCE_WIDE=1 selects the 64-bit variant at any size (tests)
     static const bool force_wide = [] { const char* v = getenv("FTQ_FORCE_WIDE"); return v && v[0] == '1'; }();
-    const bool wide = force_wide || m.T * nbp * kBlockF16 >= ((int64_t)1 << 32);
+    const bool wide = force_wide || act_rows * nbp * kBlockF16 >= ((int64_t)1 << 32);
     switch (bm) {
     case 128: return part ? launch_grouped<128, true>(vec, wide, gp, grid, s) : launch_grouped<128, false>(vec, wide, gp, grid, s);
     case 64: return part ? launch_grouped<64, true>(vec, wide, gp, grid, s) : launch_grouped<64, false>(vec, wide, gp, grid, s);

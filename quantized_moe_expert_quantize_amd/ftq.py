@@ -22,6 +22,8 @@ QK, Q4_0_BYTES, Q8_1_BYTES = 32, 18, 36
 EXPORTS = (
     "ftq_quantize_q8_1", "ftq_quantize_q4_0", "ftq_moe_select_path", "ftq_moe_workspace_bytes",
     "ftq_moe_q4_0_q8_1", "ftq_moe_route", "ftq_moe_q4_0_q8_1_routed", "ftq_moe_q4_0_q8_1_partials",
+    "ftq_moe_pairs_workspace_bytes", "ftq_moe_q4_0_q8_1_pairs", "ftq_moe_q4_0_q8_1_pairs_routed",
+    "ftq_moe_q4_0_q8_1_pairs_partials", "ftq_moe_combine_topk",
     "ftq_last_error", "ftq_version",
     "ftq_debug_force_block_threads",
 )
@@ -60,6 +62,13 @@ def lib() -> ctypes.CDLL:
     L.ftq_moe_q4_0_q8_1_routed.argtypes = [P, P, P, P, I64, I64, I64, I64, I64, P, SZ, I32, P]
     L.ftq_moe_q4_0_q8_1_routed.restype = I32
     L.ftq_moe_q4_0_q8_1_partials.argtypes = [P, P, P, P, I64, I64, I64, I64, I64, P, SZ, I32, P]
+    L.ftq_moe_pairs_workspace_bytes.argtypes = [I64, I64, I64, I64, I64, I32]
+    L.ftq_moe_pairs_workspace_bytes.restype = I64
+    for name in ("ftq_moe_q4_0_q8_1_pairs", "ftq_moe_q4_0_q8_1_pairs_routed", "ftq_moe_q4_0_q8_1_pairs_partials"):
+        getattr(L, name).argtypes = [P, P, P, P, I64, I64, I64, I64, I64, P, SZ, I32, P]
+        getattr(L, name).restype = I32
+    L.ftq_moe_combine_topk.argtypes = [P, P, P, I64, I64, I64, P]
+    L.ftq_moe_combine_topk.restype = I32
     L.ftq_moe_q4_0_q8_1_partials.restype = I32
     L.ftq_last_error.restype = ctypes.c_char_p
     L.ftq_version.restype = ctypes.c_char_p
@@ -130,13 +139,14 @@ def workspace_bytes(E: int, N: int, K: int, T: int, top_k: int, path: int = PATH
     return r
 
 
-def _moe_args(w, a, topk_ids, E, N, K):
+def _moe_args(w, a, topk_ids, E, N, K, per_pair=False):
     T, top_k = topk_ids.shape
     nb = K // QK
     if w.numel() != E * N * nb * Q4_0_BYTES:
         raise ValueError("w must hold E*N*(K/32) Q4_0 blocks")
-    if a.numel() != T * nb * Q8_1_BYTES:
-        raise ValueError("a must hold T*(K/32) Q8_1 blocks")
+    rows = T * top_k if per_pair else T
+    if a.numel() != rows * nb * Q8_1_BYTES:
+        raise ValueError(f"a must hold {'T*top_k' if per_pair else 'T'}*(K/32) Q8_1 blocks")
     return T, top_k
 
 
@@ -199,4 +209,70 @@ def moe_partials(w: torch.Tensor, a: torch.Tensor, topk_ids: torch.Tensor, E: in
         _dev(w, "w", torch.uint8), _dev(a, "a", torch.uint8), _dev(topk_ids, "topk_ids", torch.int32),
         _dev(out, "partials", torch.int32), E, N, K, T, top_k,
         ws.data_ptr() if ws is not None else None, ws_n, path, _stream(stream)))
+    return out
+
+
+# ---- per-pair activations (down projection) and the top-k combine -----------
+
+def pairs_workspace_bytes(E: int, N: int, K: int, T: int, top_k: int, path: int = PATH_AUTO) -> int:
+    r = lib().ftq_moe_pairs_workspace_bytes(E, N, K, T, top_k, path)
+    if r < 0:
+        raise FtqError(ERR_INVALID_ARG, last_error())
+    return r
+
+
+def moe_pairs(w: torch.Tensor, a_pairs: torch.Tensor, topk_ids: torch.Tensor, E: int, N: int, K: int,
+              path: int = PATH_AUTO, out: torch.Tensor | None = None, workspace: torch.Tensor | None = None,
+              stream=None) -> torch.Tensor:
+    """MoE expert matmul on per-pair activations a_pairs [T*top_k, K/32 Q8_1 blocks]:
+    fp32 out [T*top_k, N]."""
+    T, top_k = _moe_args(w, a_pairs, topk_ids, E, N, K, per_pair=True)
+    if out is None:
+        out = torch.empty((T * top_k, N), dtype=torch.float32, device=a_pairs.device)
+    need = pairs_workspace_bytes(E, N, K, T, top_k, path)
+    ws, ws_n = _workspace(workspace, need, a_pairs.device)
+    _check(lib().ftq_moe_q4_0_q8_1_pairs(
+        _dev(w, "w", torch.uint8), _dev(a_pairs, "a_pairs", torch.uint8), _dev(topk_ids, "topk_ids", torch.int32),
+        _dev(out, "out", torch.float32), E, N, K, T, top_k,
+        ws.data_ptr() if ws is not None else None, ws_n, path, _stream(stream)))
+    return out
+
+
+def moe_pairs_routed(w: torch.Tensor, a_pairs: torch.Tensor, topk_ids: torch.Tensor, E: int, N: int, K: int,
+                     out: torch.Tensor, workspace: torch.Tensor | None, path: int = PATH_AUTO,
+                     stream=None) -> torch.Tensor:
+    """moe_pairs on pairs already routed into `workspace` (sized by pairs_workspace_bytes) by moe_route."""
+    T, top_k = _moe_args(w, a_pairs, topk_ids, E, N, K, per_pair=True)
+    ws_n = workspace.numel() if workspace is not None else 0
+    _check(lib().ftq_moe_q4_0_q8_1_pairs_routed(
+        _dev(w, "w", torch.uint8), _dev(a_pairs, "a_pairs", torch.uint8), _dev(topk_ids, "topk_ids", torch.int32),
+        _dev(out, "out", torch.float32), E, N, K, T, top_k,
+        workspace.data_ptr() if workspace is not None else None, ws_n, path, _stream(stream)))
+    return out
+
+
+def moe_pairs_partials(w: torch.Tensor, a_pairs: torch.Tensor, topk_ids: torch.Tensor, E: int, N: int, K: int,
+                       path: int = PATH_AUTO, stream=None) -> torch.Tensor:
+    """Exact integer block partials int32 [T*top_k, N, K/32] on per-pair activations."""
+    T, top_k = _moe_args(w, a_pairs, topk_ids, E, N, K, per_pair=True)
+    out = torch.empty((T * top_k, N, K // QK), dtype=torch.int32, device=a_pairs.device)
+    need = pairs_workspace_bytes(E, N, K, T, top_k, path)
+    ws, ws_n = _workspace(None, need, a_pairs.device)
+    _check(lib().ftq_moe_q4_0_q8_1_pairs_partials(
+        _dev(w, "w", torch.uint8), _dev(a_pairs, "a_pairs", torch.uint8), _dev(topk_ids, "topk_ids", torch.int32),
+        _dev(out, "partials", torch.int32), E, N, K, T, top_k,
+        ws.data_ptr() if ws is not None else None, ws_n, path, _stream(stream)))
+    return out
+
+
+def combine_topk(y: torch.Tensor, gates: torch.Tensor, out: torch.Tensor | None = None, stream=None) -> torch.Tensor:
+    """out[t, n] = sum_j gates[t, j] * y[t*top_k + j, n] (fp32, j ascending)."""
+    T, top_k = gates.shape
+    if y.dim() != 2 or y.shape[0] != T * top_k:
+        raise ValueError("y must be [T*top_k, N]")
+    N = y.shape[1]
+    if out is None:
+        out = torch.empty((T, N), dtype=torch.float32, device=y.device)
+    _check(lib().ftq_moe_combine_topk(_dev(y, "y", torch.float32), _dev(gates, "gates", torch.float32),
+                                      _dev(out, "out", torch.float32), T, top_k, N, _stream(stream)))
     return out

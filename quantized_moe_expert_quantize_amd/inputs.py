@@ -1,19 +1,21 @@
 """Seeded synthetic inputs shared by the HIP path's tests/benchmark and the oracle.
 
 This module draws random numbers only: fp32 weights, fp32 activations and
-top-k routing ids.  It holds none of the method's arithmetic (no quantisation,
+top-k routing ids and gate weights.  It holds none of the method's arithmetic (no quantisation,
 no dot products); each side quantises the fp32 tensors with its own code.
 
 Recipe (the pages run real checkpoints that are not available, so seeded
 synthetic tensors with the same shapes stand in for them):
   * one numpy PCG64 stream per tensor: SeedSequence([seed, tensor_id]) with
-    tensor ids weights=0, activations=1, routing=2;
+    tensor ids weights=0, activations=1, routing=2, gates=3;
   * weights   fp32 N(0, 0.02), shape [E, N, K];
   * activations fp32 N(0, 1), shape [T, K];
   * routing: per token, top_k DISTINCT experts.  "uniform": every k-subset
     equally likely (argsort of iid uniforms); "zipf": expert r drawn with
     weight (r+1)^-s, k distinct by successive weighted sampling without
-    replacement (Gumbel-top-k).
+    replacement (Gumbel-top-k);
+  * gates fp32 [T, top_k]: iid U(0.05, 1) per slot, scaled so each token's
+    row sums to about one (routing weights after a top-k softmax).
 Shapes of the pages' workloads: FreeToken PR #185 "Performance" (nrows=1408,
 hidden=2816, top_k=8, 128 experts) and mlxcel PR #652 "Summary"
 (qwen3-30b-a3b at 8192 tokens, mixtral-8x7b at 32768 tokens).
@@ -22,7 +24,7 @@ from __future__ import annotations
 
 import numpy as np
 
-WEIGHTS, ACTIVATIONS, ROUTING = 0, 1, 2
+WEIGHTS, ACTIVATIONS, ROUTING, GATES = 0, 1, 2, 3
 
 
 def _rng(seed: int, tensor_id: int) -> np.random.Generator:
@@ -60,6 +62,12 @@ def routing(T: int, E: int, top_k: int, seed: int = 0, kind: str = "uniform",
     else:
         raise ValueError(f"unknown routing kind {kind!r}")
     return np.ascontiguousarray(ids, dtype=np.int32)
+
+
+def gates(T: int, top_k: int, seed: int = 0) -> np.ndarray:
+    """fp32 [T, top_k] positive weights, each row summing to about one."""
+    g = _rng(seed, GATES).uniform(0.05, 1.0, (T, top_k))
+    return np.ascontiguousarray(g / g.sum(axis=1, keepdims=True), dtype=np.float32)
 
 
 # The workloads, by name.  Each entry: E, top_k, K (hidden), N (rows per

@@ -114,3 +114,32 @@ def test_quantize_rejects_invalid_arguments():
     assert L.ftq_quantize_q4_0(P(0x1000), 4, 40, P(0x2000), None) == ftq.ERR_INVALID_ARG
     assert L.ftq_quantize_q4_0(P(0x1000), 4, 64, P(0x2001), None) == ftq.ERR_INVALID_ARG
     assert L.ftq_quantize_q4_0(None, 0, 64, None, None) == ftq.OK
+
+
+def test_pairs_and_combine_validate_before_any_launch():
+    """Argument checks of the second-layer calls run on the host and never reach a kernel."""
+    L = ftq.lib()
+    P = ctypes.c_void_p
+    base = P(0x100000)
+    # per-pair matmul: the same size and pointer rules as the per-token call
+    assert L.ftq_moe_q4_0_q8_1_pairs(base, base, base, base, 8, 64, 250, 4, 2, None, 0, ftq.PATH_GEMV, None) == ftq.ERR_INVALID_ARG
+    assert L.ftq_moe_q4_0_q8_1_pairs(base, None, base, base, 8, 64, 256, 4, 2, None, 0, ftq.PATH_GEMV, None) == ftq.ERR_INVALID_ARG
+    assert L.ftq_moe_q4_0_q8_1_pairs(None, None, None, None, 8, 64, 256, 0, 2, None, 0, ftq.PATH_AUTO, None) == ftq.OK
+    assert L.ftq_moe_q4_0_q8_1_pairs_partials(base, base, base, None, 8, 64, 256, 4, 2, None, 0, ftq.PATH_GEMV, None) == ftq.ERR_INVALID_ARG
+    # the grouped path stages one activation row per pair, so it needs more workspace
+    E, N, K, T, k = 128, 1408, 2816, 8191, 8
+    tok = ftq.workspace_bytes(E, N, K, T, k, ftq.PATH_GROUPED)
+    pp = ftq.pairs_workspace_bytes(E, N, K, T, k, ftq.PATH_GROUPED)
+    assert pp > tok > 0
+    assert pp - tok >= (T * k - T) * K * 2
+    assert ftq.pairs_workspace_bytes(E, N, K, T, k, ftq.PATH_GEMV) == ftq.workspace_bytes(E, N, K, T, k, ftq.PATH_GEMV)
+    assert L.ftq_moe_q4_0_q8_1_pairs(base, base, base, base, E, N, K, T, k, base, tok, ftq.PATH_GROUPED, None) == ftq.ERR_WORKSPACE
+    assert "workspace" in ftq.last_error()
+    # combine
+    assert L.ftq_moe_combine_topk(None, None, None, 0, 2, 16, None) == ftq.OK
+    assert L.ftq_moe_combine_topk(base, base, None, 3, 2, 16, None) == ftq.ERR_INVALID_ARG
+    assert L.ftq_moe_combine_topk(base, P(0x100002), base, 3, 2, 16, None) == ftq.ERR_INVALID_ARG
+    assert "misaligned" in ftq.last_error()
+    for T_, k_, N_ in ((-1, 2, 16), (3, 0, 16), (3, 2, 0)):
+        assert L.ftq_moe_combine_topk(base, base, base, T_, k_, N_, None) == ftq.ERR_INVALID_ARG
+    assert L.ftq_moe_combine_topk(base, base, base, 2 ** 40, 8, 2 ** 20, None) == ftq.ERR_UNSUPPORTED

@@ -318,3 +318,83 @@ def test_routing_generators():
     assert all(len(set(r)) == 8 for r in z[:512].tolist())
     assert counts[0] > 20 * counts[-1]                 # hot and cold experts
     assert np.array_equal(inputs.routing(4096, 128, 8, seed=0), u)
+
+
+# ------------------------------------------- second layer: per-pair rows ------
+
+def _tiny_pp(seed=0, E=8, top_k=2, T=16, K=256, N=128, kind="uniform"):
+    """Per-pair activations: one distinct Q8_1 row per (token, slot) pair."""
+    w = oracle.quantize_q4_0(inputs.weights(E, N, K, seed=seed))
+    a = oracle.quantize_q8_1(inputs.activations(T * top_k, K, seed=seed + 101))
+    ids = inputs.routing(T, E, top_k, seed=seed, kind=kind)
+    return w, a, ids, dict(E=E, N=N, K=K, T=T, top_k=top_k)
+
+
+def test_moe_per_pair_exact_rational_bruteforce():
+    """Pair p reads activation row p (not p // top_k): exact Fractions, fp64 error bound."""
+    w, a, ids, c = _tiny_pp(E=3, top_k=3, T=2, K=96, N=4, seed=3)
+    out, ab = _run(w, a, ids, c, want_abssum=True, per_pair=True)
+    wd, wq = _decode.q4_0(w.reshape(3, 4, -1), 96)
+    ad, _, aq = _decode.q8_1(a, 96)
+    for p in range(6):
+        e = int(ids.reshape(-1)[p])
+        for n in range(4):
+            exact = Fraction(0)
+            for b in range(3):
+                P = sum(int(wq[e, n, b, i]) * int(aq[p, b, i]) for i in range(32))
+                exact += Fraction(P) * Fraction(wd[e, n, b]) * Fraction(ad[p, b])
+            assert abs(Fraction(out[p, n]) - exact) <= Fraction(gamma(3, U64)) * Fraction(ab[p, n])
+
+
+def test_moe_per_pair_partials_match_integer_einsum():
+    w, a, ids, c = _tiny_pp(seed=5, kind="zipf")
+    P = oracle.moe_partials(w, a, ids, c["E"], c["N"], c["K"], c["T"], c["top_k"], per_pair=True)
+    _, wq = _decode.q4_0(w.reshape(c["E"], c["N"], -1), c["K"])
+    _, _, aq = _decode.q8_1(a, c["K"])
+    ref = np.einsum("pnbi,pbi->pnb", wq[ids.reshape(-1)], aq)
+    assert P.dtype == np.int32 and np.array_equal(P, ref)
+
+
+def test_moe_per_pair_replicated_rows_equal_per_token():
+    """Per-pair rows that repeat each token's row give the per-token result exactly."""
+    w, a, ids, c = _tiny(seed=6)
+    nb36 = c["K"] // 32 * 36
+    a_rep = np.ascontiguousarray(np.repeat(a.reshape(c["T"], nb36), c["top_k"], axis=0)).reshape(-1)
+    assert np.array_equal(_run(w, a_rep, ids, c, per_pair=True), _run(w, a, ids, c))
+    pairs = np.array([3, 0, 31, 3], np.int64)
+    sub = oracle.moe_pairs(w, a_rep, ids, c["E"], c["N"], c["K"], c["T"], c["top_k"], pairs, per_pair=True)
+    assert np.array_equal(sub, _run(w, a, ids, c)[pairs])
+
+
+def test_moe_per_pair_masked_rows_zero():
+    w, a, ids, c = _tiny_pp(seed=8)
+    bad = ids.copy()
+    bad[2, 1] = -5
+    bad[7, 0] = c["E"] + 3
+    out = _run(w, a, bad, c, per_pair=True)
+    ref = _run(w, a, ids, c, per_pair=True)
+    assert not out[5].any() and not out[14].any()
+    keep = np.ones(out.shape[0], bool)
+    keep[[5, 14]] = False
+    assert np.array_equal(out[keep], ref[keep])
+
+
+def test_combine_topk_bruteforce_and_special_cases():
+    rng = np.random.default_rng(11)
+    T, k, N = 7, 3, 45
+    y = rng.standard_normal((T * k, N))
+    g = rng.random((T, k)).astype(np.float32)
+    out, ab = oracle.combine_topk(y, g, want_abssum=True)
+    exact = [[sum(Fraction(float(g[t, j])) * Fraction(y[t * k + j, n]) for j in range(k))
+              for n in range(N)] for t in range(T)]
+    for t in range(T):
+        for n in range(N):
+            assert abs(Fraction(out[t, n]) - exact[t][n]) <= Fraction(gamma(k + 1, U64)) * Fraction(ab[t, n])
+    # one-hot gates pick one row exactly; k = 1 with gate 1 is the identity
+    sel = rng.integers(0, k, T)
+    oh = np.zeros((T, k), np.float32)
+    oh[np.arange(T), sel] = 1.0
+    assert np.array_equal(oracle.combine_topk(y, oh), y[np.arange(T) * k + sel])
+    assert np.array_equal(oracle.combine_topk(y, np.ones((T * k, 1), np.float32)), y)
+    # a gate of 2 doubles its row exactly
+    assert np.array_equal(oracle.combine_topk(y, 2 * oh), 2 * y[np.arange(T) * k + sel])
