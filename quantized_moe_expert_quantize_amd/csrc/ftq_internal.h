@@ -107,6 +107,17 @@ struct MoeArgs {
 int run_gemv(const MoeArgs& m, const BucketPlan* plan, const void* ws, hipStream_t s);
 constexpr int64_t kGemvScanMaxPairs = 4096;
 
+// Device helper.  Values every lane holds the same copy of (read from LDS or from global memory
+// at a uniform address): moved to scalar registers so that loops over them are
+// scalar loops.
+__device__ __forceinline__ int32_t uniform(int32_t v) { return __builtin_amdgcn_readfirstlane(v); }
+__device__ __forceinline__ int64_t uniform(int64_t v)
+{
+    const uint64_t u = (uint64_t)v;
+    const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)u), hi = __builtin_amdgcn_readfirstlane((uint32_t)(u >> 32));
+    return (int64_t)(((uint64_t)hi << 32) | lo);
+}
+
 // Grouped MFMA path.  Its workspace is the bucket plan's bytes followed by
 // grouped_prep_bytes(activation rows, K) of per-call activation staging.
 int run_grouped(const MoeArgs& m, const BucketPlan& plan, void* ws, hipStream_t s);

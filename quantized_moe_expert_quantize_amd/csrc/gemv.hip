@@ -105,17 +105,6 @@ __host__ __device__ constexpr LdsLayout lds_layout(int64_t E, int64_t seg, int64
 
 __device__ __forceinline__ int64_t bucket_of(int32_t id, int64_t E) { return (id >= 0 && id < E) ? id : E; }
 
-// Values every lane holds the same copy of (read from LDS or from global memory
-// at a uniform address): moved to scalar registers so that loops over them are
-// scalar loops.
-__device__ __forceinline__ int32_t uniform(int32_t v) { return __builtin_amdgcn_readfirstlane(v); }
-__device__ __forceinline__ int64_t uniform(int64_t v)
-{
-    const uint64_t u = (uint64_t)v;
-    const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)u), hi = __builtin_amdgcn_readfirstlane((uint32_t)(u >> 32));
-    return (int64_t)(((uint64_t)hi << 32) | lo);
-}
-
 __device__ __forceinline__ float half_bits_to_float(uint32_t bits)
 {
     return (float)__builtin_bit_cast(_Float16, (uint16_t)bits);

@@ -16,8 +16,9 @@
 //     codes (|q| <= 127) and the Q4_0 values (q-8 in [-8, 7]) are exact in
 //     fp16, every product is an exact small integer and every partial sum stays
 //     below 2^24, so the fp32 result is P_b exactly, in any summation order;
-//   * d4*d8: one more f16 MFMA used as an outer product (only k = 0 non-zero);
-//     a product of two fp16 values is exact in fp32;
+//   * d4*d8: one more f16 MFMA (32x32x8) used as an outer product: both
+//     operands are read from LDS as {scale, 0, 0, 0}, so only k = 0 adds and a
+//     product of two fp16 values is exact in fp32;
 //   * the vector ALUs then do a single fp32 FMA per element and block:
 //     acc = fma(P_b, d4*d8, acc), blocks in ascending order.
 // Doing the products on the MFMA units leaves one VALU op per element-block,
@@ -32,7 +33,9 @@
 // four packed fp16 pairs with one mask-or and one packed add each; the
 // activation codes are written in that same order, so the dot products match.
 // Tiles are double buffered in LDS (loads for block pair s+1 are in flight while
-// block pair s is multiplied).  Workgroups are mapped to tiles XCD by XCD: each
+// block pair s is multiplied); the global loads are buffer loads whose per-lane
+// offsets are fixed for a tile and whose per-pass advance is a scalar offset.
+// In ragged tiles a wave whose rows hold no pair skips its MFMA work.  Workgroups are mapped to tiles XCD by XCD: each
 // of the 8 XCDs takes a contiguous range of tiles, walked in groups of kGroupM
 // M tiles with the N tiles inner, so a gathered activation tile and an expert's
 // weight tiles are reused from that XCD's L2.
@@ -44,6 +47,7 @@ namespace ftq {
 namespace {
 
 typedef _Float16 v8h __attribute__((ext_vector_type(8)));
+typedef _Float16 v4h __attribute__((ext_vector_type(4)));
 typedef _Float16 h2 __attribute__((ext_vector_type(2)));
 typedef float v16f __attribute__((ext_vector_type(16)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
@@ -52,9 +56,28 @@ constexpr int kThreads = 256;
 constexpr int kBN = 128;          // weight rows per tile
 constexpr int kKB = 2;            // quantisation blocks per staged pass
 constexpr int kBlockF16 = 64;     // bytes of one block's 32 fp16 codes
-constexpr int kRowBytes = kKB * kBlockF16 + 16;   // LDS bytes per staged row (+16: bank skew)
+constexpr int kRowBytes = kKB * kBlockF16;   // LDS bytes per staged row (16-byte chunks, swizzled)
 constexpr int kXcds = 8;
 constexpr int kGroupM = 4;
+constexpr int kBufferFlags = 0x00020000;      // raw buffer resource: 32-bit data, no swizzle
+
+// LDS row layout: 16-byte chunk c (0..7) of staged row r sits at chunk
+// c ^ f(r), f(r) = (r & 7) ^ ((r >> 3) & 1).  Lanes reading one logical chunk
+// of consecutive rows then hit 8 distinct chunks in every 8 consecutive rows
+// and in every 8 rows of one parity among 16, so the fragment reads (32 rows
+// per half-wave) and the stage writes (8 chunks of one row) are free of bank
+// conflicts for 8 or for 16 lanes served per clock.  f depends on r % 16 only,
+// so every 32-row sub-tile has the swizzle of its lane's row l32.
+__device__ __forceinline__ int row_swizzle(int r) { return (r & 7) ^ ((r >> 3) & 1); }
+__device__ __forceinline__ int lds_chunk(int r, int c) { return r * kRowBytes + ((c ^ row_swizzle(r)) << 4); }
+
+// Buffer resource over `range` bytes from `base` (range: a 32-bit unsigned
+// count carried in an int).  Both arguments must be wave-uniform: a resource
+// the compiler thinks divergent costs a loop per load.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, int range)
+{
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, range, kBufferFlags);
+}
 
 struct GroupedParams {
     const uint8_t* w;
@@ -67,6 +90,9 @@ struct GroupedParams {
     const int32_t* sorted;
     int64_t E, N, nb, top_k, nbuckets, n_tiles_n, max_mt;
     int64_t act_div;          // activation row of pair p: p / act_div
+    int32_t a16_range;        // buffer ranges in bytes (32-bit unsigned counts): a16, d8
+    int32_t d8_range;         // (narrow variant only: a16 below 4 GiB)
+    int32_t wtile_range;      // bytes of kBN weight rows
 };
 
 // Waves per workgroup for BM = 128 tiles.  4 waves of 64x64 (two workgroups
@@ -93,8 +119,8 @@ template <int BM>
 struct Smem {
     uint8_t a[2][BM * kRowBytes];
     uint8_t b[2][kBN * kRowBytes];
-    uint32_t as[2][kKB][BM];    // fp16 scale bits of A rows (upper half zero)
-    uint32_t bs[2][kKB][kBN + 1];   // fp16 scale bits of weight rows; entry kBN stays 0
+    uint2 as[2][kKB][BM];        // {fp16 scale bits, 0} of the A rows
+    uint2 bs[2][kKB][kBN + 1];   // {fp16 scale bits, 0} of the weight rows; entry kBN stays zero
     int32_t row_pair[BM];
     int32_t row_tok[BM];
 };
@@ -103,13 +129,15 @@ struct Smem {
 // a block holds elements 4j..4j+3 in its low nibbles and 16+4j..16+4j+3 in its
 // high nibbles; the outputs are the pairs (4j, 4j+2), (4j+1, 4j+3),
 // (16+4j, 16+4j+2), (16+4j+1, 16+4j+3).  0x6400 | q is the fp16 1024 + q.
-__device__ __forceinline__ void nibbles_to_f16(uint32_t x, uint32_t o[4])
+// mask = 0x000f000f and magic = 0x64006400 come in registers so that each
+// mask-and-or is one instruction.
+__device__ __forceinline__ void nibbles_to_f16(uint32_t x, uint32_t mask, uint32_t magic, uint32_t o[4])
 {
     const h2 bias = {(_Float16)-1032.0f, (_Float16)-1032.0f};
-    const uint32_t t0 = (x & 0x000f000fu) | 0x64006400u;
-    const uint32_t t1 = ((x >> 8) & 0x000f000fu) | 0x64006400u;
-    const uint32_t t2 = ((x >> 4) & 0x000f000fu) | 0x64006400u;
-    const uint32_t t3 = ((x >> 12) & 0x000f000fu) | 0x64006400u;
+    const uint32_t t0 = (x & mask) | magic;
+    const uint32_t t1 = ((x >> 8) & mask) | magic;
+    const uint32_t t2 = ((x >> 4) & mask) | magic;
+    const uint32_t t3 = ((x >> 12) & mask) | magic;
     o[0] = __builtin_bit_cast(uint32_t, __builtin_bit_cast(h2, t0) + bias);
     o[1] = __builtin_bit_cast(uint32_t, __builtin_bit_cast(h2, t1) + bias);
     o[2] = __builtin_bit_cast(uint32_t, __builtin_bit_cast(h2, t2) + bias);
@@ -181,7 +209,9 @@ __global__ __launch_bounds__(Shape<BM>::kThreads, Shape<BM>::kWavesPerSimd) void
     constexpr int kThreads = S::kThreads;
     __shared__ __align__(16) Smem<BM> sm;
 
-    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    // the wave index is uniform per wave: say so, so that what derives from it
+    // (sub-tile counts, loop control) stays in scalar registers
+    const int tid = threadIdx.x, lane = tid & 63, wave = uniform((int32_t)(tid >> 6));
     const int wm = wave / S::WN, wn = wave % S::WN;
     const int half = lane >> 5, l32 = lane & 31;
     const int64_t total_tiles = p.tiles[p.nbuckets];
@@ -189,6 +219,11 @@ __global__ __launch_bounds__(Shape<BM>::kThreads, Shape<BM>::kWavesPerSimd) void
     const bool direct = (int64_t)gridDim.x >= work;   // one workgroup per tile: remap by XCD
     const int64_t nb = p.nb;
     const int64_t nbp = padded_blocks(nb);
+
+    uint32_t nib_mask = 0x000f000fu, nib_magic = 0x64006400u;
+    __asm__ volatile("" : "+v"(nib_mask), "+v"(nib_magic));
+    const __amdgpu_buffer_rsrc_t ars = make_rsrc(p.a16, p.a16_range);
+    const __amdgpu_buffer_rsrc_t drs = make_rsrc(p.d8, p.d8_range);
 
     for (int64_t w = blockIdx.x; w < work; w += gridDim.x) {
         const int64_t L = direct ? xcd_remap(w, work) : w;
@@ -217,7 +252,7 @@ __global__ __launch_bounds__(Shape<BM>::kThreads, Shape<BM>::kWavesPerSimd) void
             sm.row_pair[m] = pid;
             sm.row_tok[m] = (int32_t)(pid / p.act_div);
         }
-        if (tid < 2 * kKB) sm.bs[tid / kKB][tid % kKB][kBN] = 0u;
+        if (tid < 2 * kKB) sm.bs[tid / kKB][tid % kKB][kBN] = uint2{0u, 0u};
         __syncthreads();
 
         if (bucket == p.E) {   // masked pairs: zero rows
@@ -235,34 +270,43 @@ __global__ __launch_bounds__(Shape<BM>::kThreads, Shape<BM>::kWavesPerSimd) void
         }
 
         // ---- per-tile staging plan ------------------------------------------
-        // Every address is a per-thread offset fixed for the tile plus a base
-        // that is uniform across the workgroup and advances by a constant per
-        // pass.  Rows past the tile (A) or past N (B) read valid memory and are
-        // never stored.  The activations are padded to whole passes; a weight
-        // block past K/32 (odd K/32, last pass only) is read from block K/32-1
-        // with scale 0, so it adds fma(P, 0, acc) = acc exactly.
+        // Every global address is a per-thread offset fixed for the tile plus
+        // a workgroup-uniform offset that advances by a constant per pass (the
+        // scalar offset of a buffer load).  Rows past the tile (A) or past N
+        // (B) read valid memory and are never stored.  The activations are
+        // padded to whole passes; a weight block past K/32 (odd K/32, last pass
+        // only) is read from block K/32-1 with scale 0, so it adds
+        // fma(P, 0, acc) = acc exactly.
         // A: BM rows x kKB blocks x 64 B = BM*8 units of 16 B (unit c of a row: block c/4, piece c%4)
         constexpr int kAUnits = BM * kKB * 4;
         constexpr int kAPer = (kAUnits + kThreads - 1) / kThreads;
         static_assert(kAUnits % kThreads == 0, "whole A units per thread");
         using AOff = typename std::conditional<kWide, int64_t, uint32_t>::type;
         AOff a_off_g[kAPer];
+        int a_lds[kAPer];
 #pragma unroll
         for (int i = 0; i < kAPer; ++i) {
             const int u = tid + i * kThreads;
             const int m = u >> 3, c = u & 7;
             a_off_g[i] = (AOff)(((int64_t)sm.row_tok[m < rows ? m : 0] * nbp + (c >> 2)) * kBlockF16 + (c & 3) * 16);
+            a_lds[i] = lds_chunk(m, c);
         }
-        // A scales: thread < BM*kKB owns (row tid % BM, block tid / BM)
-        const int d_m = tid % BM, d_blk = tid / BM;
-        const AOff d_off = (AOff)((int64_t)sm.row_tok[d_m < rows ? d_m : 0] * nbp + d_blk);
+        // A scales: thread < BM*kKB owns (row tid % BM, block tid / BM); the
+        // others load a valid scale and do not store it
+        const int d_m = tid % BM, d_blk = min(tid / BM, kKB - 1);
+        const bool d_thread = tid < BM * kKB;
+        const uint32_t d_off = (uint32_t)(((int64_t)sm.row_tok[d_m < rows ? d_m : 0] * nbp + d_blk) * 2);
         // B: one block (18 B) of one weight row per thread of the first
         // kBN * kKB threads; bh is uniform per wave
         static_assert(kBN * kKB <= kThreads, "one weight block per thread");
         const bool b_thread = tid < kBN * kKB;
-        const int bn = tid % kBN, bh = (tid / kBN) % kKB;
-        const uint8_t* wtile = p.w + (bucket * p.N + n0) * nb * kQ4Bytes;   // uniform per tile
+        const int bn = tid % kBN, bh = uniform((int32_t)((tid / kBN) % kKB));
+        const uint8_t* wtile = p.w + (uniform(bucket) * p.N + uniform(n0)) * nb * kQ4Bytes;   // uniform per tile
+        const __amdgpu_buffer_rsrc_t wrs = make_rsrc(wtile, p.wtile_range);
         const uint32_t bg_off = (uint32_t)((n0 + bn < p.N ? bn : 0) * nb * kQ4Bytes);
+        int b_lds[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) b_lds[i] = lds_chunk(bn, bh * 4 + i);
 
         u32x4 ra[kAPer];
         uint32_t rb[5];
@@ -270,34 +314,41 @@ __global__ __launch_bounds__(Shape<BM>::kThreads, Shape<BM>::kWavesPerSimd) void
         bool rb_ok;
 
         auto issue = [&](int64_t kb0) {
-            const uint8_t* abase = p.a16 + kb0 * kBlockF16;
+            if constexpr (kWide) {
+                const uint8_t* abase = p.a16 + kb0 * kBlockF16;
 #pragma unroll
-            for (int i = 0; i < kAPer; ++i) ra[i] = *reinterpret_cast<const u32x4*>(abase + a_off_g[i]);
-            if (tid < BM * kKB) rd8 = p.d8[kb0 + d_off];
+                for (int i = 0; i < kAPer; ++i) ra[i] = *reinterpret_cast<const u32x4*>(abase + a_off_g[i]);
+                rd8 = p.d8[kb0 + d_off / 2];
+            } else {
+                const int soff = uniform((int32_t)(kb0 * kBlockF16));
+#pragma unroll
+                for (int i = 0; i < kAPer; ++i)
+                    ra[i] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(ars, a_off_g[i], soff, 0));
+                rd8 = __builtin_amdgcn_raw_buffer_load_b16(drs, d_off, uniform((int32_t)(kb0 * 2)), 0);
+            }
             // past K/32 only in the last pass of an odd K/32; uniform per wave
             rb_ok = kb0 + bh < nb;
-            const int64_t kb = rb_ok ? kb0 + bh : nb - 1;
             if (!b_thread) return;
+            const int wsoff = uniform((int32_t)(kb0 * kQ4Bytes));
             if constexpr (VEC == 4) {
                 // a pair of blocks starts 4-byte aligned (K/32 even, kb0 even):
                 // block kb0 is words 0..4 of the pair, block kb0+1 words 4..8
-                const uint32_t* wp = reinterpret_cast<const uint32_t*>(wtile + bg_off + kb0 * kQ4Bytes) + 4 * bh;
-#pragma unroll
-                for (int i = 0; i < 5; ++i) rb[i] = wp[i];
+                const u32x4 w4 = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(wrs, bg_off + 16 * bh, wsoff, 0));
+                rb[0] = w4.x; rb[1] = w4.y; rb[2] = w4.z; rb[3] = w4.w;
+                rb[4] = __builtin_amdgcn_raw_buffer_load_b32(wrs, bg_off + 16 * bh + 16, wsoff, 0);
             } else {
-                const uint16_t* hp = reinterpret_cast<const uint16_t*>(wtile + bg_off + kb * kQ4Bytes);
-                rb[0] = hp[0];
+                const uint32_t boff = bg_off + (uint32_t)((rb_ok ? bh : nb - 1 - kb0) * kQ4Bytes);
+                rb[0] = __builtin_amdgcn_raw_buffer_load_b16(wrs, boff, wsoff, 0);
 #pragma unroll
-                for (int i = 0; i < 4; ++i) rb[1 + i] = (uint32_t)hp[1 + 2 * i] | ((uint32_t)hp[2 + 2 * i] << 16);
+                for (int i = 0; i < 4; ++i)
+                    rb[1 + i] = (uint32_t)__builtin_amdgcn_raw_buffer_load_b16(wrs, boff + 2 + 4 * i, wsoff, 0) |
+                                ((uint32_t)__builtin_amdgcn_raw_buffer_load_b16(wrs, boff + 4 + 4 * i, wsoff, 0) << 16);
             }
         };
         auto commit = [&](int buf) {
 #pragma unroll
-            for (int i = 0; i < kAPer; ++i) {
-                const int u = tid + i * kThreads;
-                *reinterpret_cast<u32x4*>(&sm.a[buf][(u >> 3) * kRowBytes + (u & 7) * 16]) = ra[i];
-            }
-            if (tid < BM * kKB) sm.as[buf][d_blk][d_m] = rd8;
+            for (int i = 0; i < kAPer; ++i) *reinterpret_cast<u32x4*>(&sm.a[buf][a_lds[i]]) = ra[i];
+            if (d_thread) sm.as[buf][d_blk][d_m] = uint2{rd8 & 0xffffu, 0u};
             if (!b_thread) return;
             // weight block -> 32 fp16 values (q - 8) and its scale
             uint32_t dbits, qs[4];
@@ -316,29 +367,35 @@ __global__ __launch_bounds__(Shape<BM>::kThreads, Shape<BM>::kWavesPerSimd) void
                 dbits = rb[0];
                 qs[0] = rb[1]; qs[1] = rb[2]; qs[2] = rb[3]; qs[3] = rb[4];
             }
-            uint32_t o[16];
 #pragma unroll
-            for (int j = 0; j < 4; ++j) nibbles_to_f16(qs[j], &o[4 * j]);
-            u32x4* dst = reinterpret_cast<u32x4*>(&sm.b[buf][bn * kRowBytes + bh * kBlockF16]);
-#pragma unroll
-            for (int i = 0; i < 4; ++i) dst[i] = u32x4{o[4 * i], o[4 * i + 1], o[4 * i + 2], o[4 * i + 3]};
-            sm.bs[buf][bh][bn] = rb_ok ? dbits : 0u;
+            for (int j = 0; j < 4; ++j) {
+                uint32_t o[4];
+                nibbles_to_f16(qs[j], nib_mask, nib_magic, o);
+                *reinterpret_cast<u32x4*>(&sm.b[buf][b_lds[j]]) = u32x4{o[0], o[1], o[2], o[3]};
+            }
+            sm.bs[buf][bh][bn] = uint2{rb_ok ? dbits : 0u, 0u};
         };
 
-        // LDS read offsets of this lane's fragments (constant over the K loop)
-        int a_off[S::SM], b_off[S::SN], as_off[S::SM], bs_off[S::SN];
+        // LDS read offsets of this lane's fragments (constant over the K loop):
+        // rows of a sub-tile start at multiples of 32, so the swizzle of row r
+        // is that of l32 and sub-tile and buffer offsets are immediates.
+        // frag[blk][s]: this lane's chunk (block blk, piece 2*half + s)
+        int frag_a[kKB][2], frag_b[kKB][2];
 #pragma unroll
-        for (int i = 0; i < S::SM; ++i) {
-            const int m = (wm * S::SM + i) * 32 + l32;
-            a_off[i] = m * kRowBytes + 32 * half;
-            as_off[i] = m;
-        }
+        for (int blk = 0; blk < kKB; ++blk)
 #pragma unroll
-        for (int j = 0; j < S::SN; ++j) {
-            const int n = (wn * S::SN + j) * 32 + l32;
-            b_off[j] = n * kRowBytes + 32 * half;
-            bs_off[j] = half ? kBN : n;   // upper-half lanes read the zero slot
-        }
+            for (int s2 = 0; s2 < 2; ++s2) {
+                const int c = (blk * 4 + 2 * half + s2) ^ row_swizzle(l32);
+                frag_a[blk][s2] = (wm * S::SM * 32 + l32) * kRowBytes + (c << 4);
+                frag_b[blk][s2] = (wn * S::SN * 32 + l32) * kRowBytes + (c << 4);
+            }
+        const int as_row = wm * S::SM * 32 + l32;
+        int bs_row[S::SN];
+#pragma unroll
+        for (int j = 0; j < S::SN; ++j) bs_row[j] = half ? kBN : (wn * S::SN + j) * 32 + l32;   // upper half: zero slot
+
+        // does any row of this wave hold a pair (uniform per wave)
+        const bool wave_rows = uniform((int32_t)(wm * S::SM * 32 < rows)) != 0;
 
         v16f acc[S::SM][S::SN];
 #pragma unroll
@@ -348,65 +405,49 @@ __global__ __launch_bounds__(Shape<BM>::kThreads, Shape<BM>::kWavesPerSimd) void
 #pragma unroll
                 for (int k = 0; k < 16; ++k) acc[i][j][k] = 0.0f;
 
-        // One staged pass: kKB blocks from LDS buffer `buf`.  (Issuing the next
-        // sub-tile's MFMAs before the current FMAs needs a second set of result
-        // registers and spills at BM = 128; two waves per SIMD overlap instead.)
+        // One staged pass: kKB blocks from LDS buffer `buf`
         auto compute = [&](int buf, int64_t kb0) {
-#pragma unroll 1
+            if (!wave_rows) return;
+#pragma unroll
             for (int blk = 0; blk < kKB; ++blk) {
                 v8h alo[S::SM], ahi[S::SM], blo[S::SN], bhi[S::SN];
-                u32x4 as_v[S::SM], bs_v[S::SN];
+                v4h as_v[S::SM], bs_v[S::SN];
 #pragma unroll
                 for (int ii = 0; ii < S::SM; ++ii) {
-                    const uint8_t* src = &sm.a[buf][a_off[ii] + blk * kBlockF16];
-                    alo[ii] = *reinterpret_cast<const v8h*>(src);
-                    ahi[ii] = *reinterpret_cast<const v8h*>(src + 16);
-                    as_v[ii] = u32x4{sm.as[buf][blk][as_off[ii]], 0, 0, 0};
+                    alo[ii] = *reinterpret_cast<const v8h*>(&sm.a[buf][frag_a[blk][0] + ii * 32 * kRowBytes]);
+                    ahi[ii] = *reinterpret_cast<const v8h*>(&sm.a[buf][frag_a[blk][1] + ii * 32 * kRowBytes]);
+                    as_v[ii] = __builtin_bit_cast(v4h, sm.as[buf][blk][as_row + ii * 32]);
                 }
 #pragma unroll
                 for (int jj = 0; jj < S::SN; ++jj) {
-                    const uint8_t* src = &sm.b[buf][b_off[jj] + blk * kBlockF16];
-                    blo[jj] = *reinterpret_cast<const v8h*>(src);
-                    bhi[jj] = *reinterpret_cast<const v8h*>(src + 16);
-                    bs_v[jj] = u32x4{sm.bs[buf][blk][bs_off[jj]], 0, 0, 0};
+                    blo[jj] = *reinterpret_cast<const v8h*>(&sm.b[buf][frag_b[blk][0] + jj * 32 * kRowBytes]);
+                    bhi[jj] = *reinterpret_cast<const v8h*>(&sm.b[buf][frag_b[blk][1] + jj * 32 * kRowBytes]);
+                    bs_v[jj] = __builtin_bit_cast(v4h, sm.bs[buf][blk][bs_row[jj]]);
                 }
-                constexpr int kSub = S::SM * S::SN;
-                v16f P, Sc;
-                auto mfmas = [&](int t, v16f& Pt, v16f& St) {
-                    const int i = t / S::SN, j = t % S::SN;
-                    Pt = __builtin_amdgcn_mfma_f32_32x32x16_f16(alo[i], blo[j], v16f{}, 0, 0, 0);
-                    Pt = __builtin_amdgcn_mfma_f32_32x32x16_f16(ahi[i], bhi[j], Pt, 0, 0, 0);
-                    if constexpr (!kPartials)
-                        St = __builtin_amdgcn_mfma_f32_32x32x16_f16(
-                            __builtin_bit_cast(v8h, as_v[i]), __builtin_bit_cast(v8h, bs_v[j]), v16f{}, 0, 0, 0);
-                };
-                auto consume = [&](int t, const v16f& Pt, const v16f& St) {
-                    const int i = t / S::SN, j = t % S::SN;
-                    if constexpr (kPartials) {
-                        const int64_t n = n0 + (wn * S::SN + j) * 32 + l32;
-                        const int64_t b = kb0 + blk;
 #pragma unroll
-                        for (int r = 0; r < 16; ++r) {
-                            const int m = (wm * S::SM + i) * 32 + 8 * (r / 4) + 4 * half + (r % 4);
-                            if (m < rows && n < p.N && b < nb)
-                                p.partials[((int64_t)sm.row_pair[m] * p.N + n) * nb + b] = (int32_t)Pt[r];
+                for (int i = 0; i < S::SM; ++i) {
+#pragma unroll
+                    for (int j = 0; j < S::SN; ++j) {
+                        v16f P = __builtin_amdgcn_mfma_f32_32x32x16_f16(alo[i], blo[j], v16f{}, 0, 0, 0);
+                        P = __builtin_amdgcn_mfma_f32_32x32x16_f16(ahi[i], bhi[j], P, 0, 0, 0);
+                        if constexpr (kPartials) {
+                            const int64_t n = n0 + (wn * S::SN + j) * 32 + l32;
+                            const int64_t b = kb0 + blk;
+#pragma unroll
+                            for (int r = 0; r < 16; ++r) {
+                                const int m = (wm * S::SM + i) * 32 + 8 * (r / 4) + 4 * half + (r % 4);
+                                if (m < rows && n < p.N && b < nb)
+                                    p.partials[((int64_t)sm.row_pair[m] * p.N + n) * nb + b] = (int32_t)P[r];
+                            }
+                        } else {
+                            const v16f Sc = __builtin_amdgcn_mfma_f32_32x32x8f16(as_v[i], bs_v[j], v16f{}, 0, 0, 0);
+#pragma unroll
+                            for (int r = 0; r < 16; ++r) acc[i][j][r] = __builtin_fmaf(P[r], Sc[r], acc[i][j][r]);
                         }
-                    } else {
-#pragma unroll
-                        for (int r = 0; r < 16; ++r) acc[i][j][r] = __builtin_fmaf(Pt[r], St[r], acc[i][j][r]);
                     }
-                };
-#pragma unroll
-                for (int t = 0; t < kSub; ++t) {
-                    mfmas(t, P, Sc);
-                    consume(t, P, Sc);
-                    // one sub-tile's results live at a time (the register budget
-                    // of four waves per SIMD has no room for two)
-                    if constexpr (S::kWaves == 8) __builtin_amdgcn_sched_barrier(0);
                 }
             }
         };
-
         // ---- K loop: double-buffered, unrolled by two so buffers are constants
         const int64_t nstages = nbp / kKB;
         issue(0);
@@ -519,6 +560,11 @@ int run_grouped(const MoeArgs& m, const BucketPlan& plan, void* ws, hipStream_t 
     gp.nb = nb;
     gp.top_k = m.top_k;
     gp.act_div = m.act_div;
+    // buffer ranges: 32-bit unsigned byte counts (the narrow variant's a16 is below 4 GiB)
+    auto range32 = [](int64_t bytes) { return (int32_t)(uint32_t)std::min<int64_t>(bytes, UINT32_MAX); };
+    gp.a16_range = range32(act_rows * nbp * kBlockF16);
+    gp.d8_range = range32(act_rows * nbp * 2);
+    gp.wtile_range = range32((int64_t)kBN * nb * kQ4Bytes);
     gp.nbuckets = plan.buckets;
     gp.n_tiles_n = (m.N + kBN - 1) / kBN;
     const int64_t bm = plan.tile_m;
