@@ -66,6 +66,9 @@ def _load():
     lib.oracle_moe_pairs_ex.argtypes = [P, P, P, I64, I64, I64, I64, I64, I64, P, I64, P, P]
     lib.oracle_moe_partials_ex.argtypes = [P, P, P, I64, I64, I64, I64, I64, I64, P]
     lib.oracle_combine_topk.argtypes = [P, P, I64, I64, I64, P, P]
+    lib.oracle_act.argtypes = [ctypes.c_int, ctypes.c_double]
+    lib.oracle_act.restype = ctypes.c_double
+    lib.oracle_act_and_mul.argtypes = [P, I64, I64, ctypes.c_int, P]
     lib.oracle_num_threads.restype = ctypes.c_int
     _lib = lib
     return lib
@@ -153,6 +156,24 @@ def moe_partials(w, a, ids, E, N, K, T, top_k, per_pair=False):
     div = _check(w, a, ids, E, N, K, T, top_k, per_pair)
     out = np.empty((T * top_k, N, K // QK), np.int32)
     _load().oracle_moe_partials_ex(_ptr(w), _ptr(a), _ptr(ids), E, N, K, T, top_k, div, _ptr(out))
+    return out
+
+
+ACT_SILU, ACT_GELU_TANH = 1, 2
+
+
+def act(kind: int, x: float) -> float:
+    """SiLU (kind 1) or tanh-approximated GELU (kind 2) of one value, fp64."""
+    return float(_load().oracle_act(int(kind), float(x)))
+
+
+def act_and_mul(y, kind: int):
+    """fp64 [rows, I]: act(y[:, :I]) * y[:, I:] for y [rows, 2I] (gate half first)."""
+    y = np.ascontiguousarray(y, dtype=np.float64)
+    assert y.ndim == 2 and y.shape[1] % 2 == 0
+    rows, I = y.shape[0], y.shape[1] // 2
+    out = np.empty((rows, I), np.float64)
+    _load().oracle_act_and_mul(_ptr(y), rows, I, int(kind), _ptr(out))
     return out
 
 

@@ -22,6 +22,13 @@
  *     of t.  Its outputs are combined per token as the router-weighted sum
  *     out[t][n] = sum_j gates[t][j] * y[t*top_k + j][n] (the usual top-k MoE
  *     combine; the pages do not print it).
+ *   - The first layer's output feeds a gated activation: the matmul output of
+ *     a pair holds the gate in columns [0, I) and the up projection in
+ *     [I, 2I), and the layer's output is act(gate) * up, [rows][I].  The
+ *     activations are the tanh-approximated GELU that follows the GEMV in
+ *     FreeToken PR #185 (Problem) and SiLU ("Current Bug: CuTeDSLMoERunner",
+ *     Bug 6).  The [gate | up] order of the halves is a reading; the pages
+ *     print no layout.
  *   - The byte layouts are the GGUF Q4_0 / Q8_1 blocks the FreeToken page
  *     serves ("Tested on": a Q4_0 .gguf checkpoint).  The pages name the
  *     formats but do not print them; the readings used here are:
@@ -338,6 +345,30 @@ void oracle_combine_topk(const double* y, const float* gates, int64_t T, int64_t
             if (abssum) abssum[t * N + n] = aabs;
         }
     }
+}
+
+/* Gated activations in fp64 (libm exp and tanh):
+ *   act 1, SiLU:      x / (1 + exp(-x))
+ *   act 2, GELU-tanh: x / 2 * (1 + tanh(sqrt(2/pi) * (x + 0.044715 x^3))) */
+double oracle_act(int act, double x)
+{
+    if (act == 1) return x / (1.0 + exp(-x));
+    if (act == 2) {
+        const double k = sqrt(2.0 / 3.14159265358979323846);
+        return 0.5 * x * (1.0 + tanh(k * (x + 0.044715 * x * x * x)));
+    }
+    return NAN;
+}
+
+/* y: [rows][2 I] fp64, gate in columns [0, I), up in [I, 2 I);
+ * out[r][c] = act(y[r][c]) * y[r][I + c], out: [rows][I]. */
+void oracle_act_and_mul(const double* y, int64_t rows, int64_t I, int act, double* out)
+{
+    int64_t r;
+#pragma omp parallel for schedule(static)
+    for (r = 0; r < rows; ++r)
+        for (int64_t c = 0; c < I; ++c)
+            out[r * I + c] = oracle_act(act, y[r * 2 * I + c]) * y[r * 2 * I + I + c];
 }
 
 int oracle_num_threads(void)

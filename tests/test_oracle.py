@@ -398,3 +398,43 @@ def test_combine_topk_bruteforce_and_special_cases():
     assert np.array_equal(oracle.combine_topk(y, np.ones((T * k, 1), np.float32)), y)
     # a gate of 2 doubles its row exactly
     assert np.array_equal(oracle.combine_topk(y, 2 * oh), 2 * y[np.arange(T) * k + sel])
+
+
+# ----------------------------------------------- gated activations ------
+
+def test_silu_closed_forms_and_logistic_identity():
+    from scipy.special import expit
+    assert oracle.act(oracle.ACT_SILU, 0.0) == 0.0
+    assert abs(oracle.act(oracle.ACT_SILU, np.log(3.0)) - 0.75 * np.log(3.0)) <= 4 * U64
+    rng = np.random.default_rng(3)
+    for x in np.concatenate([rng.standard_normal(200) * 4, [-30.0, -7.5, 7.5, 30.0]]):
+        s, sm = oracle.act(oracle.ACT_SILU, x), oracle.act(oracle.ACT_SILU, -x)
+        assert abs((s - sm) - x) <= 8 * U64 * (abs(x) + 1)            # silu(x) - silu(-x) = x
+        assert abs(s - x * expit(x)) <= 8 * U64 * (abs(x) + 1)        # x * logistic(x)
+
+
+def test_gelu_tanh_identities_and_distance_to_erf_gelu():
+    from scipy.special import erf
+    assert oracle.act(oracle.ACT_GELU_TANH, 0.0) == 0.0
+    xs = np.linspace(-9.0, 9.0, 3601)
+    g = np.array([oracle.act(oracle.ACT_GELU_TANH, x) for x in xs])
+    gm = np.array([oracle.act(oracle.ACT_GELU_TANH, -x) for x in xs])
+    assert np.all(np.abs((g - gm) - xs) <= 16 * U64 * (np.abs(xs) + 1))   # odd part is x / 2
+    exact_gelu = 0.5 * xs * (1 + erf(xs / np.sqrt(2.0)))
+    # the tanh form approximates the erf form to within 5e-4 everywhere; a wrong
+    # constant (0.44715 for 0.044715, sqrt(2 pi) for sqrt(2 / pi)) misses by > 1e-3
+    assert np.abs(g - exact_gelu).max() <= 5e-4
+    assert abs(oracle.act(oracle.ACT_GELU_TANH, 9.0) - 9.0) < 1e-12       # saturates to x
+
+
+def test_act_and_mul_takes_gate_from_the_first_half():
+    y = np.array([[np.log(3.0), -1.0, 2.0, 5.0],
+                  [0.0, 2.5, 7.0, -3.0]])
+    out = oracle.act_and_mul(y, oracle.ACT_SILU)
+    assert out.shape == (2, 2)
+    assert abs(out[0, 0] - 0.75 * np.log(3.0) * 2.0) <= 8 * U64
+    assert out[1, 0] == 0.0                                            # silu(0) * 7
+    s25 = oracle.act(oracle.ACT_SILU, 2.5)
+    assert out[1, 1] == s25 * -3.0
+    swapped = oracle.act_and_mul(np.concatenate([y[:, 2:], y[:, :2]], axis=1), oracle.ACT_SILU)
+    assert not np.allclose(swapped, out)
