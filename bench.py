@@ -11,6 +11,7 @@ before timing starts.
 
     python bench.py [--steps K] [--warmup W] [--T tokens]
     python bench.py --workload page1_down  # the second layer: per-pair rows + combine
+    python bench.py --workload page1_act   # the first layer with act(gate) * up fused
     python bench.py --mode profile         # a short run for rocprofv3
     python bench.py --summarize-pmc DIR    # HBM traffic from rocprofv3 --pmc runs
 
@@ -41,7 +42,9 @@ DEFAULT_T = 8191
 # (`--workload`); the bench line proper is the page-1 workload above.
 # A "down" workload is the second layer of the expert FFN: one Q8_1 row per
 # (token, slot) pair in, the expert width as K and the hidden size as N, then
-# the per-token router-weighted combine of the k pair outputs.
+# the per-token router-weighted combine of the k pair outputs.  An "act"
+# workload is the first layer with its gated activation fused: N weight rows
+# per expert (gate rows, then up rows), output act(gate) * up of width N/2.
 WORKLOADS = {
     "page1": (WORKLOAD, DEFAULT_T),
     "mixtral": (dict(workload="mixtral_8x7b_up", E=8, N=14336, K=4096, top_k=2, routing="uniform", seed=0), 8),
@@ -52,6 +55,12 @@ WORKLOADS = {
                           routing="uniform", seed=0), 8),
     "qwen_down": (dict(workload="qwen3_30b_a3b_down", layer="down", E=128, N=2048, K=768, top_k=8,
                        routing="zipf", seed=0), 8192),
+    "page1_act": (dict(workload="freetoken_pr185_moe_q4_0_gelu_tanh_and_mul", layer="act", act="gelu_tanh", E=128,
+                       N=1408, K=2816, top_k=8, routing="uniform", seed=0), DEFAULT_T),
+    "mixtral_act": (dict(workload="mixtral_8x7b_gate_up_silu", layer="act", act="silu", E=8, N=28672, K=4096,
+                         top_k=2, routing="uniform", seed=0), 8),
+    "qwen_act": (dict(workload="qwen3_30b_a3b_gate_up_silu", layer="act", act="silu", E=128, N=1536, K=2048,
+                      top_k=8, routing="zipf", seed=0), 8192),
 }
 # The pages' own measurement of this workload: the fixed GEMV kernel at 8191
 # tokens on a Tesla T4 (FreeToken PR #185, Performance), the faster of two runs.
@@ -71,15 +80,16 @@ def _lib_hash() -> str:
     return open(p).read().strip() if os.path.exists(p) else ""
 
 
-def _algorithmic_bytes(E, N, K, T, k, ids, act_rows=None):
+def _algorithmic_bytes(E, N, K, T, k, ids, act_rows=None, out_cols=None):
     """Bytes the method must move: the distinct experts' Q4_0 rows, the Q8_1
     activations (one row per token, or per pair), the int32 ids and the fp32
-    output."""
+    output (N columns, or N/2 with the activation fused)."""
     import numpy as np
     nb = K // 32
     rows = T if act_rows is None else act_rows
+    cols = N if out_cols is None else out_cols
     distinct = len(np.unique(ids[(ids >= 0) & (ids < E)]))
-    return distinct * N * nb * 18 + rows * nb * 36 + 4 * T * k + 4 * T * k * N
+    return distinct * N * nb * 18 + rows * nb * 36 + 4 * T * k + 4 * T * k * cols
 
 
 def summarize_pmc(d: str, kernel: str = DOMINANT) -> None:
@@ -150,7 +160,10 @@ def main() -> None:
     T = args.T if args.T is not None else wl_T
     seed = wl["seed"]
     down = wl.get("layer") == "down"
+    fused = wl.get("layer") == "act"
+    act_kind = {"silu": 1, "gelu_tanh": 2}.get(wl.get("act", ""), 0)
     act_rows = T * k if down else T
+    out_cols = N // 2 if fused else N
     torch.cuda.set_device(0)
     dev = torch.device("cuda", 0)
 
@@ -167,7 +180,7 @@ def main() -> None:
     path = ftq.select_path(E, N, K, T, k)
     gates_d = torch.from_numpy(gates).to(dev)
     aq = torch.empty((act_rows, K // 32 * 36), dtype=torch.uint8, device=dev)
-    out = torch.empty((T * k, N), dtype=torch.float32, device=dev)
+    out = torch.empty((T * k, out_cols), dtype=torch.float32, device=dev)
     comb = torch.empty((T, N), dtype=torch.float32, device=dev) if down else None
     need = (ftq.pairs_workspace_bytes if down else ftq.workspace_bytes)(E, N, K, T, k, path)
     ws = torch.empty(max(need, 256), dtype=torch.uint8, device=dev) if need else None
@@ -187,6 +200,8 @@ def main() -> None:
             marks[2].record()
         if down:
             ftq.moe_pairs_routed(wq, aq, ids_d, E, N, K, out, ws, path)
+        elif fused:
+            ftq.moe_act_routed(wq, aq, ids_d, E, N, K, act_kind, out, ws, path)
         else:
             ftq.moe_routed(wq, aq, ids_d, E, N, K, out, ws, path)
         if marks:
@@ -229,7 +244,7 @@ def main() -> None:
     # ---- roofline of the dominant kernel ------------------------------------
     pairs = T * k
     ops = 2.0 * pairs * N * K
-    alg_bytes = _algorithmic_bytes(E, N, K, T, k, ids, act_rows)
+    alg_bytes = _algorithmic_bytes(E, N, K, T, k, ids, act_rows, out_cols)
     kern_s = mm_ms / 1e3
     tops = ops / kern_s / 1e12
     gbs = alg_bytes / kern_s / 1e9
@@ -264,13 +279,18 @@ def main() -> None:
             oa = oracle.quantize_q8_1(x32[:ts * k]).reshape(-1)
             y = oracle.moe(ow, oa, np.ascontiguousarray(ids[:ts]), E, N, K, ts, k, per_pair=True)
             oracle.combine_topk(y, gates[:ts])
+        elif fused:
+            oa = oracle.quantize_q8_1(x32[:ts]).reshape(-1)
+            y = oracle.moe(ow, oa, np.ascontiguousarray(ids[:ts]), E, N, K, ts, k)
+            oracle.act_and_mul(y, act_kind)
         else:
             oa = oracle.quantize_q8_1(x32[:ts]).reshape(-1)
             oracle.moe(ow, oa, np.ascontiguousarray(ids[:ts]), E, N, K, ts, k)
         c1 = time.perf_counter()
         cpu = {"value": round((c1 - c0) * 1e3 * T / ts, 1), "unit": "ms", "cores": oracle.num_threads(),
                "kind": "oracle",
-               "sample": f"Q8_1 quantisation + matmul{' + combine' if down else ''} of the first {ts} of {T} "
+               "sample": f"Q8_1 quantisation + matmul{' + combine' if down else (' + activation' if fused else '')} "
+                         f"of the first {ts} of {T} "
                          f"tokens ({ts * k} of {pairs} pairs), "
                          f"{(c1 - c0):.1f} s measured, scaled by {T}/{ts} to one step"}
 

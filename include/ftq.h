@@ -64,8 +64,13 @@ typedef enum {
 typedef enum {
     FTQ_PATH_AUTO = 0,        /* chosen on the host from the sizes alone     */
     FTQ_PATH_GEMV = 1,        /* memory-bound path for few pairs per expert  */
-    FTQ_PATH_GROUPED = 2      /* expert-sorted int8-MFMA tiles for prefill   */
+    FTQ_PATH_GROUPED = 2      /* expert-sorted MFMA tiles for prefill        */
 } ftq_path;
+
+typedef enum {
+    FTQ_ACT_SILU = 1,         /* x / (1 + exp(-x))                           */
+    FTQ_ACT_GELU_TANH = 2     /* x/2 (1 + tanh(sqrt(2/pi) (x + 0.044715 x^3))) */
+} ftq_act;
 
 #define FTQ_QK 32
 #define FTQ_Q4_0_BLOCK_BYTES 18
@@ -218,6 +223,37 @@ int ftq_moe_combine_topk(const float* y, const float* gates, float* out, int64_t
 
 /* Message for the last failing call on this thread ("" if none).  The pointer
  * stays valid until the next ftq_* call on the same thread. */
+/*
+ * The first layer of an expert FFN with its gated activation fused into the
+ * matmul's epilogue: the GEMV's output feeds gelu_tanh_and_mul in FreeToken
+ * PR #185 (Problem), and the second layer's input is the output "after
+ * SiLU*up" in "Current Bug: CuTeDSLMoERunner" (Bug 6).  Each expert's N weight
+ * rows are [gate rows 0..N/2-1 | up rows N/2..N-1] (the order of the halves is
+ * this library's reading; the pages print no layout).  For pair p and output
+ * column c < N/2:
+ *
+ *   out[p][c] = act(y[p][c]) * y[p][N/2 + c],  y[p][n] the plain matmul value
+ *
+ * computed in fp32 from the matmul's fp32 gate and up values (expf / tanhf),
+ * without writing y.  Arguments are those of ftq_moe_q4_0_q8_1 (per-token
+ * activations, the same workspace: ftq_moe_workspace_bytes(E, N, K, ...)), plus
+ *   N:    weight rows per expert, even (gate and up halves);
+ *   act:  FTQ_ACT_SILU or FTQ_ACT_GELU_TANH;
+ *   out:  fp32 [T*top_k][N/2], row p = t*top_k + j; masked pairs give zero rows.
+ * Errors: N odd or act unknown: FTQ_ERR_INVALID_ARG.  FTQ_ERR_UNSUPPORTED when
+ * one expert's weights reach 4 GiB (grouped path) or when one activation row
+ * does not fit the GEMV path's on-chip staging (K beyond about 45 000).
+ * ftq_moe_q4_0_q8_1_act_routed takes pairs routed by ftq_moe_route, as
+ * ftq_moe_q4_0_q8_1_routed does.
+ */
+int ftq_moe_q4_0_q8_1_act(const void* w, const void* a, const int32_t* topk_ids, float* out,
+                          int64_t E, int64_t N, int64_t K, int64_t T, int64_t top_k, int act,
+                          void* workspace, size_t workspace_bytes, int path, hipStream_t stream);
+
+int ftq_moe_q4_0_q8_1_act_routed(const void* w, const void* a, const int32_t* topk_ids, float* out,
+                                 int64_t E, int64_t N, int64_t K, int64_t T, int64_t top_k, int act,
+                                 void* workspace, size_t workspace_bytes, int path, hipStream_t stream);
+
 const char* ftq_last_error(void);
 
 /* Library version string, e.g. "ftq 0.1.0 gfx950". */

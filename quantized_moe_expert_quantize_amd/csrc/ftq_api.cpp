@@ -150,11 +150,15 @@ int64_t act_rows_of(int64_t T, int64_t top_k, bool act_per_pair) { return act_pe
 
 int moe_common(const void* w, const void* a, const int32_t* ids, float* out, int32_t* partials,
                int64_t E, int64_t N, int64_t K, int64_t T, int64_t top_k, void* ws, size_t ws_bytes,
-               int path, hipStream_t stream, int phases, bool act_per_pair = false)
+               int path, hipStream_t stream, int phases, bool act_per_pair = false, int act = 0)
 {
     clear_error();
     int st = check_sizes(E, N, K, T, top_k);
     if (st != FTQ_OK) return st;
+    if (act != 0) {
+        if (act != FTQ_ACT_SILU && act != FTQ_ACT_GELU_TANH) { set_error("unknown activation %d", act); return FTQ_ERR_INVALID_ARG; }
+        if (N % 2 != 0) { set_error("a gated activation needs an even N (gate and up halves), got %lld", (long long)N); return FTQ_ERR_INVALID_ARG; }
+    }
     const int rp = resolve_path(path, E, T, top_k);
     if (rp < 0) { set_error("unknown path %d", path); return FTQ_ERR_INVALID_ARG; }
     if (T == 0) return FTQ_OK;
@@ -181,7 +185,7 @@ int moe_common(const void* w, const void* a, const int32_t* ids, float* out, int
         }
     }
     if (!(phases & kMatmul)) return FTQ_OK;
-    MoeArgs m{w, a, ids, out, partials, E, N, K, T, top_k, act_per_pair ? 1 : top_k};
+    MoeArgs m{w, a, ids, out, partials, E, N, K, T, top_k, act_per_pair ? 1 : top_k, act};
     if (rp == FTQ_PATH_GEMV) return run_gemv(m, bucketed ? &plan : nullptr, ws, stream);
     return run_grouped(m, plan, ws, stream);
 }
@@ -321,6 +325,22 @@ int ftq_moe_combine_topk(const float* y, const float* gates, float* out, int64_t
         return FTQ_ERR_INVALID_ARG;
     }
     return run_combine_topk(y, gates, out, T, top_k, N, stream);
+}
+
+int ftq_moe_q4_0_q8_1_act(const void* w, const void* a, const int32_t* topk_ids, float* out, int64_t E,
+                          int64_t N, int64_t K, int64_t T, int64_t top_k, int act, void* workspace,
+                          size_t workspace_bytes, int path, hipStream_t stream)
+{
+    return moe_common(w, a, topk_ids, out, nullptr, E, N, K, T, top_k, workspace, workspace_bytes, path, stream,
+                      kRoute | kMatmul, false, act);
+}
+
+int ftq_moe_q4_0_q8_1_act_routed(const void* w, const void* a, const int32_t* topk_ids, float* out, int64_t E,
+                                 int64_t N, int64_t K, int64_t T, int64_t top_k, int act, void* workspace,
+                                 size_t workspace_bytes, int path, hipStream_t stream)
+{
+    return moe_common(w, a, topk_ids, out, nullptr, E, N, K, T, top_k, workspace, workspace_bytes, path, stream,
+                      kMatmul, false, act);
 }
 
 const char* ftq_last_error(void) { return g_error.c_str(); }

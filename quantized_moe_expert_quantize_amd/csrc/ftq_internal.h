@@ -100,7 +100,23 @@ struct MoeArgs {
     int32_t* partials;     // integer partials when non-null
     int64_t E, N, K, T, top_k;
     int64_t act_div;       // activation row of pair p: p / act_div (top_k: per token; 1: per pair)
+    int act;               // 0: plain output [T*k][N]; FTQ_ACT_*: act(gate) * up, [T*k][N/2]
 };
+
+// Gated activation of one fp32 value ("Current Bug: CuTeDSLMoERunner", Bug 6:
+// SiLU; FreeToken PR #185, Problem: the tanh form of GELU), both as x times a
+// logistic, x / (1 + e^-y): y = x for SiLU, and for GELU y = 2 sqrt(2/pi)
+// (x + 0.044715 x^3), since (1 + tanh(z)) / 2 = 1 / (1 + e^-2z).  e^-y is one
+// hardware exp2 of -y log2(e) and the quotient one hardware reciprocal: the
+// relative error stays within a few units of the last place plus |y| units for
+// the exponent's rounding, which the tests bound as 9 u (|act| + |x|).  Large
+// |y| saturate cleanly: e^-y = inf gives x * 0, e^-y = 0 gives x.
+__device__ __forceinline__ float gated_act(int act, float x)
+{
+    const float y = act == FTQ_ACT_SILU ? x : 1.5957691216057308f * (x + 0.044715f * x * x * x);
+    const float e = __builtin_amdgcn_exp2f(-y * 1.4426950408889634f);
+    return x * __builtin_amdgcn_rcpf(1.0f + e);
+}
 
 // GEMV path; `bucketed` selects the pair list from the workspace (else the
 // kernel scans the ids itself).

@@ -66,6 +66,8 @@ struct GemvParams {
     const int32_t* sorted;    // bucketed mode: pair ids grouped by bucket
     int64_t E, N, nb, top_k, pairs, row_tiles;
     int64_t act_div;          // activation row of pair p: p / act_div
+    int64_t half;             // fused activation: N/2 output columns (gate rows [0, half), up rows [half, N))
+    int act;                  // fused activation: FTQ_ACT_*
     int64_t grid;             // workgroups launched
     int64_t seg;              // K blocks staged per pass (a multiple of 8)
     int pc_cap;               // activation rows staged per pass (<= kPairChunk)
@@ -224,7 +226,11 @@ __device__ __forceinline__ void store_step(uint8_t* wrow, int l, const Raw<VEC>&
 // segment case so that the weight loads are the only loads in flight there).
 // NPC > 0: exactly NPC pairs are staged (no per-pair guards); NPC == 0: npc
 // (1..8) pairs, guarded at run time.
-template <int VEC, bool kPartials, bool kMultiSeg, int NPC>
+// kFused: a tile's 16 rows are the gate and up rows of 8 output columns; in
+// wave w, row rw holds column 8t + 2w + (rw & 1), gate for rw < 2 and up for
+// rw >= 2, so that after the row sums lane l holds the gate and lane l ^ 32
+// the up value of the same column.
+template <int VEC, bool kPartials, bool kMultiSeg, int NPC, bool kFused>
 __device__ __forceinline__ void stream_tiles(const GemvParams& p, int64_t e, int64_t t0, int64_t t1, int64_t sb, int len,
                                              int npc, const int32_t* plist, uint8_t* wrow, const uint8_t* codes,
                                              const uint8_t* ds, int l, int rw, int wave)
@@ -237,7 +243,15 @@ __device__ __forceinline__ void stream_tiles(const GemvParams& p, int64_t e, int
     const int64_t gbeg = sb / kGroup, gend = (sb + len + kGroup - 1) / kGroup;
     const int64_t seg_end = (sb + len) * kQ4Bytes;   // row bytes up to the segment's end
     auto step_len = [&](int64_t ws) { return (int)min<int64_t>(kStepBytes, seg_end - ws * kGroup * kQ4Bytes); };
-    auto row_of = [&](int64_t t) { return t * kRowsPerTile + wave * kRowsPerWave + rw; };
+    // output column of this lane's row in tile t (the weight row unless fused)
+    auto col_of = [&](int64_t t) {
+        if constexpr (kFused) return t * (kRowsPerTile / 2) + wave * (kRowsPerWave / 2) + (rw & 1);
+        return t * kRowsPerTile + wave * kRowsPerWave + rw;
+    };
+    auto row_of = [&](int64_t t) {
+        if constexpr (kFused) return (rw >> 1) * p.half + min<int64_t>(col_of(t), p.half - 1);
+        return col_of(t);
+    };
     // rows past N (last tile only) load row N-1; their sums are never written
     auto src_of = [&](int64_t t, int64_t ws) {
         return wexp + min<int64_t>(row_of(t), p.N - 1) * row_bytes + ws * kGroup * kQ4Bytes;
@@ -263,7 +277,7 @@ __device__ __forceinline__ void stream_tiles(const GemvParams& p, int64_t e, int
     int64_t t = t0, ws = gbeg;
     load_step<VEC>(src_of(t, ws), step_len(ws), l, R);
     while (t < t1) {
-        const int64_t n = row_of(t);
+        const int64_t n = kFused ? col_of(t) : row_of(t);
         wave_lds_fence();   // the previous step's reads of the buffer come first
         store_step<VEC>(wrow, l, R);
         wave_lds_fence();   // and this step's writes before its reads
@@ -319,7 +333,20 @@ __device__ __forceinline__ void stream_tiles(const GemvParams& p, int64_t e, int
             }
         }
         if (t2 != t) {   // the tile's rows are complete (wave-uniform)
-            if constexpr (!kPartials) {
+            if constexpr (kFused) {
+#pragma unroll
+                for (int j = 0; j < kJ; ++j) {
+                    float v = acc[j];
+                    v += __shfl_xor(v, 8);
+                    v += __shfl_xor(v, 4);
+                    v += __shfl_xor(v, 2);
+                    v += __shfl_xor(v, 1);
+                    const float up = __shfl_xor(v, 32);
+                    acc[j] = 0.0f;
+                    if (n < p.half && rw < 2 && l == 0 && (NPC > 0 || j < npc))
+                        p.out[(int64_t)plist[j] * p.half + n] = gated_act(p.act, v) * up;
+                }
+            } else if constexpr (!kPartials) {
 #pragma unroll
                 for (int j = 0; j < kJ; ++j) {
                     float v = acc[j];
@@ -344,7 +371,7 @@ __device__ __forceinline__ void stream_tiles(const GemvParams& p, int64_t e, int
     }
 }
 
-template <int VEC, bool kBucketed, bool kPartials, bool kMultiSeg>
+template <int VEC, bool kBucketed, bool kPartials, bool kMultiSeg, bool kFused>
 __global__ __launch_bounds__(kThreads, kWavesPerSimd) void moe_gemv_kernel(GemvParams p)
 {
     extern __shared__ __align__(16) uint8_t lds[];
@@ -451,15 +478,17 @@ __global__ __launch_bounds__(kThreads, kWavesPerSimd) void moe_gemv_kernel(GemvP
             }
             __syncthreads();
 
-            if (e == p.E) {   // masked bucket: zero rows of tiles [t0, t1)
-                const int64_t r0 = t0 * kRowsPerTile, r1 = min<int64_t>(t1 * kRowsPerTile, p.N);
+            if (e == p.E) {   // masked bucket: zero outputs of tiles [t0, t1)
+                constexpr int64_t kCols = kFused ? kRowsPerTile / 2 : kRowsPerTile;
+                const int64_t width = kFused ? p.half : p.N;
+                const int64_t r0 = t0 * kCols, r1 = min<int64_t>(t1 * kCols, width);
                 for (int64_t i = tid; i < (int64_t)npc * (r1 - r0); i += kThreads) {
                     const int j = (int)(i / (r1 - r0));
                     const int64_t n = r0 + (i - (int64_t)j * (r1 - r0));
                     if constexpr (kPartials) {
                         for (int64_t b = 0; b < nb; ++b) p.partials[((int64_t)plist[j] * p.N + n) * nb + b] = 0;
                     } else {
-                        p.out[(int64_t)plist[j] * p.N + n] = 0.0f;
+                        p.out[(int64_t)plist[j] * width + n] = 0.0f;
                     }
                 }
                 continue;
@@ -472,7 +501,7 @@ __global__ __launch_bounds__(kThreads, kWavesPerSimd) void moe_gemv_kernel(GemvP
                 stage_acts(p, ptok, npc, sb, len, codes, ds);
                 __syncthreads();
                 uint8_t* wrow = lds + L.wt + wave * kWaveW + rw * kWRowPitch;
-#define FTQ_STREAM(NPC) stream_tiles<VEC, kPartials, kMultiSeg, NPC>(p, e, t0, t1, sb, len, npc, plist, wrow, codes, ds, l, rw, wave)
+#define FTQ_STREAM(NPC) stream_tiles<VEC, kPartials, kMultiSeg, NPC, kFused>(p, e, t0, t1, sb, len, npc, plist, wrow, codes, ds, l, rw, wave)
                 // one or two pairs per expert (decode) without per-pair guards;
                 // more pairs keep the guarded loop, whose guards also stop the
                 // scheduler from interleaving all 8 blocks (which would need
@@ -493,8 +522,14 @@ __global__ __launch_bounds__(kThreads, kWavesPerSimd) void moe_gemv_kernel(GemvP
 template <int VEC, bool kBucketed, bool kPartials>
 int launch_seg(bool multi, const GemvParams& gp, size_t lds, hipStream_t s)
 {
-    if (multi) return launch("moe_gemv_kernel", moe_gemv_kernel<VEC, kBucketed, kPartials, true>, gp.grid, kThreads, lds, s, gp);
-    return launch("moe_gemv_kernel", moe_gemv_kernel<VEC, kBucketed, kPartials, false>, gp.grid, kThreads, lds, s, gp);
+    if constexpr (!kPartials) {   // a fused activation needs whole rows (one K segment)
+        if (gp.act != 0)
+            return launch("moe_gemv_kernel<act>", moe_gemv_kernel<VEC, kBucketed, false, false, true>, gp.grid, kThreads,
+                          lds, s, gp);
+    }
+    if (multi)
+        return launch("moe_gemv_kernel", moe_gemv_kernel<VEC, kBucketed, kPartials, true, false>, gp.grid, kThreads, lds, s, gp);
+    return launch("moe_gemv_kernel", moe_gemv_kernel<VEC, kBucketed, kPartials, false, false>, gp.grid, kThreads, lds, s, gp);
 }
 
 template <bool kBucketed, bool kPartials>
@@ -524,7 +559,10 @@ int run_gemv(const MoeArgs& m, const BucketPlan* plan, const void* ws, hipStream
     gp.top_k = m.top_k;
     gp.act_div = m.act_div;
     gp.pairs = m.T * m.top_k;
-    gp.row_tiles = (m.N + kRowsPerTile - 1) / kRowsPerTile;
+    gp.act = m.act;
+    gp.half = m.act ? m.N / 2 : 0;
+    // fused: 8 output columns (their 8 gate and 8 up rows) per tile
+    gp.row_tiles = m.act ? (gp.half + kRowsPerTile / 2 - 1) / (kRowsPerTile / 2) : (m.N + kRowsPerTile - 1) / kRowsPerTile;
     if (gp.pairs == 0) return FTQ_OK;
     DeviceLimits lim;
     int st = device_limits(&lim);
@@ -546,6 +584,16 @@ int run_gemv(const MoeArgs& m, const BucketPlan* plan, const void* ws, hipStream
     const int64_t fixed = lds_layout(m.E, 0, 0, gp.list_cap).bytes;
     const int64_t budget = std::max<int64_t>(kLdsPerCU / kTargetWGPerCU - fixed, 0);
     auto act_bytes = [&](int64_t seg) { return code_bytes(seg, gp.pc_cap) + ent_bytes(seg, gp.pc_cap); };
+    if (m.act) {
+        // the activation is applied once a row's sum is complete: stage whole
+        // rows, with fewer pairs per pass if need be
+        while (gp.pc_cap > 1 && act_bytes(gp.nb) > budget) --gp.pc_cap;
+        if (act_bytes(gp.nb) > budget) {
+            set_error("fused activation on the GEMV path: one activation row of K = %lld does not fit on chip",
+                      (long long)m.K);
+            return FTQ_ERR_UNSUPPORTED;
+        }
+    }
     if (act_bytes(gp.nb) <= budget) {
         gp.seg = gp.nb;
     } else {

@@ -35,7 +35,12 @@
 // Tiles are double buffered in LDS (loads for block pair s+1 are in flight while
 // block pair s is multiplied); the global loads are buffer loads whose per-lane
 // offsets are fixed for a tile and whose per-pass advance is a scalar offset.
-// In ragged tiles a wave whose rows hold no pair skips its MFMA work.  Workgroups are mapped to tiles XCD by XCD: each
+// In ragged tiles a wave whose rows hold no pair skips its MFMA work.
+//
+// Fused gated activation (kFused): a tile's 128 weight rows are the gate rows
+// of 64 output columns followed by their up rows; after the K loop the waves
+// holding up values pass them through LDS to the waves holding the gates,
+// which write act(gate) * up.  Workgroups are mapped to tiles XCD by XCD: each
 // of the 8 XCDs takes a contiguous range of tiles, walked in groups of kGroupM
 // M tiles with the N tiles inner, so a gathered activation tile and an expert's
 // weight tiles are reused from that XCD's L2.
@@ -92,7 +97,9 @@ struct GroupedParams {
     int64_t act_div;          // activation row of pair p: p / act_div
     int32_t a16_range;        // buffer ranges in bytes (32-bit unsigned counts): a16, d8
     int32_t d8_range;         // (narrow variant only: a16 below 4 GiB)
-    int32_t wtile_range;      // bytes of kBN weight rows
+    int32_t wtile_range;      // bytes of kBN weight rows (fused: of one expert)
+    int64_t half;             // fused: N/2 output columns
+    int act;                  // fused: FTQ_ACT_*
 };
 
 // Waves per workgroup for BM = 128 tiles.  4 waves of 64x64 (two workgroups
@@ -202,7 +209,7 @@ __device__ __forceinline__ int64_t xcd_remap(int64_t bid, int64_t G)
     return xcd * q + min<int64_t>(xcd, r) + local;
 }
 
-template <int BM, int VEC, bool kWide, bool kPartials>
+template <int BM, int VEC, bool kWide, bool kPartials, bool kFused>
 __global__ __launch_bounds__(Shape<BM>::kThreads, Shape<BM>::kWavesPerSimd) void moe_grouped_kernel(GroupedParams p)
 {
     using S = Shape<BM>;
@@ -244,7 +251,8 @@ __global__ __launch_bounds__(Shape<BM>::kThreads, Shape<BM>::kWavesPerSimd) void
         const int64_t bucket = lo;
         const int64_t slot0 = p.offsets[bucket] + (mt - p.tiles[bucket]) * BM;
         const int rows = (int)min<int64_t>(BM, p.offsets[bucket + 1] - slot0);
-        const int64_t n0 = nt * kBN;
+        // first output column of the tile (fused: kBN/2 columns of gate and up rows)
+        const int64_t n0 = nt * (kFused ? kBN / 2 : kBN);
 
         __syncthreads();   // the previous tile is done with LDS
         for (int m = tid; m < BM; m += kThreads) {
@@ -256,10 +264,12 @@ __global__ __launch_bounds__(Shape<BM>::kThreads, Shape<BM>::kWavesPerSimd) void
         __syncthreads();
 
         if (bucket == p.E) {   // masked pairs: zero rows
-            for (int i = tid; i < rows * kBN; i += kThreads) {
-                const int m = i / kBN, n = i - m * kBN;
-                if (n0 + n >= p.N) continue;
-                const int64_t o = (int64_t)sm.row_pair[m] * p.N + n0 + n;
+            constexpr int kCols = kFused ? kBN / 2 : kBN;
+            const int64_t width = kFused ? p.half : p.N;
+            for (int i = tid; i < rows * kCols; i += kThreads) {
+                const int m = i / kCols, n = i - m * kCols;
+                if (n0 + n >= width) continue;
+                const int64_t o = (int64_t)sm.row_pair[m] * width + n0 + n;
                 if constexpr (kPartials) {
                     for (int64_t b = 0; b < nb; ++b) p.partials[o * nb + b] = 0;
                 } else {
@@ -301,9 +311,17 @@ __global__ __launch_bounds__(Shape<BM>::kThreads, Shape<BM>::kWavesPerSimd) void
         static_assert(kBN * kKB <= kThreads, "one weight block per thread");
         const bool b_thread = tid < kBN * kKB;
         const int bn = tid % kBN, bh = uniform((int32_t)((tid / kBN) % kKB));
-        const uint8_t* wtile = p.w + (uniform(bucket) * p.N + uniform(n0)) * nb * kQ4Bytes;   // uniform per tile
+        // uniform per tile: the tile's first weight row, or (fused) the expert's
+        const uint8_t* wtile = p.w + (uniform(bucket) * p.N + (kFused ? 0 : uniform(n0))) * nb * kQ4Bytes;
         const __amdgpu_buffer_rsrc_t wrs = make_rsrc(wtile, p.wtile_range);
-        const uint32_t bg_off = (uint32_t)((n0 + bn < p.N ? bn : 0) * nb * kQ4Bytes);
+        uint32_t bg_off;
+        if constexpr (kFused) {
+            // tile row bn: gate row of column n0 + bn (bn < 64) or up row of column n0 + bn - 64
+            const int64_t c = n0 + bn % (kBN / 2);
+            bg_off = (uint32_t)((c < p.half ? (bn >= kBN / 2 ? p.half : 0) + c : 0) * nb * kQ4Bytes);
+        } else {
+            bg_off = (uint32_t)((n0 + bn < p.N ? bn : 0) * nb * kQ4Bytes);
+        }
         int b_lds[4];
 #pragma unroll
         for (int i = 0; i < 4; ++i) b_lds[i] = lds_chunk(bn, bh * 4 + i);
@@ -465,7 +483,46 @@ __global__ __launch_bounds__(Shape<BM>::kThreads, Shape<BM>::kWavesPerSimd) void
             __syncthreads();
         }
 
-        if constexpr (!kPartials) {
+        if constexpr (kFused) {
+            // tile rows (sub-tile column groups) below kBN/2 are gates, the rest
+            // the up rows of the same columns: exchange through LDS, which the
+            // K loop no longer uses (its last barrier has passed)
+            constexpr int kXPitch = kBN / 2 + 4;   // floats per exchanged row
+            static_assert(BM * kXPitch * 4 <= (int)(sizeof(sm.a) + sizeof(sm.b)), "exchange fits the stage buffers");
+            float* xch = reinterpret_cast<float*>(&sm.a[0][0]);
+            int l32e = l32, halfe = half;
+            __asm__ volatile("" : "+v"(l32e), "+v"(halfe));
+#pragma unroll
+            for (int i = 0; i < S::SM; ++i)
+#pragma unroll
+                for (int j = 0; j < S::SN; ++j) {
+                    const int R = (wn * S::SN + j) * 32;   // first tile row of the sub-tile (uniform)
+                    if (R >= kBN / 2) {
+#pragma unroll
+                        for (int r = 0; r < 16; ++r) {
+                            const int m = (wm * S::SM + i) * 32 + 8 * (r / 4) + 4 * halfe + (r % 4);
+                            xch[m * kXPitch + R - kBN / 2 + l32e] = acc[i][j][r];
+                        }
+                    }
+                }
+            __syncthreads();
+#pragma unroll
+            for (int i = 0; i < S::SM; ++i)
+#pragma unroll
+                for (int j = 0; j < S::SN; ++j) {
+                    const int R = (wn * S::SN + j) * 32;
+                    if (R < kBN / 2) {
+                        const int64_t c = n0 + R + l32e;
+#pragma unroll
+                        for (int r = 0; r < 16; ++r) {
+                            const int m = (wm * S::SM + i) * 32 + 8 * (r / 4) + 4 * halfe + (r % 4);
+                            if (m < rows && c < p.half)
+                                __builtin_nontemporal_store(gated_act(p.act, acc[i][j][r]) * xch[m * kXPitch + R + l32e],
+                                                            &p.out[(int64_t)sm.row_pair[m] * p.half + c]);
+                        }
+                    }
+                }
+        } else if constexpr (!kPartials) {
             // row and column of this lane's outputs, made opaque here so that
             // the compiler does not compute them before the K loop and keep them
             // live through it
@@ -488,16 +545,24 @@ __global__ __launch_bounds__(Shape<BM>::kThreads, Shape<BM>::kWavesPerSimd) void
     }
 }
 
-template <int BM, bool kPartials>
-int launch_grouped(int vec, bool wide, const GroupedParams& gp, int64_t grid, hipStream_t s)
+template <int BM, bool kPartials, bool kFused>
+int launch_grouped_v(int vec, bool wide, const GroupedParams& gp, int64_t grid, hipStream_t s)
 {
     constexpr int kT = Shape<BM>::kThreads;
     if (vec == 4) {
-        return wide ? launch("moe_grouped_kernel<4,wide>", moe_grouped_kernel<BM, 4, true, kPartials>, grid, kT, 0, s, gp)
-                    : launch("moe_grouped_kernel<4>", moe_grouped_kernel<BM, 4, false, kPartials>, grid, kT, 0, s, gp);
+        return wide ? launch("moe_grouped_kernel<4,wide>", moe_grouped_kernel<BM, 4, true, kPartials, kFused>, grid, kT, 0, s, gp)
+                    : launch("moe_grouped_kernel<4>", moe_grouped_kernel<BM, 4, false, kPartials, kFused>, grid, kT, 0, s, gp);
     }
-    return wide ? launch("moe_grouped_kernel<2,wide>", moe_grouped_kernel<BM, 2, true, kPartials>, grid, kT, 0, s, gp)
-                : launch("moe_grouped_kernel<2>", moe_grouped_kernel<BM, 2, false, kPartials>, grid, kT, 0, s, gp);
+    return wide ? launch("moe_grouped_kernel<2,wide>", moe_grouped_kernel<BM, 2, true, kPartials, kFused>, grid, kT, 0, s, gp)
+                : launch("moe_grouped_kernel<2>", moe_grouped_kernel<BM, 2, false, kPartials, kFused>, grid, kT, 0, s, gp);
+}
+
+template <int BM>
+int launch_grouped(bool part, bool fused, int vec, bool wide, const GroupedParams& gp, int64_t grid, hipStream_t s)
+{
+    if (part) return launch_grouped_v<BM, true, false>(vec, wide, gp, grid, s);
+    if (fused) return launch_grouped_v<BM, false, true>(vec, wide, gp, grid, s);
+    return launch_grouped_v<BM, false, false>(vec, wide, gp, grid, s);
 }
 
 }  // namespace
@@ -564,9 +629,21 @@ int run_grouped(const MoeArgs& m, const BucketPlan& plan, void* ws, hipStream_t 
     auto range32 = [](int64_t bytes) { return (int32_t)(uint32_t)std::min<int64_t>(bytes, UINT32_MAX); };
     gp.a16_range = range32(act_rows * nbp * kBlockF16);
     gp.d8_range = range32(act_rows * nbp * 2);
-    gp.wtile_range = range32((int64_t)kBN * nb * kQ4Bytes);
+    gp.act = m.act;
+    gp.half = m.act ? m.N / 2 : 0;
+    if (m.act) {
+        // fused tiles address the gate and up rows from the expert's base
+        if (m.N * nb * kQ4Bytes > (int64_t)UINT32_MAX) {
+            set_error("fused activation on the grouped path: one expert's weights reach 4 GiB");
+            return FTQ_ERR_UNSUPPORTED;
+        }
+        gp.wtile_range = range32(m.N * nb * kQ4Bytes);
+        gp.n_tiles_n = (gp.half + kBN / 2 - 1) / (kBN / 2);
+    } else {
+        gp.wtile_range = range32((int64_t)kBN * nb * kQ4Bytes);
+        gp.n_tiles_n = (m.N + kBN - 1) / kBN;
+    }
     gp.nbuckets = plan.buckets;
-    gp.n_tiles_n = (m.N + kBN - 1) / kBN;
     const int64_t bm = plan.tile_m;
     // sum over buckets of ceil(count/BM) <= (pairs + buckets*(BM-1)) / BM
     gp.max_mt = (plan.pairs + plan.buckets * (bm - 1)) / bm;
@@ -578,10 +655,11 @@ int run_grouped(const MoeArgs& m, const BucketPlan& plan, void* ws, hipStream_t 
     // FTQ_FORCE_WIDE=1 selects the 64-bit variant at any size (tests)
     static const bool force_wide = [] { const char* v = getenv("FTQ_FORCE_WIDE"); return v && v[0] == '1'; }();
     const bool wide = force_wide || act_rows * nbp * kBlockF16 >= ((int64_t)1 << 32);
+    const bool fused = m.act != 0;
     switch (bm) {
-    case 128: return part ? launch_grouped<128, true>(vec, wide, gp, grid, s) : launch_grouped<128, false>(vec, wide, gp, grid, s);
-    case 64: return part ? launch_grouped<64, true>(vec, wide, gp, grid, s) : launch_grouped<64, false>(vec, wide, gp, grid, s);
-    default: return part ? launch_grouped<32, true>(vec, wide, gp, grid, s) : launch_grouped<32, false>(vec, wide, gp, grid, s);
+    case 128: return launch_grouped<128>(part, fused, vec, wide, gp, grid, s);
+    case 64: return launch_grouped<64>(part, fused, vec, wide, gp, grid, s);
+    default: return launch_grouped<32>(part, fused, vec, wide, gp, grid, s);
     }
 }
 

@@ -17,6 +17,7 @@ LIB_PATH = os.path.join(_PKG, "libftq.so")
 
 OK, ERR_INVALID_ARG, ERR_WORKSPACE, ERR_LAUNCH, ERR_UNSUPPORTED, ERR_HIP = range(6)
 PATH_AUTO, PATH_GEMV, PATH_GROUPED = 0, 1, 2
+ACT_SILU, ACT_GELU_TANH = 1, 2
 QK, Q4_0_BYTES, Q8_1_BYTES = 32, 18, 36
 
 EXPORTS = (
@@ -24,6 +25,7 @@ EXPORTS = (
     "ftq_moe_q4_0_q8_1", "ftq_moe_route", "ftq_moe_q4_0_q8_1_routed", "ftq_moe_q4_0_q8_1_partials",
     "ftq_moe_pairs_workspace_bytes", "ftq_moe_q4_0_q8_1_pairs", "ftq_moe_q4_0_q8_1_pairs_routed",
     "ftq_moe_q4_0_q8_1_pairs_partials", "ftq_moe_combine_topk",
+    "ftq_moe_q4_0_q8_1_act", "ftq_moe_q4_0_q8_1_act_routed",
     "ftq_last_error", "ftq_version",
     "ftq_debug_force_block_threads",
 )
@@ -69,6 +71,10 @@ def lib() -> ctypes.CDLL:
         getattr(L, name).restype = I32
     L.ftq_moe_combine_topk.argtypes = [P, P, P, I64, I64, I64, P]
     L.ftq_moe_combine_topk.restype = I32
+    for name in ("ftq_moe_q4_0_q8_1_act", "ftq_moe_q4_0_q8_1_act_routed"):
+        f = getattr(L, name)
+        f.argtypes = [P, P, P, P, I64, I64, I64, I64, I64, I32, P, ctypes.c_size_t, I32, P]
+        f.restype = I32
     L.ftq_moe_q4_0_q8_1_partials.restype = I32
     L.ftq_last_error.restype = ctypes.c_char_p
     L.ftq_version.restype = ctypes.c_char_p
@@ -262,6 +268,37 @@ def moe_pairs_partials(w: torch.Tensor, a_pairs: torch.Tensor, topk_ids: torch.T
         _dev(w, "w", torch.uint8), _dev(a_pairs, "a_pairs", torch.uint8), _dev(topk_ids, "topk_ids", torch.int32),
         _dev(out, "partials", torch.int32), E, N, K, T, top_k,
         ws.data_ptr() if ws is not None else None, ws_n, path, _stream(stream)))
+    return out
+
+
+# ---- first layer with the gated activation fused (gate rows, then up rows) ----
+
+def moe_act(w: torch.Tensor, a: torch.Tensor, topk_ids: torch.Tensor, E: int, N: int, K: int, act: int,
+            path: int = PATH_AUTO, out: torch.Tensor | None = None, workspace: torch.Tensor | None = None,
+            stream=None) -> torch.Tensor:
+    """act(gate) * up: fp32 out [T*top_k, N/2] from N = 2*(N/2) weight rows per expert."""
+    T, top_k = _moe_args(w, a, topk_ids, E, N, K)
+    if out is None:
+        out = torch.empty((T * top_k, N // 2), dtype=torch.float32, device=a.device)
+    need = workspace_bytes(E, N, K, T, top_k, path)
+    ws, ws_n = _workspace(workspace, need, a.device)
+    _check(lib().ftq_moe_q4_0_q8_1_act(
+        _dev(w, "w", torch.uint8), _dev(a, "a", torch.uint8), _dev(topk_ids, "topk_ids", torch.int32),
+        _dev(out, "out", torch.float32), E, N, K, T, top_k, act,
+        ws.data_ptr() if ws is not None else None, ws_n, path, _stream(stream)))
+    return out
+
+
+def moe_act_routed(w: torch.Tensor, a: torch.Tensor, topk_ids: torch.Tensor, E: int, N: int, K: int, act: int,
+                   out: torch.Tensor, workspace: torch.Tensor | None, path: int = PATH_AUTO,
+                   stream=None) -> torch.Tensor:
+    """moe_act on pairs already routed into `workspace` by moe_route."""
+    T, top_k = _moe_args(w, a, topk_ids, E, N, K)
+    ws_n = workspace.numel() if workspace is not None else 0
+    _check(lib().ftq_moe_q4_0_q8_1_act_routed(
+        _dev(w, "w", torch.uint8), _dev(a, "a", torch.uint8), _dev(topk_ids, "topk_ids", torch.int32),
+        _dev(out, "out", torch.float32), E, N, K, T, top_k, act,
+        workspace.data_ptr() if workspace is not None else None, ws_n, path, _stream(stream)))
     return out
 
 

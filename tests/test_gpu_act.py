@@ -1,0 +1,166 @@
+"""First layer with the gated activation fused into the matmul epilogue, on the
+GPU through the C ABI: out[p][c] = act(y[p][c]) * y[p][N/2 + c] for the gate
+rows [0, N/2) and up rows [N/2, N) of each expert (FreeToken PR #185, Problem:
+gelu_tanh_and_mul follows the GEMV; "Current Bug: CuTeDSLMoERunner", Bug 6:
+SiLU*up).
+
+Bound per element (u = 2^-24): the fp32 matmul bounds eg, eu of the gate and up
+values (as for the plain matmul), the activation's slope (|act'| <= 1.13 for
+both), and the fp32 evaluation of act and the product, at most 9u (|act| + |g|)
+|u| (the |g| term covers the cancellation in 1 + tanh for large negative g)."""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from quantized_moe_expert_quantize_amd import ftq, inputs
+from tests._cases import U32, U64, Case, gamma, sample_pairs, say
+
+pytestmark = pytest.mark.gpu
+
+PATHS = [ftq.PATH_GEMV, ftq.PATH_GROUPED, ftq.PATH_AUTO]
+PATH_NAMES = {ftq.PATH_GEMV: "gemv", ftq.PATH_GROUPED: "grouped", ftq.PATH_AUTO: "auto"}
+ACTS = {ftq.ACT_SILU: "silu", ftq.ACT_GELU_TANH: "gelu_tanh"}
+SLOPE = 1.13
+
+
+def act64(kind, x):
+    """The oracle's act in fp64, elementwise (act(x) * 1 through act_and_mul)."""
+    x = np.asarray(x, dtype=np.float64)
+    flat = x.reshape(1, -1) if x.ndim < 2 else x.reshape(x.shape[0], -1)
+    return oracle.act_and_mul(np.concatenate([flat, np.ones_like(flat)], axis=1), kind).reshape(x.shape)
+
+
+def assert_act_matches(got, y, ab, nb, kind):
+    """got [P, I] fp32 against the oracle's fp64 y [P, 2I] (with |term| sums ab)."""
+    I = y.shape[1] // 2
+    g, u = y[:, :I], y[:, I:]
+    e = (gamma(nb + 2, U32) + gamma(nb, U64)) * ab
+    eg, eu = e[:, :I], e[:, I:]
+    ag = act64(kind, g)
+    ref = ag * u
+    bound = (SLOPE * eg * (np.abs(u) + eu) + np.abs(ag) * eu
+             + 9 * U32 * (np.abs(ag) + SLOPE * eg + np.abs(g) + eg) * (np.abs(u) + eu) + 1e-30)
+    got = got.astype(np.float64)
+    assert got.shape == ref.shape and np.all(np.isfinite(got))
+    diff = np.abs(got - ref)
+    worst = np.unravel_index(np.argmax(diff - bound), diff.shape)
+    assert np.all(diff <= bound), f"element {worst}: |diff| {diff[worst]:.3e} > bound {bound[worst]:.3e}"
+    if np.linalg.norm(ref) > 0:
+        assert np.linalg.norm(got - ref) <= 1e-5 * np.linalg.norm(ref)
+
+
+def run_act(c, kind, path):
+    wq, aq, ids = c.gpu()
+    out = ftq.moe_act(wq, aq, ids, c.E, c.N, c.K, kind, path=path)
+    torch.cuda.synchronize()
+    return out
+
+
+# (E, N = 2I, K, T, top_k, routing)
+SHAPES = {
+    "tiny": (8, 256, 256, 16, 2, "uniform"),
+    "ragged": (4, 154, 96, 9, 3, "uniform"),        # I = 77: not a tile multiple; K/32 odd
+    "one_block": (3, 80, 32, 5, 1, "uniform"),
+    "page1_rows": (16, 400, 2816, 33, 4, "uniform"),
+    "zipf": (32, 320, 512, 300, 8, "zipf"),
+    "many_pairs": (4, 272, 384, 200, 2, "uniform"),
+}
+
+
+@pytest.fixture(scope="module", params=list(SHAPES))
+def case(request):
+    E, N, K, T, k, kind = SHAPES[request.param]
+    say(f"[act case] {request.param}: E={E} N={N} K={K} T={T} top_k={k} routing={kind}")
+    c = Case(E, N, K, T, k, seed=31, kind=kind)
+    c.ref = c.oracle_out()
+    return c
+
+
+@pytest.mark.parametrize("kind", list(ACTS), ids=lambda a: ACTS[a])
+@pytest.mark.parametrize("path", PATHS, ids=lambda p: PATH_NAMES[p])
+def test_fused_matches_oracle(case, path, kind):
+    got = run_act(case, kind, path).cpu().numpy()
+    y, ab = case.ref
+    assert_act_matches(got, y, ab, case.nb, kind)
+
+
+@pytest.mark.parametrize("kind", list(ACTS), ids=lambda a: ACTS[a])
+@pytest.mark.parametrize("path", [ftq.PATH_GEMV, ftq.PATH_GROUPED], ids=lambda p: PATH_NAMES[p])
+def test_epilogue_pairs_gate_and_up_of_one_column(case, path, kind):
+    """The fused output against act(gate) * up of the same path's plain fp32 output:
+    only the epilogue's rounding separates them (a wrong column pairing does not)."""
+    y = case.run(path).cpu().numpy().astype(np.float64)
+    got = run_act(case, kind, path).cpu().numpy().astype(np.float64)
+    I = case.N // 2
+    g, u = y[:, :I], y[:, I:]
+    ag = act64(kind, g)
+    bound = 9 * U32 * (np.abs(ag) + np.abs(g)) * np.abs(u) + 1e-30
+    assert np.all(np.abs(got - ag * u) <= bound)
+
+
+def test_fused_masked_ids_and_zero_tokens():
+    E, N, K, T, k = 6, 192, 192, 40, 3
+    ids = inputs.routing(T, E, k, seed=3)
+    ids[0, 0] = -1
+    ids[5, 2] = E
+    c = Case(E, N, K, T, k, seed=3, ids=ids)
+    y, ab = c.oracle_out()
+    for path in [ftq.PATH_GEMV, ftq.PATH_GROUPED]:
+        for kind in ACTS:
+            got = run_act(c, kind, path).cpu().numpy()
+            assert_act_matches(got, y, ab, c.nb, kind)
+            assert not got[0].any() and not got[5 * k + 2].any()
+    wq = ftq.quantize_q4_0(torch.from_numpy(inputs.weights(4, 64, 64)).cuda())
+    a = torch.empty((0, 2 * 36), dtype=torch.uint8, device="cuda")
+    ids0 = torch.empty((0, 2), dtype=torch.int32, device="cuda")
+    out = ftq.moe_act(wq, a, ids0, 4, 64, 64, ftq.ACT_SILU)
+    assert out.shape == (0, 32)
+
+
+@pytest.mark.parametrize("path", [ftq.PATH_GEMV, ftq.PATH_GROUPED], ids=lambda p: PATH_NAMES[p])
+def test_route_then_act_routed_equals_one_call(path):
+    E, N, K, T, k = 16, 256, 512, 150, 4
+    c = Case(E, N, K, T, k, seed=8, kind="zipf")
+    wq, aq, ids = c.gpu()
+    one = ftq.moe_act(wq, aq, ids, E, N, K, ftq.ACT_GELU_TANH, path=path)
+    need = ftq.workspace_bytes(E, N, K, T, k, path)
+    ws = torch.empty(need, dtype=torch.uint8, device="cuda") if need else None
+    ftq.moe_route(ids, E, ws, path)
+    out = torch.empty_like(one)
+    ftq.moe_act_routed(wq, aq, ids, E, N, K, ftq.ACT_GELU_TANH, out, ws, path)
+    torch.cuda.synchronize()
+    assert torch.equal(out, one)
+
+
+def test_fused_errors_are_reported():
+    c = Case(4, 64, 64, 8, 2, seed=1)
+    wq, aq, ids = c.gpu()
+    with pytest.raises(ftq.FtqError):
+        ftq.moe_act(wq, aq, ids, 4, 64, 64, 7)
+    w_odd = ftq.quantize_q4_0(torch.from_numpy(inputs.weights(4, 63, 64)).cuda())
+    with pytest.raises(ftq.FtqError):
+        ftq.moe_act(w_odd, aq, ids, 4, 63, 64, ftq.ACT_SILU)
+
+
+FULL = [
+    # name, E, N (gate + up rows), K, top_k, T, routing, sampled pairs
+    ("mixtral_gate_up_T8", 8, 28672, 4096, 2, 8, "uniform", 6),
+    ("page1_T8191", 128, 1408, 2816, 8, 8191, "uniform", 32),
+    ("qwen3_gate_up_T8192_zipf", 128, 1536, 2048, 8, 8192, "zipf", 32),
+]
+
+
+@pytest.mark.parametrize("wl", FULL, ids=[w[0] for w in FULL])
+def test_full_size_sampled(wl):
+    name, E, N, K, k, T, routing, ns = wl
+    say(f"[act full] {name}: E={E} N={N} K={K} top_k={k} T={T} path={ftq.select_path(E, N, K, T, k)}")
+    c = Case(E, N, K, T, k, seed=0, kind=routing)
+    wq, aq, ids = c.gpu()
+    pairs = sample_pairs(T, k, ns, seed=5)
+    y, ab = c.oracle_out(pairs)
+    for kind in ACTS:
+        out = ftq.moe_act(wq, aq, ids, E, N, K, kind)
+        got = out[torch.from_numpy(pairs).cuda()].cpu().numpy()
+        del out
+        assert_act_matches(got, y, ab, c.nb, kind)
