@@ -66,6 +66,12 @@ def _load():
     lib.oracle_moe_pairs_ex.argtypes = [P, P, P, I64, I64, I64, I64, I64, I64, P, I64, P, P]
     lib.oracle_moe_partials_ex.argtypes = [P, P, P, I64, I64, I64, I64, I64, I64, P]
     lib.oracle_combine_topk.argtypes = [P, P, I64, I64, I64, P, P]
+    I32 = ctypes.c_int
+    lib.oracle_w_block_bytes.argtypes = [I32]
+    lib.oracle_w_block_bytes.restype = I32
+    lib.oracle_quantize_w.argtypes = [I32, P, I64, I64, P]
+    lib.oracle_moe_w_pairs.argtypes = [I32, P, P, P, I64, I64, I64, I64, P, I64, P, P]
+    lib.oracle_moe_w_partials.argtypes = [I32, P, P, P, I64, I64, I64, I64, I64, I64, P]
     lib.oracle_act.argtypes = [ctypes.c_int, ctypes.c_double]
     lib.oracle_act.restype = ctypes.c_double
     lib.oracle_act_and_mul.argtypes = [P, I64, I64, ctypes.c_int, P]
@@ -160,6 +166,55 @@ def moe_partials(w, a, ids, E, N, K, T, top_k, per_pair=False):
 
 
 ACT_SILU, ACT_GELU_TANH = 1, 2
+
+# GGUF block types (type ids as in GGUF files): Q4_0, Q4_1, Q5_0, Q5_1, Q8_0
+W_Q4_0, W_Q4_1, W_Q5_0, W_Q5_1, W_Q8_0 = 2, 3, 6, 7, 8
+W_TYPES = (W_Q4_0, W_Q4_1, W_Q5_0, W_Q5_1, W_Q8_0)
+
+
+def w_block_bytes(wtype: int) -> int:
+    return int(_load().oracle_w_block_bytes(int(wtype)))
+
+
+def quantize_w(wtype: int, w: np.ndarray) -> np.ndarray:
+    """fp32 [..., K] -> uint8 [..., K/32 * block bytes] blocks of `wtype`."""
+    w = np.ascontiguousarray(w, dtype=np.float32)
+    K = w.shape[-1]
+    assert K % QK == 0
+    bb = w_block_bytes(wtype)
+    rows = w.size // K
+    y = np.empty(w.shape[:-1] + (K // QK * bb,), np.uint8)
+    _load().oracle_quantize_w(int(wtype), _ptr(w), rows, K, _ptr(y))
+    return y
+
+
+def _check_w(wtype, w, a, ids, E, N, K, T, top_k, per_pair):
+    nb = K // QK
+    rows = T * top_k if per_pair else T
+    assert w.dtype == np.uint8 and w.size == E * N * nb * w_block_bytes(wtype) and w.flags.c_contiguous
+    assert a.dtype == np.uint8 and a.size == rows * nb * Q8_1_BYTES and a.flags.c_contiguous
+    assert ids.dtype == np.int32 and ids.size == T * top_k and ids.flags.c_contiguous
+    return 1 if per_pair else top_k
+
+
+def moe_w(wtype, w, a, ids, E, N, K, T, top_k, pairs=None, want_abssum=False, per_pair=False):
+    """fp64 outputs for weights of `wtype`: [T*top_k, N], or the listed pairs' rows.
+    abssum holds, per element, the sum over blocks of |d d8 P| + |m d8 S|."""
+    div = _check_w(wtype, w, a, ids, E, N, K, T, top_k, per_pair)
+    pairs = np.arange(T * top_k, dtype=np.int64) if pairs is None else np.ascontiguousarray(pairs, dtype=np.int64)
+    out = np.empty((pairs.size, N), np.float64)
+    ab = np.empty_like(out) if want_abssum else None
+    _load().oracle_moe_w_pairs(int(wtype), _ptr(w), _ptr(a), _ptr(ids), E, N, K, div, _ptr(pairs), pairs.size,
+                               _ptr(out), _ptr(ab) if ab is not None else None)
+    return (out, ab) if want_abssum else out
+
+
+def moe_w_partials(wtype, w, a, ids, E, N, K, T, top_k, per_pair=False):
+    """Exact integer parts sum((q - z) * q8) [T*top_k, N, K/32] for weights of `wtype`."""
+    div = _check_w(wtype, w, a, ids, E, N, K, T, top_k, per_pair)
+    out = np.empty((T * top_k, N, K // QK), np.int32)
+    _load().oracle_moe_w_partials(int(wtype), _ptr(w), _ptr(a), _ptr(ids), E, N, K, T, top_k, div, _ptr(out))
+    return out
 
 
 def act(kind: int, x: float) -> float:

@@ -347,6 +347,211 @@ void oracle_combine_topk(const double* y, const float* gates, int64_t T, int64_t
     }
 }
 
+/* ------------------------------------------------------------------------ */
+/* Sibling GGUF weight formats against Q8_1 activations.                    */
+/* ------------------------------------------------------------------------ */
+/* FreeToken PR #185 (Problem) counts launchers for the other GGUF block
+ * types sharing the GEMV's geometry; the pages print none of their layouts.
+ * Reading: the GGUF layouts, type ids as in GGUF files:
+ *   Q4_1 (3, 20 B): fp16 d, fp16 m, 16 nibble bytes    w = q d + m,    q in 0..15
+ *   Q5_0 (6, 22 B): fp16 d, 32-bit qh, 16 nibble bytes w = (q - 16) d, q in 0..31
+ *   Q5_1 (7, 24 B): fp16 d, fp16 m, qh, 16 nibble bytes w = q d + m,   q in 0..31
+ *   Q8_0 (8, 34 B): fp16 d, 32 int8                      w = q d
+ * (Q4_0 is type 2.)  Nibble byte i holds element i (low) and i + 16 (high);
+ * bit i of qh (little-endian) is bit 4 of element i.  The matmul is the dot
+ * product of the dequantised weights and the dequantised Q8_1 activations;
+ * per block that is d d8 sum((q - z) q8) + m d8 sum(q8), z the format's zero
+ * point (8, 16 or 0), exact in fp64.  The Q8_1 s field is not used. */
+
+int oracle_w_block_bytes(int type)
+{
+    switch (type) {
+    case 2: return 18;
+    case 3: return 20;
+    case 6: return 22;
+    case 7: return 24;
+    case 8: return 34;
+    default: return 0;
+    }
+}
+
+/* codes q[32], zero point, scale, offset of one block */
+static void w_decode(int type, const uint8_t* blk, int q[32], int* zero, double* d, double* m)
+{
+    *d = (double)oracle_fp16_to_fp32(get_u16(blk));
+    *m = 0.0;
+    *zero = 0;
+    const uint8_t* nib = NULL;
+    uint32_t qh = 0;
+    switch (type) {
+    case 2: nib = blk + 2; *zero = 8; break;
+    case 3: *m = (double)oracle_fp16_to_fp32(get_u16(blk + 2)); nib = blk + 4; break;
+    case 6:
+        qh = (uint32_t)blk[2] | ((uint32_t)blk[3] << 8) | ((uint32_t)blk[4] << 16) | ((uint32_t)blk[5] << 24);
+        nib = blk + 6; *zero = 16; break;
+    case 7:
+        *m = (double)oracle_fp16_to_fp32(get_u16(blk + 2));
+        qh = (uint32_t)blk[4] | ((uint32_t)blk[5] << 8) | ((uint32_t)blk[6] << 16) | ((uint32_t)blk[7] << 24);
+        nib = blk + 8; break;
+    case 8:
+        for (int i = 0; i < QK; ++i) q[i] = (int)(int8_t)blk[2 + i];
+        return;
+    default: return;
+    }
+    for (int i = 0; i < QK; ++i) {
+        int v = (i < 16) ? (nib[i] & 0x0f) : (nib[i - 16] >> 4);
+        if (type == 6 || type == 7) v |= (int)((qh >> i) & 1u) << 4;
+        q[i] = v;
+    }
+}
+
+static void w_encode(int type, const int q[32], float d, float m, uint8_t* blk)
+{
+    put_u16(blk, oracle_fp32_to_fp16(d));
+    if (type == 8) {
+        for (int i = 0; i < QK; ++i) blk[2 + i] = (uint8_t)(int8_t)q[i];
+        return;
+    }
+    uint8_t* nib = blk + 2;
+    uint32_t qh = 0;
+    for (int i = 0; i < QK; ++i) qh |= (uint32_t)((q[i] >> 4) & 1) << i;
+    if (type == 3 || type == 7) { put_u16(blk + 2, oracle_fp32_to_fp16(m)); nib = blk + 4; }
+    if (type == 6 || type == 7) {
+        uint8_t* h = (type == 6) ? blk + 2 : blk + 4;
+        for (int k = 0; k < 4; ++k) h[k] = (uint8_t)(qh >> (8 * k));
+        nib = h + 4;
+    }
+    for (int i = 0; i < QK / 2; ++i) nib[i] = (uint8_t)((q[i] & 0x0f) | ((q[i + 16] & 0x0f) << 4));
+}
+
+/* Quantise fp32 rows [rows][K] into blocks of `type` (test input generation):
+ * symmetric formats scale by the element of largest magnitude (Q5_0: d =
+ * that element / -16, Q8_0: d = max|x| / 127), offset formats by the range
+ * (d = (max - min) / levels, m = min); codes round to nearest and clamp. */
+void oracle_quantize_w(int type, const float* w, int64_t rows, int64_t K, uint8_t* y)
+{
+    const int64_t nb = K / QK;
+    const int bytes = oracle_w_block_bytes(type);
+    int64_t r;
+#pragma omp parallel for schedule(static)
+    for (r = 0; r < rows; ++r) {
+        for (int64_t b = 0; b < nb; ++b) {
+            const float* xb = w + r * K + b * QK;
+            uint8_t* yb = y + (r * nb + b) * bytes;
+            float mn = xb[0], mx = xb[0], amax = 0.0f, sgn = 0.0f;
+            for (int i = 0; i < QK; ++i) {
+                if (xb[i] < mn) mn = xb[i];
+                if (xb[i] > mx) mx = xb[i];
+                if (fabsf(xb[i]) > amax) { amax = fabsf(xb[i]); sgn = xb[i]; }
+            }
+            int q[QK];
+            float d = 0.0f, m = 0.0f;
+            if (type == 2 || type == 6) {
+                const int half = (type == 2) ? 8 : 16;
+                d = sgn / (float)-half;
+                for (int i = 0; i < QK; ++i) {
+                    int v = d == 0.0f ? half : (int)roundf(xb[i] / d) + half;
+                    q[i] = v < 0 ? 0 : (v > 2 * half - 1 ? 2 * half - 1 : v);
+                }
+            } else if (type == 8) {
+                d = amax / 127.0f;
+                for (int i = 0; i < QK; ++i) q[i] = d == 0.0f ? 0 : (int)roundf(xb[i] / d);
+            } else {
+                const int levels = (type == 3) ? 15 : 31;
+                d = (mx - mn) / (float)levels;
+                m = mn;
+                for (int i = 0; i < QK; ++i) {
+                    int v = d == 0.0f ? 0 : (int)roundf((xb[i] - mn) / d);
+                    q[i] = v < 0 ? 0 : (v > levels ? levels : v);
+                }
+            }
+            if (type == 2) {   /* the Q4_0 layout */
+                put_u16(yb, oracle_fp32_to_fp16(d));
+                for (int i = 0; i < QK / 2; ++i) yb[2 + i] = (uint8_t)(q[i] | (q[i + QK / 2] << 4));
+            } else {
+                w_encode(type, q, d, m, yb);
+            }
+        }
+    }
+}
+
+/* One block: integer part P = sum (q - z) q8, the activation sum S = sum q8,
+ * and the fp64 term d d8 P + m d8 S with the sum of the absolute parts. */
+static void w_block(int type, const uint8_t* wb, const uint8_t* ab, int32_t* P, double* term, double* absterm)
+{
+    int q[QK], z;
+    double d, m;
+    w_decode(type, wb, q, &z, &d, &m);
+    const double d8 = (double)oracle_fp16_to_fp32(get_u16(ab));
+    int32_t p = 0, sum = 0;
+    for (int i = 0; i < QK; ++i) {
+        const int a = q8_value(ab, i);
+        p += (q[i] - z) * a;
+        sum += a;
+    }
+    *P = p;
+    const double t1 = d * d8 * (double)p, t2 = m * d8 * (double)sum;
+    *term = t1 + t2;
+    *absterm = fabs(t1) + fabs(t2);
+}
+
+static void w_pair(int type, const uint8_t* w, const uint8_t* a, int64_t e, int64_t row,
+                   int64_t E, int64_t N, int64_t nb, double* out, double* abssum)
+{
+    const int bytes = oracle_w_block_bytes(type);
+    for (int64_t n = 0; n < N; ++n) {
+        double acc = 0.0, aabs = 0.0;
+        if (e >= 0 && e < E) {
+            for (int64_t b = 0; b < nb; ++b) {
+                int32_t P;
+                double t, at;
+                w_block(type, w + ((e * N + n) * nb + b) * bytes, act_block(a, row, b, nb), &P, &t, &at);
+                acc += t;
+                aabs += at;
+            }
+        }
+        out[n] = acc;
+        if (abssum) abssum[n] = aabs;
+    }
+}
+
+/* The matmul for weights of `type`: as oracle_moe_pairs_ex (pair p reads
+ * activation row p / act_div; out row i belongs to pair pairs[i]). */
+void oracle_moe_w_pairs(int type, const uint8_t* w, const uint8_t* a, const int32_t* ids,
+                        int64_t E, int64_t N, int64_t K, int64_t act_div,
+                        const int64_t* pairs, int64_t npairs, double* out, double* abssum)
+{
+    const int64_t nb = K / QK;
+    int64_t i;
+#pragma omp parallel for schedule(dynamic, 1)
+    for (i = 0; i < npairs; ++i) {
+        const int64_t p = pairs[i];
+        w_pair(type, w, a, (int64_t)ids[p], p / act_div, E, N, nb, out + i * N, abssum ? abssum + i * N : NULL);
+    }
+}
+
+/* Integer parts P[p][n][b] = sum (q - z) q8 for weights of `type` (zeros for masked pairs). */
+void oracle_moe_w_partials(int type, const uint8_t* w, const uint8_t* a, const int32_t* ids,
+                           int64_t E, int64_t N, int64_t K, int64_t T, int64_t top_k, int64_t act_div,
+                           int32_t* partials)
+{
+    const int64_t nb = K / QK;
+    const int bytes = oracle_w_block_bytes(type);
+    int64_t p;
+#pragma omp parallel for schedule(dynamic, 1)
+    for (p = 0; p < T * top_k; ++p) {
+        const int64_t e = ids[p];
+        for (int64_t n = 0; n < N; ++n)
+            for (int64_t b = 0; b < nb; ++b) {
+                int32_t P = 0;
+                double t, at;
+                if (e >= 0 && e < E)
+                    w_block(type, w + ((e * N + n) * nb + b) * bytes, act_block(a, p / act_div, b, nb), &P, &t, &at);
+                partials[(p * N + n) * nb + b] = P;
+            }
+    }
+}
+
 /* Gated activations in fp64 (libm exp and tanh):
  *   act 1, SiLU:      x / (1 + exp(-x))
  *   act 2, GELU-tanh: x / 2 * (1 + tanh(sqrt(2/pi) * (x + 0.044715 x^3))) */

@@ -438,3 +438,101 @@ def test_act_and_mul_takes_gate_from_the_first_half():
     assert out[1, 1] == s25 * -3.0
     swapped = oracle.act_and_mul(np.concatenate([y[:, 2:], y[:, :2]], axis=1), oracle.ACT_SILU)
     assert not np.allclose(swapped, out)
+
+
+# ------------------------------------------- sibling GGUF block types ------
+
+SIBLINGS = [oracle.W_Q4_1, oracle.W_Q5_0, oracle.W_Q5_1, oracle.W_Q8_0]
+
+
+def _tiny_w(wtype, seed=0, E=3, top_k=2, T=3, K=96, N=5):
+    w = oracle.quantize_w(wtype, inputs.weights(E, N, K, seed=seed) * 40)   # spread codes over the range
+    a = oracle.quantize_q8_1(inputs.activations(T, K, seed=seed))
+    ids = inputs.routing(T, E, top_k, seed=seed)
+    return w, a, ids, dict(E=E, N=N, K=K, T=T, top_k=top_k)
+
+
+@pytest.mark.parametrize("wtype", SIBLINGS)
+def test_sibling_exact_rational_bruteforce(wtype):
+    """Independent numpy decode, exact Fractions; fp64 error within gamma(2 nb) * sum of |parts|."""
+    w, a, ids, c = _tiny_w(wtype, seed=wtype)
+    out, ab = oracle.moe_w(wtype, w, a, ids, c["E"], c["N"], c["K"], c["T"], c["top_k"], want_abssum=True)
+    d, m, q, z = _decode.gguf_w(wtype, w.reshape(c["E"], c["N"], -1), c["K"])
+    ad, _, aq = _decode.q8_1(a, c["K"])
+    nb = c["K"] // 32
+    for p in range(c["T"] * c["top_k"]):
+        t, e = p // c["top_k"], int(ids.reshape(-1)[p])
+        for n in range(c["N"]):
+            exact = Fraction(0)
+            for b in range(nb):
+                P = sum((int(q[e, n, b, i]) - z) * int(aq[t, b, i]) for i in range(32))
+                S = sum(int(aq[t, b, i]) for i in range(32))
+                exact += Fraction(ad[t, b]) * (Fraction(d[e, n, b]) * P + Fraction(m[e, n, b]) * S)
+            assert abs(Fraction(out[p, n]) - exact) <= Fraction(gamma(2 * nb, U64)) * Fraction(ab[p, n])
+
+
+@pytest.mark.parametrize("wtype", SIBLINGS)
+def test_sibling_partials_match_integer_einsum(wtype):
+    w, a, ids, c = _tiny_w(wtype, seed=1, E=4, T=9, K=256, N=17)
+    P = oracle.moe_w_partials(wtype, w, a, ids, c["E"], c["N"], c["K"], c["T"], c["top_k"])
+    _, _, q, z = _decode.gguf_w(wtype, w.reshape(c["E"], c["N"], -1), c["K"])
+    _, _, aq = _decode.q8_1(a, c["K"])
+    tok = np.arange(c["T"] * c["top_k"]) // c["top_k"]
+    ref = np.einsum("pnbi,pbi->pnb", q[ids.reshape(-1)] - z, aq[tok])
+    assert P.dtype == np.int32 and np.array_equal(P, ref)
+
+
+def test_generic_path_reproduces_q4_0():
+    w, a, ids, c = _tiny(seed=9)
+    assert np.array_equal(oracle.moe_w(oracle.W_Q4_0, w, a, ids, c["E"], c["N"], c["K"], c["T"], c["top_k"]),
+                          _run(w, a, ids, c))
+
+
+@pytest.mark.parametrize("wtype", SIBLINGS)
+def test_sibling_quantizers_recover_exact_grids(wtype):
+    rng = np.random.default_rng(wtype)
+    levels = {oracle.W_Q4_1: 15, oracle.W_Q5_0: 31, oracle.W_Q5_1: 31, oracle.W_Q8_0: 254}[wtype]
+    d = 2.0 ** -6
+    rows = []
+    for _ in range(16):
+        q = rng.integers(0, levels + 1, 32)
+        q[0], q[1] = 0, levels                       # both ends present: the range is levels * d
+        if wtype == oracle.W_Q5_0:
+            q[1] = 0; q[2] = 31 - 15                 # extreme -16 * d: (0 - 16) d sets d
+            rows.append((q - 16) * d)
+        elif wtype == oracle.W_Q8_0:
+            rows.append((q - 127) * d)               # |x| <= 127 d with 127 d present
+        else:
+            rows.append(q * d - 0.5)                 # offset -0.5: m = min = -0.5
+    x = np.array(rows, np.float32)
+    y = oracle.quantize_w(wtype, x)
+    dd, mm, qq, z = _decode.gguf_w(wtype, y, 32)
+    back = dd[..., None] * (qq - z) + mm[..., None]
+    assert np.array_equal(back.reshape(x.shape).astype(np.float32), x)
+
+
+def test_sibling_layout_closed_forms():
+    a = np.zeros((1, 36), np.uint8)                  # one Q8_1 block: d8 = 0.5, codes 1..32 at element i
+    a[0, 0:2] = np.frombuffer(np.float16(0.5).tobytes(), np.uint8)
+    a[0, 4:36] = np.arange(1, 33, dtype=np.int8).view(np.uint8)
+    ids = np.zeros((1, 1), np.int32)
+    S = sum(range(1, 33))
+    # Q4_1 with every nibble 0: every weight is m, so out = m * d8 * S
+    w = np.zeros(20, np.uint8)
+    w[0:2] = np.frombuffer(np.float16(0.25).tobytes(), np.uint8)
+    w[2:4] = np.frombuffer(np.float16(-1.5).tobytes(), np.uint8)
+    assert oracle.moe_w(oracle.W_Q4_1, w, a.reshape(-1), ids, 1, 1, 32, 1, 1)[0, 0] == -1.5 * 0.5 * S
+    # Q5_0: qh bit 21 and nibble 15 of element 21 (high nibble of byte 5) give q = 31, others q = 16 (zero)
+    w = np.zeros(22, np.uint8)
+    w[0:2] = np.frombuffer(np.float16(0.125).tobytes(), np.uint8)
+    w[2:6] = np.frombuffer(np.uint32(1 << 21).tobytes(), np.uint8)
+    w[6:22] = 0x00
+    w[6 + 5] = 0xF0
+    qh_other = np.uint32(0xFFFFFFFF ^ (1 << 21))     # every other element: bit 4 set, nibble 0 -> 16
+    w[2:6] = np.frombuffer(np.uint32(qh_other | (1 << 21)).tobytes(), np.uint8)
+    assert oracle.moe_w(oracle.W_Q5_0, w, a.reshape(-1), ids, 1, 1, 32, 1, 1)[0, 0] == 15 * 0.125 * 0.5 * 22
+    # Q8_0: code -3 at element 7 only
+    w = np.zeros(34, np.uint8)
+    w[0:2] = np.frombuffer(np.float16(2.0).tobytes(), np.uint8)
+    w[2 + 7] = np.uint8(np.int8(-3).view(np.uint8))
+    assert oracle.moe_w(oracle.W_Q8_0, w, a.reshape(-1), ids, 1, 1, 32, 1, 1)[0, 0] == -3 * 2.0 * 0.5 * 8
