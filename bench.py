@@ -12,6 +12,7 @@ before timing starts.
     python bench.py [--steps K] [--warmup W] [--T tokens]
     python bench.py --workload page1_down  # the second layer: per-pair rows + combine
     python bench.py --workload page1_act   # the first layer with act(gate) * up fused
+    python bench.py --workload mixtral --T 1 --wtype q8_0   # another GGUF weight type (GEMV path)
     python bench.py --mode profile         # a short run for rocprofv3
     python bench.py --summarize-pmc DIR    # HBM traffic from rocprofv3 --pmc runs
 
@@ -80,7 +81,11 @@ def _lib_hash() -> str:
     return open(p).read().strip() if os.path.exists(p) else ""
 
 
-def _algorithmic_bytes(E, N, K, T, k, ids, act_rows=None, out_cols=None):
+WTYPES = {"q4_0": 2, "q4_1": 3, "q5_0": 6, "q5_1": 7, "q8_0": 8}
+W_BLOCK_BYTES = {2: 18, 3: 20, 6: 22, 7: 24, 8: 34}
+
+
+def _algorithmic_bytes(E, N, K, T, k, ids, act_rows=None, out_cols=None, block_bytes=18):
     """Bytes the method must move: the distinct experts' Q4_0 rows, the Q8_1
     activations (one row per token, or per pair), the int32 ids and the fp32
     output (N columns, or N/2 with the activation fused)."""
@@ -89,7 +94,7 @@ def _algorithmic_bytes(E, N, K, T, k, ids, act_rows=None, out_cols=None):
     rows = T if act_rows is None else act_rows
     cols = N if out_cols is None else out_cols
     distinct = len(np.unique(ids[(ids >= 0) & (ids < E)]))
-    return distinct * N * nb * 18 + rows * nb * 36 + 4 * T * k + 4 * T * k * cols
+    return distinct * N * nb * block_bytes + rows * nb * 36 + 4 * T * k + 4 * T * k * cols
 
 
 def summarize_pmc(d: str, kernel: str = DOMINANT) -> None:
@@ -134,6 +139,8 @@ def main() -> None:
     ap.add_argument("--workload", choices=sorted(WORKLOADS), default="page1")
     ap.add_argument("--T", type=int, default=None, help="tokens (default: the workload's own)")
     ap.add_argument("--mode", choices=["bench", "profile"], default="bench")
+    ap.add_argument("--wtype", choices=sorted(WTYPES), default="q4_0",
+                    help="weight block type (not q4_0: random valid blocks, GEMV path, plain layers only)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-sample-tokens", type=int, default=2048)
     ap.add_argument("--summarize-pmc", metavar="DIR")
@@ -161,6 +168,10 @@ def main() -> None:
     seed = wl["seed"]
     down = wl.get("layer") == "down"
     fused = wl.get("layer") == "act"
+    wt = WTYPES[args.wtype]
+    if wt != 2 and fused:
+        print("bench.py: the fused activation takes Q4_0 weights only", file=sys.stderr)
+        sys.exit(2)
     act_kind = {"silu": 1, "gelu_tanh": 2}.get(wl.get("act", ""), 0)
     act_rows = T * k if down else T
     out_cols = N // 2 if fused else N
@@ -168,16 +179,19 @@ def main() -> None:
     dev = torch.device("cuda", 0)
 
     # ---- inputs, resident in HBM --------------------------------------------
-    w32 = inputs.weights(E, N, K, seed=seed)
+    w32 = inputs.weights(E, N, K, seed=seed) if wt == 2 else None
     x32 = inputs.activations(act_rows, K, seed=seed)
     ids = inputs.routing(T, E, k, seed=seed, kind=wl["routing"])
     gates = inputs.gates(T, k, seed=seed)
-    wdev = torch.from_numpy(w32).to(dev)
-    wq = ftq.quantize_q4_0(wdev)
-    del wdev
+    if wt == 2:
+        wdev = torch.from_numpy(w32).to(dev)
+        wq = ftq.quantize_q4_0(wdev)
+        del wdev
+    else:
+        wq = torch.from_numpy(inputs.gguf_blocks(wt, E, N, K, seed=seed)).to(dev)
     x = torch.from_numpy(x32).to(dev)
     ids_d = torch.from_numpy(ids).to(dev)
-    path = ftq.select_path(E, N, K, T, k)
+    path = ftq.select_path(E, N, K, T, k) if wt == 2 else ftq.PATH_GEMV
     gates_d = torch.from_numpy(gates).to(dev)
     aq = torch.empty((act_rows, K // 32 * 36), dtype=torch.uint8, device=dev)
     out = torch.empty((T * k, out_cols), dtype=torch.float32, device=dev)
@@ -198,7 +212,9 @@ def main() -> None:
         ftq.moe_route(ids_d, E, ws, path)
         if marks:
             marks[2].record()
-        if down:
+        if wt != 2:
+            ftq.moe_gguf(wq, wt, aq, ids_d, E, N, K, per_pair=down, path=path, out=out, workspace=ws)
+        elif down:
             ftq.moe_pairs_routed(wq, aq, ids_d, E, N, K, out, ws, path)
         elif fused:
             ftq.moe_act_routed(wq, aq, ids_d, E, N, K, act_kind, out, ws, path)
@@ -244,7 +260,7 @@ def main() -> None:
     # ---- roofline of the dominant kernel ------------------------------------
     pairs = T * k
     ops = 2.0 * pairs * N * K
-    alg_bytes = _algorithmic_bytes(E, N, K, T, k, ids, act_rows, out_cols)
+    alg_bytes = _algorithmic_bytes(E, N, K, T, k, ids, act_rows, out_cols, W_BLOCK_BYTES[wt])
     kern_s = mm_ms / 1e3
     tops = ops / kern_s / 1e12
     gbs = alg_bytes / kern_s / 1e9
@@ -273,9 +289,13 @@ def main() -> None:
     if not args.no_cpu_baseline:
         import oracle
         ts = min(args.cpu_sample_tokens, T)
-        ow = oracle.quantize_q4_0(w32).reshape(-1)       # weight preparation: not part of a step
+        # weight preparation: not part of a step
+        ow = oracle.quantize_q4_0(w32).reshape(-1) if wt == 2 else wq.cpu().numpy().reshape(-1)
         c0 = time.perf_counter()
-        if down:
+        if wt != 2:
+            oa = oracle.quantize_q8_1(x32[:ts * k] if down else x32[:ts]).reshape(-1)
+            oracle.moe_w(wt, ow, oa, np.ascontiguousarray(ids[:ts]), E, N, K, ts, k, per_pair=down)
+        elif down:
             oa = oracle.quantize_q8_1(x32[:ts * k]).reshape(-1)
             y = oracle.moe(ow, oa, np.ascontiguousarray(ids[:ts]), E, N, K, ts, k, per_pair=True)
             oracle.combine_topk(y, gates[:ts])
@@ -306,9 +326,9 @@ def main() -> None:
         "scaling": "weak",
         "vs_baseline": round(ms_per_step / PAGES_MS_T8191, 6) if args.workload == "page1" and T == DEFAULT_T else None,
         "dtype": ("q4_0 x q8_1 (exact integer block dots on f16 MFMA, fp32 scale-accumulate)" if path == ftq.PATH_GROUPED
-                  else "q4_0 x q8_1 (int8 dot4 block dots, fp32 scale-accumulate)"),
+                  else f"{args.wtype} x q8_1 (int8 dot4 block dots, fp32 scale-accumulate)"),
         "data": "synthetic",
-        "config": dict(wl, T=T, pairs=pairs, path={1: "gemv", 2: "grouped"}[path]),
+        "config": dict(wl, T=T, pairs=pairs, path={1: "gemv", 2: "grouped"}[path], wtype=args.wtype),
         "breakdown_ms": dict({"quantize_q8_1": round(q_ms, 4), "route": round(r_ms, 4), "matmul": round(mm_ms, 4)},
                              **({"combine_topk": round(cb_ms, 4)} if down else {})),
         "throughput": dict({"tokens_per_s": round(T / (ms_per_step / 1e3), 1), "matmul_TOPS": round(tops, 2),

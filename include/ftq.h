@@ -67,6 +67,15 @@ typedef enum {
     FTQ_PATH_GROUPED = 2      /* expert-sorted MFMA tiles for prefill        */
 } ftq_path;
 
+/* Weight block types, with the type ids GGUF files use (see ftq_moe_gguf_q8_1). */
+typedef enum {
+    FTQ_W_Q4_0 = 2,           /* 18 B: fp16 d, 16 nibble bytes           w = (q - 8) d  */
+    FTQ_W_Q4_1 = 3,           /* 20 B: fp16 d, fp16 m, 16 nibble bytes   w = q d + m    */
+    FTQ_W_Q5_0 = 6,           /* 22 B: fp16 d, 32-bit qh, nibble bytes   w = (q - 16) d */
+    FTQ_W_Q5_1 = 7,           /* 24 B: fp16 d, fp16 m, qh, nibble bytes  w = q d + m    */
+    FTQ_W_Q8_0 = 8            /* 34 B: fp16 d, 32 int8                   w = q d        */
+} ftq_wtype;
+
 typedef enum {
     FTQ_ACT_SILU = 1,         /* x / (1 + exp(-x))                           */
     FTQ_ACT_GELU_TANH = 2     /* x/2 (1 + tanh(sqrt(2/pi) (x + 0.044715 x^3))) */
@@ -253,6 +262,41 @@ int ftq_moe_q4_0_q8_1_act(const void* w, const void* a, const int32_t* topk_ids,
 int ftq_moe_q4_0_q8_1_act_routed(const void* w, const void* a, const int32_t* topk_ids, float* out,
                                  int64_t E, int64_t N, int64_t K, int64_t T, int64_t top_k, int act,
                                  void* workspace, size_t workspace_bytes, int path, hipStream_t stream);
+
+/*
+ * The matmul for the other GGUF weight block types that FreeToken PR #185
+ * (Problem) counts among the GEMV's sibling launchers: Q4_1, Q5_0, Q5_1 and
+ * Q8_0 (layouts in ftq_wtype; the pages name the types but print no layout:
+ * these are the GGUF layouts), against Q8_1 activations.  For pair p, row n:
+ *
+ *   out[p][n] = sum_b ( d[n][b] * d8[b] * sum_i (q[n][b][i] - z) * q8[b][i]
+ *                     + m[n][b] * d8[b] * sum_i q8[b][i] )
+ *
+ * z the zero point (8 for Q4_0, 16 for Q5_0, else 0) and m the offset (Q4_1,
+ * Q5_1; else 0): the dot product of the dequantised weights and activations.
+ * The integer sums are exact; the offset term uses the exact integer sum of
+ * the activation codes, not the fp16 s field.  Evaluation: fp32, per block
+ * acc = fma(P, d*d8, acc) then, for offset types, acc = fma(S, m*d8, acc).
+ *   w:          [E][N][K/32] blocks of wtype;
+ *   a:          Q8_1, [T][K/32] (act_per_pair == 0) or [T*top_k][K/32] (one
+ *               row per pair, as ftq_moe_q4_0_q8_1_pairs);
+ *   other arguments as ftq_moe_q4_0_q8_1; the workspace is
+ *   ftq_moe_workspace_bytes(E, N, K, T, top_k, FTQ_PATH_GEMV) bytes.
+ * FTQ_W_Q4_0 runs the Q4_0 paths (both).  The other types run on the GEMV
+ * path (FTQ_PATH_AUTO selects it); FTQ_PATH_GROUPED returns
+ * FTQ_ERR_UNSUPPORTED, as do weight rows that are not 4-byte aligned (Q5_0 and
+ * Q8_0 with an odd K/32).  Unknown wtype: FTQ_ERR_INVALID_ARG.
+ * ftq_moe_gguf_q8_1_partials writes the integer parts sum((q - z) * q8) as
+ * int32 [T*top_k][N][K/32] instead (checking aid).
+ */
+int ftq_moe_gguf_q8_1(const void* w, int wtype, const void* a, const int32_t* topk_ids, float* out,
+                      int64_t E, int64_t N, int64_t K, int64_t T, int64_t top_k, int act_per_pair,
+                      void* workspace, size_t workspace_bytes, int path, hipStream_t stream);
+
+int ftq_moe_gguf_q8_1_partials(const void* w, int wtype, const void* a, const int32_t* topk_ids,
+                               int32_t* partials, int64_t E, int64_t N, int64_t K, int64_t T, int64_t top_k,
+                               int act_per_pair, void* workspace, size_t workspace_bytes, int path,
+                               hipStream_t stream);
 
 const char* ftq_last_error(void);
 

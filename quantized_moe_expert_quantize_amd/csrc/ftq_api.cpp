@@ -107,7 +107,7 @@ int select_path(int64_t E, int64_t T, int64_t top_k)
 int64_t tile_m_for(int64_t E, int64_t N, int64_t K, int64_t T, int64_t top_k)
 {
     MoeArgs m{};
-    m.E = E; m.N = N; m.K = K; m.T = T; m.top_k = top_k;
+    m.E = E; m.N = N; m.K = K; m.T = T; m.top_k = top_k; m.wtype = FTQ_W_Q4_0;
     return grouped_tile_m(m);
 }
 
@@ -150,11 +150,24 @@ int64_t act_rows_of(int64_t T, int64_t top_k, bool act_per_pair) { return act_pe
 
 int moe_common(const void* w, const void* a, const int32_t* ids, float* out, int32_t* partials,
                int64_t E, int64_t N, int64_t K, int64_t T, int64_t top_k, void* ws, size_t ws_bytes,
-               int path, hipStream_t stream, int phases, bool act_per_pair = false, int act = 0)
+               int path, hipStream_t stream, int phases, bool act_per_pair = false, int act = 0,
+               int wtype = FTQ_W_Q4_0)
 {
     clear_error();
     int st = check_sizes(E, N, K, T, top_k);
     if (st != FTQ_OK) return st;
+    if (wtype != FTQ_W_Q4_0 && wtype != FTQ_W_Q4_1 && wtype != FTQ_W_Q5_0 && wtype != FTQ_W_Q5_1 && wtype != FTQ_W_Q8_0) {
+        set_error("unknown weight type %d", wtype);
+        return FTQ_ERR_INVALID_ARG;
+    }
+    if (wtype != FTQ_W_Q4_0) {
+        // the other block types run on the GEMV path only
+        if (path == FTQ_PATH_GROUPED) {
+            set_error("weight type %d: the grouped path takes Q4_0 only; use FTQ_PATH_GEMV or FTQ_PATH_AUTO", wtype);
+            return FTQ_ERR_UNSUPPORTED;
+        }
+        if (path == FTQ_PATH_AUTO) path = FTQ_PATH_GEMV;
+    }
     if (act != 0) {
         if (act != FTQ_ACT_SILU && act != FTQ_ACT_GELU_TANH) { set_error("unknown activation %d", act); return FTQ_ERR_INVALID_ARG; }
         if (N % 2 != 0) { set_error("a gated activation needs an even N (gate and up halves), got %lld", (long long)N); return FTQ_ERR_INVALID_ARG; }
@@ -185,7 +198,7 @@ int moe_common(const void* w, const void* a, const int32_t* ids, float* out, int
         }
     }
     if (!(phases & kMatmul)) return FTQ_OK;
-    MoeArgs m{w, a, ids, out, partials, E, N, K, T, top_k, act_per_pair ? 1 : top_k, act};
+    MoeArgs m{w, a, ids, out, partials, E, N, K, T, top_k, act_per_pair ? 1 : top_k, act, wtype};
     if (rp == FTQ_PATH_GEMV) return run_gemv(m, bucketed ? &plan : nullptr, ws, stream);
     return run_grouped(m, plan, ws, stream);
 }
@@ -341,6 +354,22 @@ int ftq_moe_q4_0_q8_1_act_routed(const void* w, const void* a, const int32_t* to
 {
     return moe_common(w, a, topk_ids, out, nullptr, E, N, K, T, top_k, workspace, workspace_bytes, path, stream,
                       kMatmul, false, act);
+}
+
+int ftq_moe_gguf_q8_1(const void* w, int wtype, const void* a, const int32_t* topk_ids, float* out, int64_t E,
+                      int64_t N, int64_t K, int64_t T, int64_t top_k, int act_per_pair, void* workspace,
+                      size_t workspace_bytes, int path, hipStream_t stream)
+{
+    return moe_common(w, a, topk_ids, out, nullptr, E, N, K, T, top_k, workspace, workspace_bytes, path, stream,
+                      kRoute | kMatmul, act_per_pair != 0, 0, wtype);
+}
+
+int ftq_moe_gguf_q8_1_partials(const void* w, int wtype, const void* a, const int32_t* topk_ids, int32_t* partials,
+                               int64_t E, int64_t N, int64_t K, int64_t T, int64_t top_k, int act_per_pair,
+                               void* workspace, size_t workspace_bytes, int path, hipStream_t stream)
+{
+    return moe_common(w, a, topk_ids, nullptr, partials, E, N, K, T, top_k, workspace, workspace_bytes, path, stream,
+                      kRoute | kMatmul, act_per_pair != 0, 0, wtype);
 }
 
 const char* ftq_last_error(void) { return g_error.c_str(); }

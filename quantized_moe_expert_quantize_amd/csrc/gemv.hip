@@ -45,13 +45,22 @@ constexpr int kWaves = kThreads / 64;
 constexpr int kLPR = 16;                                        // lanes per row
 constexpr int kRowsPerWave = 64 / kLPR;                         // 4
 constexpr int kRowsPerTile = kRowsPerWave * kWaves;             // 16
-constexpr int kGroup = 8;                                       // blocks per lane group (144 bytes)
+constexpr int kGroup = 8;                                       // blocks per lane group (8 blocks: 144 B for Q4_0)
 constexpr int kPairChunk = 8;                                   // pairs served per pass
 constexpr int kStepGroups = kLPR;                               // groups per row per step
 constexpr int kStepBlocks = kStepGroups * kGroup;               // 128
-constexpr int kStepBytes = kStepBlocks * kQ4Bytes;              // 2304
-constexpr int kWRowPitch = kStepBytes + 16;                     // LDS bytes per row of a step
-constexpr int kWaveW = kRowsPerWave * kWRowPitch;               // LDS bytes per wave for weights
+
+// Weight block geometry per GGUF type (type ids as in GGUF files; Q4_0 = 2):
+// bytes per block, per step of one row, per LDS row of a step (+16 B pad), per
+// wave's rows.  A lane's group of 8 blocks is a multiple of 16 bytes for every
+// type, so whole groups load as 16-byte units.
+__host__ __device__ constexpr int w_block_bytes(int wt)
+{
+    return wt == FTQ_W_Q4_1 ? 20 : wt == FTQ_W_Q5_0 ? 22 : wt == FTQ_W_Q5_1 ? 24 : wt == FTQ_W_Q8_0 ? 34 : 18;
+}
+__host__ __device__ constexpr int step_bytes(int wt) { return kStepBlocks * w_block_bytes(wt); }
+__host__ __device__ constexpr int wrow_pitch(int wt) { return step_bytes(wt) + 16; }
+__host__ __device__ constexpr int wave_w(int wt) { return kRowsPerWave * wrow_pitch(wt); }
 constexpr int kWavesPerSimd = 3;                                // register budget: 3 waves per SIMD
 constexpr int64_t kLdsPerCU = 160 * 1024;
 constexpr int64_t kTargetWGPerCU = 2;                           // LDS is sized so that 2 workgroups fit
@@ -89,12 +98,12 @@ struct LdsLayout {
     int64_t wt, codes, ds, bits, prefix, plist, misc, list, bytes;
 };
 
-__host__ __device__ constexpr LdsLayout lds_layout(int64_t E, int64_t seg, int64_t pc_cap, int64_t list_cap)
+__host__ __device__ constexpr LdsLayout lds_layout(int wt, int64_t E, int64_t seg, int64_t pc_cap, int64_t list_cap)
 {
     LdsLayout l{};
     const int64_t words = (E + 1 + 31) / 32;
     l.wt = 0;
-    l.codes = l.wt + kWaves * kWaveW;
+    l.codes = l.wt + kWaves * wave_w(wt);
     l.ds = l.codes + code_bytes(seg, pc_cap);
     l.bits = (l.ds + ent_bytes(seg, pc_cap) + 15) / 16 * 16;
     l.prefix = l.bits + 4 * words;
@@ -133,57 +142,86 @@ __device__ __forceinline__ void stage_acts(const GemvParams& p, const int32_t* t
     }
 }
 
-// Integer partial of one block: P = sum (nib - 8) * q8 = sum nib*q8 - 8*sum q8.
-// lo/hi hold the low and high nibbles of the block's 16 bytes, one per byte.
-__device__ __forceinline__ int block_dot(const uint32_t lo[4], const uint32_t hi[4], const u32x4 a0,
-                                         const u32x4 a1, int neg8sum)
+// The 32-bit word at byte OFF (even) of a block pair held as words W.
+template <int OFF>
+__device__ __forceinline__ uint32_t word_at(const uint32_t* W)
 {
-    int acc = neg8sum;
-    acc = __builtin_amdgcn_sdot4((int)lo[0], (int)a0.x, acc, false);
-    acc = __builtin_amdgcn_sdot4((int)lo[1], (int)a0.y, acc, false);
-    acc = __builtin_amdgcn_sdot4((int)lo[2], (int)a0.z, acc, false);
-    acc = __builtin_amdgcn_sdot4((int)lo[3], (int)a0.w, acc, false);
-    acc = __builtin_amdgcn_sdot4((int)hi[0], (int)a1.x, acc, false);
-    acc = __builtin_amdgcn_sdot4((int)hi[1], (int)a1.y, acc, false);
-    acc = __builtin_amdgcn_sdot4((int)hi[2], (int)a1.z, acc, false);
-    acc = __builtin_amdgcn_sdot4((int)hi[3], (int)a1.w, acc, false);
+    if constexpr (OFF % 4 == 0) return W[OFF / 4];
+    else return __builtin_amdgcn_alignbit(W[OFF / 4 + 1], W[OFF / 4], 16);
+}
+template <int OFF>
+__device__ __forceinline__ uint32_t half_at(const uint32_t* W)
+{
+    if constexpr (OFF % 4 == 0) return W[OFF / 4] & 0xffffu;
+    else return W[OFF / 4] >> 16;
+}
+
+// Bits 0..3 of t moved to bit 4 of bytes 0..3 (the fifth bit of four codes):
+// t * 0x204081 puts bit k at bit 8k with no carries.
+__device__ __forceinline__ uint32_t high_bits(uint32_t t)
+{
+    return ((__builtin_amdgcn_ubfe(t, 0, 4) * 0x204081u) & 0x01010101u) << 4;
+}
+
+// One weight block at byte BASE of a pair's words, decoded once for all the
+// pairs it serves: eight words of byte codes (c[i] pairs with activation
+// codes 4i..4i+3, c[4+i] with 16+4i..), the fp16 bits of the scale and (offset
+// types) of the offset.  Nibble byte i holds element i (low) and i + 16
+// (high); qh bit i is bit 4 of element i; Q8_0 codes are the int8 bytes.
+template <int WT, int BASE>
+__device__ __forceinline__ void decode_block(const uint32_t* W, uint32_t c[8], uint32_t& dbits, uint32_t& mbits)
+{
+    dbits = half_at<BASE>(W);
+    mbits = 0;
+    if constexpr (WT == FTQ_W_Q8_0) {
+        c[0] = word_at<BASE + 2>(W);  c[1] = word_at<BASE + 6>(W);
+        c[2] = word_at<BASE + 10>(W); c[3] = word_at<BASE + 14>(W);
+        c[4] = word_at<BASE + 18>(W); c[5] = word_at<BASE + 22>(W);
+        c[6] = word_at<BASE + 26>(W); c[7] = word_at<BASE + 30>(W);
+    } else {
+        constexpr bool kOffset = WT == FTQ_W_Q4_1 || WT == FTQ_W_Q5_1;
+        constexpr bool kFive = WT == FTQ_W_Q5_0 || WT == FTQ_W_Q5_1;
+        constexpr int kQh = BASE + (kOffset ? 4 : 2);            // Q5 types: the 32 high bits
+        constexpr int kQs = kQh + (kFive ? 4 : 0);               // the 16 nibble bytes
+        if constexpr (kOffset) mbits = half_at<BASE + 2>(W);
+        const uint32_t qs[4] = {word_at<kQs>(W), word_at<kQs + 4>(W), word_at<kQs + 8>(W), word_at<kQs + 12>(W)};
+        uint32_t qh = 0;
+        if constexpr (kFive) qh = word_at<kQh>(W);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            c[i] = qs[i] & 0x0f0f0f0fu;
+            c[4 + i] = (qs[i] >> 4) & 0x0f0f0f0fu;
+            if constexpr (kFive) {
+                c[i] |= high_bits(qh >> (4 * i));
+                c[4 + i] |= high_bits(qh >> (16 + 4 * i));
+            }
+        }
+    }
+}
+
+// The exact integer P = sum (q - z) q8 of a decoded block against one staged
+// Q8_1 block (a0 = codes 0..15, a1 = 16..31; neg8sum = -8 * sum(q8)); the zero
+// point z (8 for Q4_0, 16 for Q5_0, else 0) enters as the integer z * sum(q8).
+template <int WT>
+__device__ __forceinline__ int block_dot(const uint32_t c[8], const u32x4 a0, const u32x4 a1, int neg8sum)
+{
+    int acc = WT == FTQ_W_Q4_0 ? neg8sum : WT == FTQ_W_Q5_0 ? 2 * neg8sum : 0;
+    acc = __builtin_amdgcn_sdot4((int)c[0], (int)a0.x, acc, false);
+    acc = __builtin_amdgcn_sdot4((int)c[1], (int)a0.y, acc, false);
+    acc = __builtin_amdgcn_sdot4((int)c[2], (int)a0.z, acc, false);
+    acc = __builtin_amdgcn_sdot4((int)c[3], (int)a0.w, acc, false);
+    acc = __builtin_amdgcn_sdot4((int)c[4], (int)a1.x, acc, false);
+    acc = __builtin_amdgcn_sdot4((int)c[5], (int)a1.y, acc, false);
+    acc = __builtin_amdgcn_sdot4((int)c[6], (int)a1.z, acc, false);
+    acc = __builtin_amdgcn_sdot4((int)c[7], (int)a1.w, acc, false);
     return acc;
 }
 
-// One lane's group of up to 8 blocks (144 bytes) as 36 words.
-struct Group {
-    uint32_t w[36];
-};
-
-// Block jb (0..7) of a group: fp16 scale bits and its low / high nibbles.
-__device__ __forceinline__ void group_block(const Group& G, int jb, uint32_t& dbits, uint32_t lo[4], uint32_t hi[4])
-{
-    const int k = 9 * (jb >> 1);
-    uint32_t qs[4];
-    if ((jb & 1) == 0) {   // the block starts at word k
-        dbits = G.w[k] & 0xffffu;
-        qs[0] = __builtin_amdgcn_alignbit(G.w[k + 1], G.w[k], 16);
-        qs[1] = __builtin_amdgcn_alignbit(G.w[k + 2], G.w[k + 1], 16);
-        qs[2] = __builtin_amdgcn_alignbit(G.w[k + 3], G.w[k + 2], 16);
-        qs[3] = __builtin_amdgcn_alignbit(G.w[k + 4], G.w[k + 3], 16);
-    } else {               // the block starts in the upper half of word k+4
-        dbits = G.w[k + 4] >> 16;
-        qs[0] = G.w[k + 5];
-        qs[1] = G.w[k + 6];
-        qs[2] = G.w[k + 7];
-        qs[3] = G.w[k + 8];
-    }
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-        lo[i] = qs[i] & 0x0f0f0f0fu;
-        hi[i] = (qs[i] >> 4) & 0x0f0f0f0fu;
-    }
-}
-
 // One lane's share of a step as loaded: VEC-byte units 16*i + l of the step.
-template <int VEC>
+template <int VEC, int WT>
 struct Raw {
-    static constexpr int kUnits = kStepBytes / VEC / kLPR;   // 9, 36 or 72
+    static constexpr int kUnits = step_bytes(WT) / VEC / kLPR;   // Q4_0: 9, 36 or 72
+    static_assert(step_bytes(WT) % (VEC * kLPR) == 0, "whole units per lane");
     using Unit = typename std::conditional<VEC == 16, u32x4, typename std::conditional<VEC == 4, uint32_t, uint16_t>::type>::type;
     Unit u[kUnits];
 };
@@ -191,14 +229,14 @@ struct Raw {
 // Load the step of `len` bytes at `src` (VEC-aligned, len a positive multiple
 // of VEC).  Units past `len` re-read the last unit instead of branching, so the
 // nine (or more) loads issue back to back with no wait between them.
-template <int VEC>
-__device__ __forceinline__ void load_step(const uint8_t* src, int len, int l, Raw<VEC>& R)
+template <int VEC, int WT>
+__device__ __forceinline__ void load_step(const uint8_t* src, int len, int l, Raw<VEC, WT>& R)
 {
-    using Unit = typename Raw<VEC>::Unit;
+    using Unit = typename Raw<VEC, WT>::Unit;
     const Unit* s = reinterpret_cast<const Unit*>(src);
     const int last = len / VEC - 1;
 #pragma unroll
-    for (int i = 0; i < Raw<VEC>::kUnits; ++i) R.u[i] = __builtin_nontemporal_load(s + min(kLPR * i + l, last));
+    for (int i = 0; i < Raw<VEC, WT>::kUnits; ++i) R.u[i] = __builtin_nontemporal_load(s + min(kLPR * i + l, last));
 }
 
 // Lanes of a wave exchange data through its private LDS step buffer.  The
@@ -211,13 +249,13 @@ __device__ __forceinline__ void wave_lds_fence() { __builtin_amdgcn_fence(__ATOM
 // Write the loaded units to the row's LDS step buffer in memory order.  Units
 // past the step's length land in the buffer's unused tail, which no lane reads
 // as a block.
-template <int VEC>
-__device__ __forceinline__ void store_step(uint8_t* wrow, int l, const Raw<VEC>& R)
+template <int VEC, int WT>
+__device__ __forceinline__ void store_step(uint8_t* wrow, int l, const Raw<VEC, WT>& R)
 {
-    using Unit = typename Raw<VEC>::Unit;
+    using Unit = typename Raw<VEC, WT>::Unit;
     Unit* d = reinterpret_cast<Unit*>(wrow);
 #pragma unroll
-    for (int i = 0; i < Raw<VEC>::kUnits; ++i) d[kLPR * i + l] = R.u[i];
+    for (int i = 0; i < Raw<VEC, WT>::kUnits; ++i) d[kLPR * i + l] = R.u[i];
 }
 
 // Rows of tiles [t0, t1) of expert e, K blocks [sb, sb+len), for the staged chunk.
@@ -230,7 +268,7 @@ __device__ __forceinline__ void store_step(uint8_t* wrow, int l, const Raw<VEC>&
 // wave w, row rw holds column 8t + 2w + (rw & 1), gate for rw < 2 and up for
 // rw >= 2, so that after the row sums lane l holds the gate and lane l ^ 32
 // the up value of the same column.
-template <int VEC, bool kPartials, bool kMultiSeg, int NPC, bool kFused>
+template <int VEC, bool kPartials, bool kMultiSeg, int NPC, bool kFused, int WT>
 __device__ __forceinline__ void stream_tiles(const GemvParams& p, int64_t e, int64_t t0, int64_t t1, int64_t sb, int len,
                                              int npc, const int32_t* plist, uint8_t* wrow, const uint8_t* codes,
                                              const uint8_t* ds, int l, int rw, int wave)
@@ -238,11 +276,13 @@ __device__ __forceinline__ void stream_tiles(const GemvParams& p, int64_t e, int
     constexpr int kJ = NPC > 0 ? NPC : kPairChunk;
     const int pc = p.pc_cap;
     const int64_t nb = p.nb;
-    const int64_t row_bytes = nb * kQ4Bytes;
+    constexpr int kBB = w_block_bytes(WT);
+    constexpr int kPairWords = kBB / 2;   // two blocks, dword aligned in LDS
+    const int64_t row_bytes = nb * kBB;
     const uint8_t* wexp = p.w + e * p.N * row_bytes;
     const int64_t gbeg = sb / kGroup, gend = (sb + len + kGroup - 1) / kGroup;
-    const int64_t seg_end = (sb + len) * kQ4Bytes;   // row bytes up to the segment's end
-    auto step_len = [&](int64_t ws) { return (int)min<int64_t>(kStepBytes, seg_end - ws * kGroup * kQ4Bytes); };
+    const int64_t seg_end = (sb + len) * kBB;   // row bytes up to the segment's end
+    auto step_len = [&](int64_t ws) { return (int)min<int64_t>(step_bytes(WT), seg_end - ws * kGroup * kBB); };
     // output column of this lane's row in tile t (the weight row unless fused)
     auto col_of = [&](int64_t t) {
         if constexpr (kFused) return t * (kRowsPerTile / 2) + wave * (kRowsPerWave / 2) + (rw & 1);
@@ -254,7 +294,7 @@ __device__ __forceinline__ void stream_tiles(const GemvParams& p, int64_t e, int
     };
     // rows past N (last tile only) load row N-1; their sums are never written
     auto src_of = [&](int64_t t, int64_t ws) {
-        return wexp + min<int64_t>(row_of(t), p.N - 1) * row_bytes + ws * kGroup * kQ4Bytes;
+        return wexp + min<int64_t>(row_of(t), p.N - 1) * row_bytes + ws * kGroup * kBB;
     };
     // steps are (tile t, first group ws of the step), tile-major
     auto advance = [&](int64_t& t, int64_t& ws) {
@@ -273,7 +313,7 @@ __device__ __forceinline__ void stream_tiles(const GemvParams& p, int64_t e, int
     // are in flight while the current one is computed.  Past the range the
     // load re-reads the last tile's first step (an L2 hit, never used): an
     // unconditional load keeps the loads in flight the same on every path.
-    Raw<VEC> R;
+    Raw<VEC, WT> R;
     int64_t t = t0, ws = gbeg;
     load_step<VEC>(src_of(t, ws), step_len(ws), l, R);
     while (t < t1) {
@@ -297,21 +337,24 @@ __device__ __forceinline__ void stream_tiles(const GemvParams& p, int64_t e, int
             // 16-byte loads imply K/32 % 8 == 0: every group is whole
             const int nblk = VEC == 16 ? kGroup : (int)min<int64_t>(kGroup, nb - (gbeg + gl) * kGroup);
             const int bl0 = (int)(gl * kGroup);   // first block of the group in the segment
-            const uint32_t* gw = reinterpret_cast<const uint32_t*>(wrow + l * kGroup * kQ4Bytes);
+            const uint32_t* gw = reinterpret_cast<const uint32_t*>(wrow + l * kGroup * kBB);
             // block pairs are read from the step buffer one at a time, which
             // bounds what is live at once to two blocks
 #pragma unroll
             for (int jp = 0; jp < kGroup / 2; ++jp) {
-                Group bp;   // two blocks = 9 words, dword aligned in LDS
+                uint32_t bp[kPairWords];
 #pragma unroll
-                for (int i = 0; i < 9; ++i) bp.w[i] = gw[9 * jp + i];
+                for (int i = 0; i < kPairWords; ++i) bp[i] = gw[kPairWords * jp + i];
 #pragma unroll
                 for (int h = 0; h < 2; ++h) {
                     const int jb = 2 * jp + h;
                     if (VEC == 16 || jb < nblk) {
-                        uint32_t dbits, lo[4], hi[4];
-                        group_block(bp, h, dbits, lo, hi);
+                        uint32_t cw[8], dbits, mbits;
+                        if (h == 0) decode_block<WT, 0>(bp, cw, dbits, mbits);
+                        else decode_block<WT, kBB>(bp, cw, dbits, mbits);
+                        // lanes past the segment add P * 0 (and S * 0)
                         const float d4 = valid ? half_bits_to_float(dbits) : 0.0f;
+                        const float m4 = valid ? half_bits_to_float(mbits) : 0.0f;
                         const uint8_t* cbj = codes + code_off(bl0 + jb, pc);
                         const uint8_t* ebj = ds + ent_off(bl0 + jb, pc);
 #pragma unroll
@@ -319,12 +362,15 @@ __device__ __forceinline__ void stream_tiles(const GemvParams& p, int64_t e, int
                             if (NPC > 0 || j < npc) {
                                 const u32x4* aqb = reinterpret_cast<const u32x4*>(cbj + 32 * j);
                                 const float2 en = *reinterpret_cast<const float2*>(ebj + 8 * j);
-                                const int P = block_dot(lo, hi, aqb[0], aqb[1], __float_as_int(en.y));
+                                const int neg8sum = __float_as_int(en.y);
+                                const int P = block_dot<WT>(cw, aqb[0], aqb[1], neg8sum);
                                 if constexpr (kPartials) {
                                     if (valid && n < p.N)
                                         p.partials[((int64_t)plist[j] * p.N + n) * nb + sb + bl0 + jb] = P;
                                 } else {
                                     acc[j] = __builtin_fmaf((float)P, d4 * en.x, acc[j]);
+                                    if constexpr (WT == FTQ_W_Q4_1 || WT == FTQ_W_Q5_1)   // + m d8 sum(q8)
+                                        acc[j] = __builtin_fmaf((float)(-(neg8sum >> 3)), m4 * en.x, acc[j]);
                                 }
                             }
                         }
@@ -371,12 +417,12 @@ __device__ __forceinline__ void stream_tiles(const GemvParams& p, int64_t e, int
     }
 }
 
-template <int VEC, bool kBucketed, bool kPartials, bool kMultiSeg, bool kFused>
+template <int VEC, bool kBucketed, bool kPartials, bool kMultiSeg, bool kFused, int WT>
 __global__ __launch_bounds__(kThreads, kWavesPerSimd) void moe_gemv_kernel(GemvParams p)
 {
     extern __shared__ __align__(16) uint8_t lds[];
     const int64_t nb = p.nb;
-    const LdsLayout L = lds_layout(p.E, p.seg, p.pc_cap, p.list_cap);
+    const LdsLayout L = lds_layout(WT, p.E, p.seg, p.pc_cap, p.list_cap);
     uint8_t* codes = lds + L.codes;
     uint8_t* ds = lds + L.ds;
     uint32_t* bits = reinterpret_cast<uint32_t*>(lds + L.bits);     // routed buckets (E+1 bits)
@@ -500,8 +546,8 @@ __global__ __launch_bounds__(kThreads, kWavesPerSimd) void moe_gemv_kernel(GemvP
                 if (sb > 0) __syncthreads();   // the previous segment's activations are consumed
                 stage_acts(p, ptok, npc, sb, len, codes, ds);
                 __syncthreads();
-                uint8_t* wrow = lds + L.wt + wave * kWaveW + rw * kWRowPitch;
-#define FTQ_STREAM(NPC) stream_tiles<VEC, kPartials, kMultiSeg, NPC, kFused>(p, e, t0, t1, sb, len, npc, plist, wrow, codes, ds, l, rw, wave)
+                uint8_t* wrow = lds + L.wt + wave * wave_w(WT) + rw * wrow_pitch(WT);
+#define FTQ_STREAM(NPC) stream_tiles<VEC, kPartials, kMultiSeg, NPC, kFused, WT>(p, e, t0, t1, sb, len, npc, plist, wrow, codes, ds, l, rw, wave)
                 // one or two pairs per expert (decode) without per-pair guards;
                 // more pairs keep the guarded loop, whose guards also stop the
                 // scheduler from interleaving all 8 blocks (which would need
@@ -519,27 +565,44 @@ __global__ __launch_bounds__(kThreads, kWavesPerSimd) void moe_gemv_kernel(GemvP
     }
 }
 
-template <int VEC, bool kBucketed, bool kPartials>
+template <int VEC, bool kBucketed, bool kPartials, int WT>
 int launch_seg(bool multi, const GemvParams& gp, size_t lds, hipStream_t s)
 {
-    if constexpr (!kPartials) {   // a fused activation needs whole rows (one K segment)
+    if constexpr (!kPartials && WT == FTQ_W_Q4_0) {   // a fused activation needs whole rows (one K segment)
         if (gp.act != 0)
-            return launch("moe_gemv_kernel<act>", moe_gemv_kernel<VEC, kBucketed, false, false, true>, gp.grid, kThreads,
-                          lds, s, gp);
+            return launch("moe_gemv_kernel<act>", moe_gemv_kernel<VEC, kBucketed, false, false, true, WT>, gp.grid,
+                          kThreads, lds, s, gp);
     }
     if (multi)
-        return launch("moe_gemv_kernel", moe_gemv_kernel<VEC, kBucketed, kPartials, true, false>, gp.grid, kThreads, lds, s, gp);
-    return launch("moe_gemv_kernel", moe_gemv_kernel<VEC, kBucketed, kPartials, false, false>, gp.grid, kThreads, lds, s, gp);
+        return launch("moe_gemv_kernel", moe_gemv_kernel<VEC, kBucketed, kPartials, true, false, WT>, gp.grid, kThreads,
+                      lds, s, gp);
+    return launch("moe_gemv_kernel", moe_gemv_kernel<VEC, kBucketed, kPartials, false, false, WT>, gp.grid, kThreads,
+                  lds, s, gp);
 }
 
-template <bool kBucketed, bool kPartials>
+template <bool kBucketed, bool kPartials, int WT>
 int launch_gemv(int vec, const GemvParams& gp, size_t lds, hipStream_t s)
 {
     const bool multi = gp.seg < gp.nb;
     switch (vec) {
-    case 16: return launch_seg<16, kBucketed, kPartials>(multi, gp, lds, s);
-    case 4: return launch_seg<4, kBucketed, kPartials>(multi, gp, lds, s);
-    default: return launch_seg<2, kBucketed, kPartials>(multi, gp, lds, s);
+    case 16: return launch_seg<16, kBucketed, kPartials, WT>(multi, gp, lds, s);
+    case 4: return launch_seg<4, kBucketed, kPartials, WT>(multi, gp, lds, s);
+    default:
+        if constexpr (WT == FTQ_W_Q4_0) return launch_seg<2, kBucketed, kPartials, WT>(multi, gp, lds, s);
+        set_error("internal: 2-byte weight loads are built for Q4_0 only");
+        return FTQ_ERR_UNSUPPORTED;
+    }
+}
+
+template <bool kBucketed, bool kPartials>
+int launch_wtype(int wtype, int vec, const GemvParams& gp, size_t lds, hipStream_t s)
+{
+    switch (wtype) {
+    case FTQ_W_Q4_1: return launch_gemv<kBucketed, kPartials, FTQ_W_Q4_1>(vec, gp, lds, s);
+    case FTQ_W_Q5_0: return launch_gemv<kBucketed, kPartials, FTQ_W_Q5_0>(vec, gp, lds, s);
+    case FTQ_W_Q5_1: return launch_gemv<kBucketed, kPartials, FTQ_W_Q5_1>(vec, gp, lds, s);
+    case FTQ_W_Q8_0: return launch_gemv<kBucketed, kPartials, FTQ_W_Q8_0>(vec, gp, lds, s);
+    default: return launch_gemv<kBucketed, kPartials, FTQ_W_Q4_0>(vec, gp, lds, s);
     }
 }
 
@@ -581,7 +644,7 @@ int run_gemv(const MoeArgs& m, const BucketPlan* plan, const void* ws, hipStream
     // K segment: whole rows when the staged activations fit next to the weight
     // buffers with kTargetWGPerCU workgroups per CU, else the largest multiple
     // of a step (128 blocks) that fits, so that every step is full
-    const int64_t fixed = lds_layout(m.E, 0, 0, gp.list_cap).bytes;
+    const int64_t fixed = lds_layout(m.wtype, m.E, 0, 0, gp.list_cap).bytes;
     const int64_t budget = std::max<int64_t>(kLdsPerCU / kTargetWGPerCU - fixed, 0);
     auto act_bytes = [&](int64_t seg) { return code_bytes(seg, gp.pc_cap) + ent_bytes(seg, gp.pc_cap); };
     if (m.act) {
@@ -601,23 +664,30 @@ int run_gemv(const MoeArgs& m, const BucketPlan* plan, const void* ws, hipStream
         while (seg + kStepBlocks < gp.nb && act_bytes(seg + kStepBlocks) <= budget) seg += kStepBlocks;
         gp.seg = seg;
     }
-    const int64_t lds = lds_layout(m.E, gp.seg, gp.pc_cap, gp.list_cap).bytes;
+    const int64_t lds = lds_layout(m.wtype, m.E, gp.seg, gp.pc_cap, gp.list_cap).bytes;
     // grid: the workgroups that are resident at once (LDS and registers permitting)
     const int64_t by_lds = std::max<int64_t>(1, kLdsPerCU / lds);
     const int64_t per_cu = std::min<int64_t>(by_lds, kWavesPerSimd * 4 / kWaves);
     const int64_t max_items = (std::min<int64_t>(m.E, gp.pairs) + 1) * gp.row_tiles;
     gp.grid = std::max<int64_t>(1, std::min<int64_t>((int64_t)lim.cu_count * per_cu, max_items));
-    // widest load unit that keeps every step aligned
+    // widest load unit that keeps every step aligned: 16 bytes when K/32 is a
+    // multiple of 8 (whole lane groups), 4 when every block boundary that a
+    // step starts or ends on is 4-byte aligned, else 2 (Q4_0 only)
+    const int64_t bb = w_block_bytes(m.wtype);
     const uintptr_t wa = reinterpret_cast<uintptr_t>(m.w);
     int vec = 2;
     if (gp.nb % 8 == 0 && wa % 16 == 0) vec = 16;
-    else if (gp.nb % 2 == 0 && wa % 4 == 0) vec = 4;
-    if (bucketed) {
-        return m.partials ? launch_gemv<true, true>(vec, gp, (size_t)lds, s)
-                          : launch_gemv<true, false>(vec, gp, (size_t)lds, s);
+    else if ((bb % 4 == 0 || gp.nb % 2 == 0) && wa % 4 == 0) vec = 4;
+    if (vec == 2 && m.wtype != FTQ_W_Q4_0) {
+        set_error("weight type %d needs 4-byte aligned weight rows (K/32 even, or 4-byte blocks)", m.wtype);
+        return FTQ_ERR_UNSUPPORTED;
     }
-    return m.partials ? launch_gemv<false, true>(vec, gp, (size_t)lds, s)
-                      : launch_gemv<false, false>(vec, gp, (size_t)lds, s);
+    if (bucketed) {
+        return m.partials ? launch_wtype<true, true>(m.wtype, vec, gp, (size_t)lds, s)
+                          : launch_wtype<true, false>(m.wtype, vec, gp, (size_t)lds, s);
+    }
+    return m.partials ? launch_wtype<false, true>(m.wtype, vec, gp, (size_t)lds, s)
+                      : launch_wtype<false, false>(m.wtype, vec, gp, (size_t)lds, s);
 }
 
 }  // namespace ftq

@@ -18,6 +18,9 @@ LIB_PATH = os.path.join(_PKG, "libftq.so")
 OK, ERR_INVALID_ARG, ERR_WORKSPACE, ERR_LAUNCH, ERR_UNSUPPORTED, ERR_HIP = range(6)
 PATH_AUTO, PATH_GEMV, PATH_GROUPED = 0, 1, 2
 ACT_SILU, ACT_GELU_TANH = 1, 2
+# weight block types (GGUF type ids) and their block bytes
+W_Q4_0, W_Q4_1, W_Q5_0, W_Q5_1, W_Q8_0 = 2, 3, 6, 7, 8
+W_BLOCK_BYTES = {W_Q4_0: 18, W_Q4_1: 20, W_Q5_0: 22, W_Q5_1: 24, W_Q8_0: 34}
 QK, Q4_0_BYTES, Q8_1_BYTES = 32, 18, 36
 
 EXPORTS = (
@@ -26,6 +29,7 @@ EXPORTS = (
     "ftq_moe_pairs_workspace_bytes", "ftq_moe_q4_0_q8_1_pairs", "ftq_moe_q4_0_q8_1_pairs_routed",
     "ftq_moe_q4_0_q8_1_pairs_partials", "ftq_moe_combine_topk",
     "ftq_moe_q4_0_q8_1_act", "ftq_moe_q4_0_q8_1_act_routed",
+    "ftq_moe_gguf_q8_1", "ftq_moe_gguf_q8_1_partials",
     "ftq_last_error", "ftq_version",
     "ftq_debug_force_block_threads",
 )
@@ -76,6 +80,10 @@ def lib() -> ctypes.CDLL:
         f.argtypes = [P, P, P, P, I64, I64, I64, I64, I64, I32, P, ctypes.c_size_t, I32, P]
         f.restype = I32
     L.ftq_moe_q4_0_q8_1_partials.restype = I32
+    for name in ("ftq_moe_gguf_q8_1", "ftq_moe_gguf_q8_1_partials"):
+        f = getattr(L, name)
+        f.argtypes = [P, I32, P, P, P, I64, I64, I64, I64, I64, I32, P, SZ, I32, P]
+        f.restype = I32
     L.ftq_last_error.restype = ctypes.c_char_p
     L.ftq_version.restype = ctypes.c_char_p
     L.ftq_debug_force_block_threads.argtypes = [I32]
@@ -299,6 +307,51 @@ def moe_act_routed(w: torch.Tensor, a: torch.Tensor, topk_ids: torch.Tensor, E: 
         _dev(w, "w", torch.uint8), _dev(a, "a", torch.uint8), _dev(topk_ids, "topk_ids", torch.int32),
         _dev(out, "out", torch.float32), E, N, K, T, top_k, act,
         workspace.data_ptr() if workspace is not None else None, ws_n, path, _stream(stream)))
+    return out
+
+
+# ---- the other GGUF weight block types (GEMV path) ---------------------------
+
+def _gguf_args(w, wtype, a, topk_ids, E, N, K, per_pair):
+    T, top_k = topk_ids.shape
+    nb = K // QK
+    if wtype not in W_BLOCK_BYTES:
+        raise ValueError(f"unknown weight type {wtype}")
+    if w.numel() != E * N * nb * W_BLOCK_BYTES[wtype]:
+        raise ValueError("w must hold E*N*(K/32) blocks of the weight type")
+    rows = T * top_k if per_pair else T
+    if a.numel() != rows * nb * Q8_1_BYTES:
+        raise ValueError(f"a must hold {'T*top_k' if per_pair else 'T'}*(K/32) Q8_1 blocks")
+    return T, top_k
+
+
+def moe_gguf(w: torch.Tensor, wtype: int, a: torch.Tensor, topk_ids: torch.Tensor, E: int, N: int, K: int,
+             per_pair: bool = False, path: int = PATH_AUTO, out: torch.Tensor | None = None,
+             workspace: torch.Tensor | None = None, stream=None) -> torch.Tensor:
+    """Matmul with weights of GGUF type `wtype` (W_*): fp32 out [T*top_k, N]."""
+    T, top_k = _gguf_args(w, wtype, a, topk_ids, E, N, K, per_pair)
+    if out is None:
+        out = torch.empty((T * top_k, N), dtype=torch.float32, device=a.device)
+    need = workspace_bytes(E, N, K, T, top_k, PATH_GEMV if wtype != W_Q4_0 else path)
+    ws, ws_n = _workspace(workspace, need, a.device)
+    _check(lib().ftq_moe_gguf_q8_1(
+        _dev(w, "w", torch.uint8), wtype, _dev(a, "a", torch.uint8), _dev(topk_ids, "topk_ids", torch.int32),
+        _dev(out, "out", torch.float32), E, N, K, T, top_k, int(per_pair),
+        ws.data_ptr() if ws is not None else None, ws_n, path, _stream(stream)))
+    return out
+
+
+def moe_gguf_partials(w: torch.Tensor, wtype: int, a: torch.Tensor, topk_ids: torch.Tensor, E: int, N: int, K: int,
+                      per_pair: bool = False, path: int = PATH_AUTO, stream=None) -> torch.Tensor:
+    """Integer parts sum((q - z) * q8), int32 [T*top_k, N, K/32]."""
+    T, top_k = _gguf_args(w, wtype, a, topk_ids, E, N, K, per_pair)
+    out = torch.empty((T * top_k, N, K // QK), dtype=torch.int32, device=a.device)
+    need = workspace_bytes(E, N, K, T, top_k, PATH_GEMV if wtype != W_Q4_0 else path)
+    ws, ws_n = _workspace(None, need, a.device)
+    _check(lib().ftq_moe_gguf_q8_1_partials(
+        _dev(w, "w", torch.uint8), wtype, _dev(a, "a", torch.uint8), _dev(topk_ids, "topk_ids", torch.int32),
+        _dev(out, "partials", torch.int32), E, N, K, T, top_k, int(per_pair),
+        ws.data_ptr() if ws is not None else None, ws_n, path, _stream(stream)))
     return out
 
 

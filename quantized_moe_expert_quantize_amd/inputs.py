@@ -15,7 +15,10 @@ synthetic tensors with the same shapes stand in for them):
     weight (r+1)^-s, k distinct by successive weighted sampling without
     replacement (Gumbel-top-k);
   * gates fp32 [T, top_k]: iid U(0.05, 1) per slot, scaled so each token's
-    row sums to about one (routing weights after a top-k softmax).
+    row sums to about one (routing weights after a top-k softmax);
+  * gguf_blocks: uniformly random code bytes with fp16 scales ~ U(1e-3, 2e-3)
+    (and offsets ~ U(-0.03, -0.01)) in the GGUF block layouts, for timing
+    the other weight types without a quantizer (tensor id 4).
 Shapes of the pages' workloads: FreeToken PR #185 "Performance" (nrows=1408,
 hidden=2816, top_k=8, 128 experts) and mlxcel PR #652 "Summary"
 (qwen3-30b-a3b at 8192 tokens, mixtral-8x7b at 32768 tokens).
@@ -24,7 +27,7 @@ from __future__ import annotations
 
 import numpy as np
 
-WEIGHTS, ACTIVATIONS, ROUTING, GATES = 0, 1, 2, 3
+WEIGHTS, ACTIVATIONS, ROUTING, GATES, BLOCKS = 0, 1, 2, 3, 4
 
 
 def _rng(seed: int, tensor_id: int) -> np.random.Generator:
@@ -62,6 +65,20 @@ def routing(T: int, E: int, top_k: int, seed: int = 0, kind: str = "uniform",
     else:
         raise ValueError(f"unknown routing kind {kind!r}")
     return np.ascontiguousarray(ids, dtype=np.int32)
+
+
+def gguf_blocks(wtype: int, E: int, N: int, K: int, seed: int = 0) -> np.ndarray:
+    """uint8 [E, N, K/32 * block bytes] of random valid blocks of GGUF type
+    wtype (3 Q4_1, 6 Q5_0, 7 Q5_1, 8 Q8_0; scale fp16 at byte 0, offset fp16 at
+    byte 2 for Q4_1/Q5_1); every other byte uniformly random."""
+    size = {2: 18, 3: 20, 6: 22, 7: 24, 8: 34}[wtype]
+    g = _rng(seed, BLOCKS)
+    nblk = E * N * (K // 32)
+    b = g.integers(0, 256, (nblk, size), dtype=np.uint8)
+    b[:, 0:2] = g.uniform(1e-3, 2e-3, nblk).astype(np.float16).view(np.uint8).reshape(nblk, 2)
+    if wtype in (3, 7):
+        b[:, 2:4] = g.uniform(-0.03, -0.01, nblk).astype(np.float16).view(np.uint8).reshape(nblk, 2)
+    return b.reshape(E, N, K // 32 * size)
 
 
 def gates(T: int, top_k: int, seed: int = 0) -> np.ndarray:
