@@ -647,6 +647,10 @@ int run_gemv(const MoeArgs& m, const BucketPlan* plan, const void* ws, hipStream
     const int64_t fixed = lds_layout(m.wtype, m.E, 0, 0, gp.list_cap).bytes;
     const int64_t budget = std::max<int64_t>(kLdsPerCU / kTargetWGPerCU - fixed, 0);
     auto act_bytes = [&](int64_t seg) { return code_bytes(seg, gp.pc_cap) + ent_bytes(seg, gp.pc_cap); };
+    // fewer pairs per pass, down to the average per expert, rather than one
+    // workgroup per CU (larger weight blocks leave less room for the rows)
+    const int64_t avg_pairs = std::max<int64_t>(1, (gp.pairs + m.E - 1) / m.E);
+    while (gp.pc_cap > avg_pairs && act_bytes(gp.nb) > budget) --gp.pc_cap;
     if (m.act) {
         // the activation is applied once a row's sum is complete: stage whole
         // rows, with fewer pairs per pass if need be
