@@ -142,7 +142,7 @@ def main() -> None:
     ap.add_argument("--wtype", choices=sorted(WTYPES), default="q4_0",
                     help="weight block type (not q4_0: random valid blocks, GEMV path, plain layers only)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--cpu-sample-tokens", type=int, default=2048)
+    ap.add_argument("--cpu-sample-tokens", type=int, default=8192, help="tokens the CPU oracle runs (10-30 s on the box)")
     ap.add_argument("--summarize-pmc", metavar="DIR")
     ap.add_argument("--pmc-kernel", default=DOMINANT, help="kernel whose counters --summarize-pmc reports")
     args = ap.parse_args()
