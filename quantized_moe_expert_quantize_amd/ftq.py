@@ -120,12 +120,20 @@ def _dev(t: torch.Tensor, name: str, dtype=None):
     return t.data_ptr()
 
 
+def _out(out: torch.Tensor, numel: int, name: str, dtype):
+    """A caller's output buffer must hold exactly the elements the call writes."""
+    if out.numel() != numel:
+        raise ValueError(f"{name} must hold {numel} elements, got {out.numel()}")
+    return _dev(out, name, dtype)
+
+
 def quantize_q8_1(x: torch.Tensor, out: torch.Tensor | None = None, stream=None) -> torch.Tensor:
     """fp32 [T, K] -> uint8 [T, K/32*36] Q8_1 blocks."""
     T, K = x.shape
     if out is None:
         out = torch.empty((T, K // QK * Q8_1_BYTES), dtype=torch.uint8, device=x.device)
-    _check(lib().ftq_quantize_q8_1(_dev(x, "x", torch.float32), T, K, _dev(out, "out", torch.uint8), _stream(stream)))
+    _check(lib().ftq_quantize_q8_1(_dev(x, "x", torch.float32), T, K, _out(out, T * (K // QK) * Q8_1_BYTES, "out", torch.uint8),
+                                   _stream(stream)))
     return out
 
 
@@ -135,7 +143,8 @@ def quantize_q4_0(w: torch.Tensor, out: torch.Tensor | None = None, stream=None)
     rows = w.numel() // K if K else 0
     if out is None:
         out = torch.empty(tuple(w.shape[:-1]) + (K // QK * Q4_0_BYTES,), dtype=torch.uint8, device=w.device)
-    _check(lib().ftq_quantize_q4_0(_dev(w, "w", torch.float32), rows, K, _dev(out, "out", torch.uint8), _stream(stream)))
+    _check(lib().ftq_quantize_q4_0(_dev(w, "w", torch.float32), rows, K, _out(out, rows * (K // QK) * Q4_0_BYTES, "out", torch.uint8),
+                                   _stream(stream)))
     return out
 
 
@@ -185,7 +194,7 @@ def moe(w: torch.Tensor, a: torch.Tensor, topk_ids: torch.Tensor, E: int, N: int
     ws, ws_n = _workspace(workspace, need, a.device)
     _check(lib().ftq_moe_q4_0_q8_1(
         _dev(w, "w", torch.uint8), _dev(a, "a", torch.uint8), _dev(topk_ids, "topk_ids", torch.int32),
-        _dev(out, "out", torch.float32), E, N, K, T, top_k,
+        _out(out, T * top_k * N, "out", torch.float32), E, N, K, T, top_k,
         ws.data_ptr() if ws is not None else None, ws_n, path, _stream(stream)))
     return out
 
@@ -207,7 +216,7 @@ def moe_routed(w: torch.Tensor, a: torch.Tensor, topk_ids: torch.Tensor, E: int,
     ws_n = workspace.numel() if workspace is not None else 0
     _check(lib().ftq_moe_q4_0_q8_1_routed(
         _dev(w, "w", torch.uint8), _dev(a, "a", torch.uint8), _dev(topk_ids, "topk_ids", torch.int32),
-        _dev(out, "out", torch.float32), E, N, K, T, top_k,
+        _out(out, T * top_k * N, "out", torch.float32), E, N, K, T, top_k,
         workspace.data_ptr() if workspace is not None else None, ws_n, path, _stream(stream)))
     return out
 
@@ -247,7 +256,7 @@ def moe_pairs(w: torch.Tensor, a_pairs: torch.Tensor, topk_ids: torch.Tensor, E:
     ws, ws_n = _workspace(workspace, need, a_pairs.device)
     _check(lib().ftq_moe_q4_0_q8_1_pairs(
         _dev(w, "w", torch.uint8), _dev(a_pairs, "a_pairs", torch.uint8), _dev(topk_ids, "topk_ids", torch.int32),
-        _dev(out, "out", torch.float32), E, N, K, T, top_k,
+        _out(out, T * top_k * N, "out", torch.float32), E, N, K, T, top_k,
         ws.data_ptr() if ws is not None else None, ws_n, path, _stream(stream)))
     return out
 
@@ -260,7 +269,7 @@ def moe_pairs_routed(w: torch.Tensor, a_pairs: torch.Tensor, topk_ids: torch.Ten
     ws_n = workspace.numel() if workspace is not None else 0
     _check(lib().ftq_moe_q4_0_q8_1_pairs_routed(
         _dev(w, "w", torch.uint8), _dev(a_pairs, "a_pairs", torch.uint8), _dev(topk_ids, "topk_ids", torch.int32),
-        _dev(out, "out", torch.float32), E, N, K, T, top_k,
+        _out(out, T * top_k * N, "out", torch.float32), E, N, K, T, top_k,
         workspace.data_ptr() if workspace is not None else None, ws_n, path, _stream(stream)))
     return out
 
@@ -292,7 +301,7 @@ def moe_act(w: torch.Tensor, a: torch.Tensor, topk_ids: torch.Tensor, E: int, N:
     ws, ws_n = _workspace(workspace, need, a.device)
     _check(lib().ftq_moe_q4_0_q8_1_act(
         _dev(w, "w", torch.uint8), _dev(a, "a", torch.uint8), _dev(topk_ids, "topk_ids", torch.int32),
-        _dev(out, "out", torch.float32), E, N, K, T, top_k, act,
+        _out(out, T * top_k * (N // 2), "out", torch.float32), E, N, K, T, top_k, act,
         ws.data_ptr() if ws is not None else None, ws_n, path, _stream(stream)))
     return out
 
@@ -305,7 +314,7 @@ def moe_act_routed(w: torch.Tensor, a: torch.Tensor, topk_ids: torch.Tensor, E: 
     ws_n = workspace.numel() if workspace is not None else 0
     _check(lib().ftq_moe_q4_0_q8_1_act_routed(
         _dev(w, "w", torch.uint8), _dev(a, "a", torch.uint8), _dev(topk_ids, "topk_ids", torch.int32),
-        _dev(out, "out", torch.float32), E, N, K, T, top_k, act,
+        _out(out, T * top_k * (N // 2), "out", torch.float32), E, N, K, T, top_k, act,
         workspace.data_ptr() if workspace is not None else None, ws_n, path, _stream(stream)))
     return out
 
@@ -336,7 +345,7 @@ def moe_gguf(w: torch.Tensor, wtype: int, a: torch.Tensor, topk_ids: torch.Tenso
     ws, ws_n = _workspace(workspace, need, a.device)
     _check(lib().ftq_moe_gguf_q8_1(
         _dev(w, "w", torch.uint8), wtype, _dev(a, "a", torch.uint8), _dev(topk_ids, "topk_ids", torch.int32),
-        _dev(out, "out", torch.float32), E, N, K, T, top_k, int(per_pair),
+        _out(out, T * top_k * N, "out", torch.float32), E, N, K, T, top_k, int(per_pair),
         ws.data_ptr() if ws is not None else None, ws_n, path, _stream(stream)))
     return out
 
@@ -364,5 +373,5 @@ def combine_topk(y: torch.Tensor, gates: torch.Tensor, out: torch.Tensor | None 
     if out is None:
         out = torch.empty((T, N), dtype=torch.float32, device=y.device)
     _check(lib().ftq_moe_combine_topk(_dev(y, "y", torch.float32), _dev(gates, "gates", torch.float32),
-                                      _dev(out, "out", torch.float32), T, top_k, N, _stream(stream)))
+                                      _out(out, T * N, "out", torch.float32), T, top_k, N, _stream(stream)))
     return out

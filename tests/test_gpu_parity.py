@@ -224,3 +224,19 @@ def test_wide_offset_variant_matches():
     env = dict(os.environ, FTQ_FORCE_WIDE="1")
     r = subprocess.run([sys.executable, "-c", code], cwd=root, env=env, capture_output=True, text=True, timeout=300)
     assert r.returncode == 0 and "wide ok" in r.stdout, r.stdout + r.stderr
+
+
+def test_binding_rejects_wrong_out_size():
+    """A caller's out buffer of the wrong size is refused before any launch."""
+    c = Case(4, 32, 64, 3, 2)
+    wq, aq, ids = c.gpu()
+    f32 = lambda *s: torch.empty(s, dtype=torch.float32, device="cuda")
+    with pytest.raises(ValueError, match="out must hold"):
+        ftq.moe(wq, aq, ids, 4, 32, 64, out=f32(5, 32))
+    with pytest.raises(ValueError, match="out must hold"):
+        ftq.moe_act(wq, aq, ids, 4, 32, 64, ftq.ACT_SILU, out=f32(6, 32))
+    with pytest.raises(ValueError, match="out must hold"):
+        ftq.quantize_q8_1(f32(3, 64), out=torch.empty(10, dtype=torch.uint8, device="cuda"))
+    with pytest.raises(ValueError, match="out must hold"):
+        ftq.combine_topk(f32(6, 8), f32(3, 2), out=f32(3, 7))
+    torch.cuda.synchronize()
