@@ -146,7 +146,6 @@ enum Phase { kRoute = 1, kMatmul = 2 };
 
 // act_per_pair: `a` holds one Q8_1 row per pair ([T*top_k][K/32]) instead of
 // one per token ([T][K/32]).
-int64_t act_rows_of(int64_t T, int64_t top_k, bool act_per_pair) { return act_per_pair ? T * top_k : T; }
 
 int moe_common(const void* w, const void* a, const int32_t* ids, float* out, int32_t* partials,
                int64_t E, int64_t N, int64_t K, int64_t T, int64_t top_k, void* ws, size_t ws_bytes,
@@ -187,10 +186,8 @@ int moe_common(const void* w, const void* a, const int32_t* ids, float* out, int
     bool bucketed = false;
     const BucketPlan plan = plan_for(rp, E, N, K, T, top_k, &bucketed);
     if (bucketed) {
-        // routing alone needs the bucket tables; the grouped matmul also stages activations
-        const int64_t need = plan.bytes + ((phases & kMatmul) && rp == FTQ_PATH_GROUPED
-                                               ? grouped_prep_bytes(act_rows_of(T, top_k, act_per_pair), K) : 0);
-        st = check_workspace(need, ws, ws_bytes);
+        // the workspace holds the bucket tables (both paths read the activations in place)
+        st = check_workspace(plan.bytes, ws, ws_bytes);
         if (st != FTQ_OK) return st;
         if (phases & kRoute) {
             st = run_bucket(ids, E, plan, ws, stream);
@@ -205,6 +202,7 @@ int moe_common(const void* w, const void* a, const int32_t* ids, float* out, int
 
 int64_t workspace_bytes(int64_t E, int64_t N, int64_t K, int64_t T, int64_t top_k, int path, bool act_per_pair)
 {
+    (void)act_per_pair;   // the workspace does not depend on how the activations are laid out
     clear_error();
     if (check_sizes(E, N, K, T, top_k) != FTQ_OK) return -1;
     const int rp = resolve_path(path, E, T, top_k);
@@ -213,7 +211,7 @@ int64_t workspace_bytes(int64_t E, int64_t N, int64_t K, int64_t T, int64_t top_
     bool bucketed = false;
     const BucketPlan plan = plan_for(rp, E, N, K, T, top_k, &bucketed);
     if (!bucketed) return 0;
-    return plan.bytes + (rp == FTQ_PATH_GROUPED ? grouped_prep_bytes(act_rows_of(T, top_k, act_per_pair), K) : 0);
+    return plan.bytes;
 }
 
 }  // namespace

@@ -135,11 +135,9 @@ __device__ __forceinline__ int64_t uniform(int64_t v)
     return (int64_t)(((uint64_t)hi << 32) | lo);
 }
 
-// Grouped MFMA path.  Its workspace is the bucket plan's bytes followed by
-// grouped_prep_bytes(activation rows, K) of per-call activation staging.
+// Grouped MFMA path.  Its workspace is the bucket plan's bytes.
 int run_grouped(const MoeArgs& m, const BucketPlan& plan, void* ws, hipStream_t s);
 int64_t grouped_tile_m(const MoeArgs& m);
-int64_t grouped_prep_bytes(int64_t act_rows, int64_t K);
 
 // Top-k weighted combine of per-pair rows into per-token rows.
 int run_combine_topk(const float* y, const float* gates, float* out, int64_t T, int64_t top_k, int64_t N,

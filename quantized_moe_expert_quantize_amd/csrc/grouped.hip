@@ -26,15 +26,18 @@
 // The per-element arithmetic does not depend on where a pair sits in a tile,
 // so results are batch invariant.
 //
-// Operands.  The activations are converted once per call by
-// prep_activations_kernel into fp16 codes (64 B per block) plus fp16 scales;
-// the weight nibbles are unpacked to fp16 while a tile is staged into LDS, in a
-// block-internal k order chosen so that each 32-bit word of nibbles yields
+// Operands.  The Q8_1 activation blocks are read as they are (36 bytes: fp16
+// scale, fp16 sum, 32 int8 codes) and their codes widened to fp16 while a tile
+// is staged into LDS; the weight nibbles are unpacked to fp16 at the same step,
+// in a block-internal k order chosen so that each 32-bit word of nibbles yields
 // four packed fp16 pairs with one mask-or and one packed add each; the
 // activation codes are written in that same order, so the dot products match.
+// The two blocks of a pass that belong to one row are loaded by adjacent lanes.
 // Tiles are double buffered in LDS (loads for block pair s+1 are in flight while
 // block pair s is multiplied); the global loads are buffer loads whose per-lane
 // offsets are fixed for a tile and whose per-pass advance is a scalar offset.
+// Within a pass the matrix products of one 32x32 sub-tile are issued before the
+// scale-accumulate of the previous one, so matrix cores and vector ALUs overlap.
 // In ragged tiles a wave whose rows hold no pair skips its MFMA work.
 //
 // Fused gated activation (kFused): a tile's 128 weight rows are the gate rows
@@ -60,7 +63,7 @@ typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 constexpr int kThreads = 256;
 constexpr int kBN = 128;          // weight rows per tile
 constexpr int kKB = 2;            // quantisation blocks per staged pass
-constexpr int kBlockF16 = 64;     // bytes of one block's 32 fp16 codes
+constexpr int kBlockF16 = 64;     // LDS bytes of one block's 32 fp16 codes
 constexpr int kRowBytes = kKB * kBlockF16;   // LDS bytes per staged row (16-byte chunks, swizzled)
 constexpr int kXcds = 8;
 constexpr int kGroupM = 4;
@@ -86,8 +89,7 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, in
 
 struct GroupedParams {
     const uint8_t* w;
-    const uint8_t* a16;       // [T][nb][64 B] fp16 codes in the block-internal order
-    const uint16_t* d8;       // [T][nb] fp16 scale bits
+    const uint8_t* a;         // Q8_1 activation rows [act rows][nb][36 B]
     float* out;
     int32_t* partials;
     const int32_t* offsets;   // [E+2]
@@ -95,8 +97,7 @@ struct GroupedParams {
     const int32_t* sorted;
     int64_t E, N, nb, top_k, nbuckets, n_tiles_n, max_mt;
     int64_t act_div;          // activation row of pair p: p / act_div
-    int32_t a16_range;        // buffer ranges in bytes (32-bit unsigned counts): a16, d8
-    int32_t d8_range;         // (narrow variant only: a16 below 4 GiB)
+    int32_t a_range;          // bytes of a (32-bit unsigned count; narrow variant only: below 4 GiB)
     int32_t wtile_range;      // bytes of kBN weight rows (fused: of one expert)
     int64_t half;             // fused: N/2 output columns
     int act;                  // fused: FTQ_ACT_*
@@ -151,52 +152,21 @@ __device__ __forceinline__ void nibbles_to_f16(uint32_t x, uint32_t mask, uint32
     o[3] = __builtin_bit_cast(uint32_t, __builtin_bit_cast(h2, t3) + bias);
 }
 
-// ---- per-call activation preparation ------------------------------------------
-
-// Blocks per staged row, padded to whole passes: the padding block has zero
-// codes and zero scale, so the tile loads never need a bounds clamp.
-__host__ __device__ constexpr int64_t padded_blocks(int64_t nb) { return (nb + kKB - 1) / kKB * kKB; }
-
-// One lane per (token, padded block): 32 int8 codes -> 32 fp16 codes in the
-// order of nibbles_to_f16 (pairs (4j, 4j+2), (4j+1, 4j+3), (16+4j, 16+4j+2),
-// (16+4j+1, 16+4j+3) for j = 0..3), and the fp16 scale.
-__global__ __launch_bounds__(kThreads) void prep_activations_kernel(
-    const uint8_t* __restrict__ a, int64_t T, int64_t nb, uint8_t* __restrict__ a16, uint16_t* __restrict__ d8)
+// Two packed fp16 pairs from one word of four int8 codes: (byte 0, byte 2) and
+// (byte 1, byte 3).  Each code q is offset to the byte q + 128, placed under the
+// exponent byte 0x64 (the fp16 1024 + byte) and shifted back by 1152: exact.
+__device__ __forceinline__ void int8_pairs_to_f16(uint32_t x, uint32_t magic, uint32_t& even, uint32_t& odd)
 {
-    const int64_t nbp = padded_blocks(nb);
-    const int64_t nblocks = T * nbp;
-    const int64_t stride = (int64_t)gridDim.x * kThreads;
-    for (int64_t i = (int64_t)blockIdx.x * kThreads + threadIdx.x; i < nblocks; i += stride) {
-        const int64_t t = i / nbp, b = i - t * nbp;
-        u32x4* dst = reinterpret_cast<u32x4*>(a16 + i * kBlockF16);
-        if (b >= nb) {
-#pragma unroll
-            for (int k = 0; k < 4; ++k) dst[k] = u32x4{0, 0, 0, 0};
-            d8[i] = 0;
-            continue;
-        }
-        const uint32_t* src = reinterpret_cast<const uint32_t*>(a + (t * nb + b) * kQ8Bytes);
-        uint32_t c[8];
-        const uint32_t head = src[0];
-#pragma unroll
-        for (int k = 0; k < 8; ++k) c[k] = src[1 + k];
-        auto f = [](uint32_t word, int byte) -> uint32_t {
-            const _Float16 h = (_Float16)(int)(int8_t)(word >> (8 * byte));   // exact
-            return (uint32_t)__builtin_bit_cast(uint16_t, h);
-        };
-        uint32_t o[16];
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-            o[4 * j + 0] = f(c[j], 0) | (f(c[j], 2) << 16);
-            o[4 * j + 1] = f(c[j], 1) | (f(c[j], 3) << 16);
-            o[4 * j + 2] = f(c[4 + j], 0) | (f(c[4 + j], 2) << 16);
-            o[4 * j + 3] = f(c[4 + j], 1) | (f(c[4 + j], 3) << 16);
-        }
-#pragma unroll
-        for (int k = 0; k < 4; ++k) dst[k] = u32x4{o[4 * k], o[4 * k + 1], o[4 * k + 2], o[4 * k + 3]};
-        d8[i] = (uint16_t)(head & 0xffffu);
-    }
+    const h2 bias = {(_Float16)-1152.0f, (_Float16)-1152.0f};
+    const uint32_t u = x ^ 0x80808080u;
+    even = __builtin_bit_cast(uint32_t, __builtin_bit_cast(h2, __builtin_amdgcn_perm(magic, u, 0x04020400u)) + bias);
+    odd = __builtin_bit_cast(uint32_t, __builtin_bit_cast(h2, __builtin_amdgcn_perm(magic, u, 0x04030401u)) + bias);
 }
+
+// Blocks per row, padded to whole passes.  A block past K/32 (odd K/32, last
+// pass only) is read from block K/32-1 with scale 0 on both sides, so it adds
+// fma(P, 0, acc) = acc exactly.
+__host__ __device__ constexpr int64_t padded_blocks(int64_t nb) { return (nb + kKB - 1) / kKB * kKB; }
 
 // ---- the tile kernel ------------------------------------------------------------
 
@@ -229,8 +199,9 @@ __global__ __launch_bounds__(Shape<BM>::kThreads, Shape<BM>::kWavesPerSimd) void
 
     uint32_t nib_mask = 0x000f000fu, nib_magic = 0x64006400u;
     __asm__ volatile("" : "+v"(nib_mask), "+v"(nib_magic));
-    const __amdgpu_buffer_rsrc_t ars = make_rsrc(p.a16, p.a16_range);
-    const __amdgpu_buffer_rsrc_t drs = make_rsrc(p.d8, p.d8_range);
+    const __amdgpu_buffer_rsrc_t ars = make_rsrc(p.a, p.a_range);
+    uint32_t i8_magic = 0x64646464u;
+    __asm__ volatile("" : "+v"(i8_magic));
 
     for (int64_t w = blockIdx.x; w < work; w += gridDim.x) {
         const int64_t L = direct ? xcd_remap(w, work) : w;
@@ -283,34 +254,25 @@ __global__ __launch_bounds__(Shape<BM>::kThreads, Shape<BM>::kWavesPerSimd) void
         // Every global address is a per-thread offset fixed for the tile plus
         // a workgroup-uniform offset that advances by a constant per pass (the
         // scalar offset of a buffer load).  Rows past the tile (A) or past N
-        // (B) read valid memory and are never stored.  The activations are
-        // padded to whole passes; a weight block past K/32 (odd K/32, last pass
-        // only) is read from block K/32-1 with scale 0, so it adds
-        // fma(P, 0, acc) = acc exactly.
-        // A: BM rows x kKB blocks x 64 B = BM*8 units of 16 B (unit c of a row: block c/4, piece c%4)
-        constexpr int kAUnits = BM * kKB * 4;
-        constexpr int kAPer = (kAUnits + kThreads - 1) / kThreads;
-        static_assert(kAUnits % kThreads == 0, "whole A units per thread");
+        // (B) read valid memory and are never stored.  A block past K/32 (odd
+        // K/32, last pass only) is read from block K/32-1 on both sides with
+        // scale 0, so it adds fma(P, 0, acc) = acc exactly.
+        // A: one Q8_1 block (36 B: fp16 d, fp16 s, 32 int8 codes) of one row per
+        // thread of the first BM * kKB threads, the two blocks of a row in
+        // adjacent lanes
+        static_assert(BM * kKB <= kThreads, "one activation block per thread");
+        const bool a_thread = tid < BM * kKB;
+        const int am = (tid / kKB) % BM, ablk = tid % kKB;
         using AOff = typename std::conditional<kWide, int64_t, uint32_t>::type;
-        AOff a_off_g[kAPer];
-        int a_lds[kAPer];
+        const AOff a_off_g = (AOff)(((int64_t)sm.row_tok[am < rows ? am : 0] * nb + ablk) * kQ8Bytes);
+        int a_lds[4];
 #pragma unroll
-        for (int i = 0; i < kAPer; ++i) {
-            const int u = tid + i * kThreads;
-            const int m = u >> 3, c = u & 7;
-            a_off_g[i] = (AOff)(((int64_t)sm.row_tok[m < rows ? m : 0] * nbp + (c >> 2)) * kBlockF16 + (c & 3) * 16);
-            a_lds[i] = lds_chunk(m, c);
-        }
-        // A scales: thread < BM*kKB owns (row tid % BM, block tid / BM); the
-        // others load a valid scale and do not store it
-        const int d_m = tid % BM, d_blk = min(tid / BM, kKB - 1);
-        const bool d_thread = tid < BM * kKB;
-        const uint32_t d_off = (uint32_t)(((int64_t)sm.row_tok[d_m < rows ? d_m : 0] * nbp + d_blk) * 2);
+        for (int j = 0; j < 4; ++j) a_lds[j] = lds_chunk(am, ablk * 4 + j);
         // B: one block (18 B) of one weight row per thread of the first
         // kBN * kKB threads; bh is uniform per wave
         static_assert(kBN * kKB <= kThreads, "one weight block per thread");
         const bool b_thread = tid < kBN * kKB;
-        const int bn = tid % kBN, bh = uniform((int32_t)((tid / kBN) % kKB));
+        const int bn = tid / kKB, bh = tid % kKB;   // the blocks of one row in adjacent lanes
         // uniform per tile: the tile's first weight row, or (fused) the expert's
         const uint8_t* wtile = p.w + (uniform(bucket) * p.N + (kFused ? 0 : uniform(n0))) * nb * kQ4Bytes;
         const __amdgpu_buffer_rsrc_t wrs = make_rsrc(wtile, p.wtile_range);
@@ -326,23 +288,28 @@ __global__ __launch_bounds__(Shape<BM>::kThreads, Shape<BM>::kWavesPerSimd) void
 #pragma unroll
         for (int i = 0; i < 4; ++i) b_lds[i] = lds_chunk(bn, bh * 4 + i);
 
-        u32x4 ra[kAPer];
+        u32x4 ra0, ra1;
+        uint32_t ra2;
+        bool ra_ok;
         uint32_t rb[5];
-        uint32_t rd8 = 0;
         bool rb_ok;
 
         auto issue = [&](int64_t kb0) {
-            if constexpr (kWide) {
-                const uint8_t* abase = p.a16 + kb0 * kBlockF16;
-#pragma unroll
-                for (int i = 0; i < kAPer; ++i) ra[i] = *reinterpret_cast<const u32x4*>(abase + a_off_g[i]);
-                rd8 = p.d8[kb0 + d_off / 2];
-            } else {
-                const int soff = uniform((int32_t)(kb0 * kBlockF16));
-#pragma unroll
-                for (int i = 0; i < kAPer; ++i)
-                    ra[i] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(ars, a_off_g[i], soff, 0));
-                rd8 = __builtin_amdgcn_raw_buffer_load_b16(drs, d_off, uniform((int32_t)(kb0 * 2)), 0);
+            ra_ok = kb0 + ablk < nb;
+            if (a_thread) {
+                const AOff voff = ra_ok ? a_off_g : a_off_g - kQ8Bytes;
+                if constexpr (kWide) {
+                    typedef u32x4 u32x4_a4 __attribute__((aligned(4)));
+                    const uint8_t* abase = p.a + kb0 * kQ8Bytes + voff;
+                    ra0 = *reinterpret_cast<const u32x4_a4*>(abase);
+                    ra1 = *reinterpret_cast<const u32x4_a4*>(abase + 16);
+                    ra2 = *reinterpret_cast<const uint32_t*>(abase + 32);
+                } else {
+                    const int soff = uniform((int32_t)(kb0 * kQ8Bytes));
+                    ra0 = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(ars, voff, soff, 0));
+                    ra1 = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(ars, voff + 16, soff, 0));
+                    ra2 = __builtin_amdgcn_raw_buffer_load_b32(ars, voff + 32, soff, 0);
+                }
             }
             // past K/32 only in the last pass of an odd K/32; uniform per wave
             rb_ok = kb0 + bh < nb;
@@ -364,23 +331,29 @@ __global__ __launch_bounds__(Shape<BM>::kThreads, Shape<BM>::kWavesPerSimd) void
             }
         };
         auto commit = [&](int buf) {
+            if (a_thread) {
+                // 32 int8 codes -> fp16 in the order of nibbles_to_f16: chunk j holds
+                // codes 4j..4j+3 (word j) and 16+4j..16+4j+3 (word 4+j)
+                const uint32_t cw[8] = {ra0.y, ra0.z, ra0.w, ra1.x, ra1.y, ra1.z, ra1.w, ra2};
 #pragma unroll
-            for (int i = 0; i < kAPer; ++i) *reinterpret_cast<u32x4*>(&sm.a[buf][a_lds[i]]) = ra[i];
-            if (d_thread) sm.as[buf][d_blk][d_m] = uint2{rd8 & 0xffffu, 0u};
+                for (int j = 0; j < 4; ++j) {
+                    uint32_t o[4];
+                    int8_pairs_to_f16(cw[j], i8_magic, o[0], o[1]);
+                    int8_pairs_to_f16(cw[4 + j], i8_magic, o[2], o[3]);
+                    *reinterpret_cast<u32x4*>(&sm.a[buf][a_lds[j]]) = u32x4{o[0], o[1], o[2], o[3]};
+                }
+                sm.as[buf][ablk][am] = uint2{ra_ok ? (ra0.x & 0xffffu) : 0u, 0u};
+            }
             if (!b_thread) return;
             // weight block -> 32 fp16 values (q - 8) and its scale
             uint32_t dbits, qs[4];
             if constexpr (VEC == 4) {
-                if (bh == 0) {
-                    dbits = rb[0] & 0xffffu;
-                    qs[0] = __builtin_amdgcn_alignbit(rb[1], rb[0], 16);
-                    qs[1] = __builtin_amdgcn_alignbit(rb[2], rb[1], 16);
-                    qs[2] = __builtin_amdgcn_alignbit(rb[3], rb[2], 16);
-                    qs[3] = __builtin_amdgcn_alignbit(rb[4], rb[3], 16);
-                } else {
-                    dbits = rb[0] >> 16;
-                    qs[0] = rb[1]; qs[1] = rb[2]; qs[2] = rb[3]; qs[3] = rb[4];
-                }
+                const bool first = bh == 0;
+                dbits = first ? (rb[0] & 0xffffu) : (rb[0] >> 16);
+                qs[0] = first ? __builtin_amdgcn_alignbit(rb[1], rb[0], 16) : rb[1];
+                qs[1] = first ? __builtin_amdgcn_alignbit(rb[2], rb[1], 16) : rb[2];
+                qs[2] = first ? __builtin_amdgcn_alignbit(rb[3], rb[2], 16) : rb[3];
+                qs[3] = first ? __builtin_amdgcn_alignbit(rb[4], rb[3], 16) : rb[4];
             } else {
                 dbits = rb[0];
                 qs[0] = rb[1]; qs[1] = rb[2]; qs[2] = rb[3]; qs[3] = rb[4];
@@ -426,29 +399,32 @@ __global__ __launch_bounds__(Shape<BM>::kThreads, Shape<BM>::kWavesPerSimd) void
         // One staged pass: kKB blocks from LDS buffer `buf`
         auto compute = [&](int buf, int64_t kb0) {
             if (!wave_rows) return;
+            v8h alo[kKB][S::SM], ahi[kKB][S::SM], blo[kKB][S::SN], bhi[kKB][S::SN];
+            v4h as_v[kKB][S::SM], bs_v[kKB][S::SN];
 #pragma unroll
             for (int blk = 0; blk < kKB; ++blk) {
-                v8h alo[S::SM], ahi[S::SM], blo[S::SN], bhi[S::SN];
-                v4h as_v[S::SM], bs_v[S::SN];
 #pragma unroll
                 for (int ii = 0; ii < S::SM; ++ii) {
-                    alo[ii] = *reinterpret_cast<const v8h*>(&sm.a[buf][frag_a[blk][0] + ii * 32 * kRowBytes]);
-                    ahi[ii] = *reinterpret_cast<const v8h*>(&sm.a[buf][frag_a[blk][1] + ii * 32 * kRowBytes]);
-                    as_v[ii] = __builtin_bit_cast(v4h, sm.as[buf][blk][as_row + ii * 32]);
+                    alo[blk][ii] = *reinterpret_cast<const v8h*>(&sm.a[buf][frag_a[blk][0] + ii * 32 * kRowBytes]);
+                    ahi[blk][ii] = *reinterpret_cast<const v8h*>(&sm.a[buf][frag_a[blk][1] + ii * 32 * kRowBytes]);
+                    as_v[blk][ii] = __builtin_bit_cast(v4h, sm.as[buf][blk][as_row + ii * 32]);
                 }
 #pragma unroll
                 for (int jj = 0; jj < S::SN; ++jj) {
-                    blo[jj] = *reinterpret_cast<const v8h*>(&sm.b[buf][frag_b[blk][0] + jj * 32 * kRowBytes]);
-                    bhi[jj] = *reinterpret_cast<const v8h*>(&sm.b[buf][frag_b[blk][1] + jj * 32 * kRowBytes]);
-                    bs_v[jj] = __builtin_bit_cast(v4h, sm.bs[buf][blk][bs_row[jj]]);
+                    blo[blk][jj] = *reinterpret_cast<const v8h*>(&sm.b[buf][frag_b[blk][0] + jj * 32 * kRowBytes]);
+                    bhi[blk][jj] = *reinterpret_cast<const v8h*>(&sm.b[buf][frag_b[blk][1] + jj * 32 * kRowBytes]);
+                    bs_v[blk][jj] = __builtin_bit_cast(v4h, sm.bs[buf][blk][bs_row[jj]]);
                 }
+            }
+            if constexpr (kPartials) {
 #pragma unroll
-                for (int i = 0; i < S::SM; ++i) {
+                for (int blk = 0; blk < kKB; ++blk)
 #pragma unroll
-                    for (int j = 0; j < S::SN; ++j) {
-                        v16f P = __builtin_amdgcn_mfma_f32_32x32x16_f16(alo[i], blo[j], v16f{}, 0, 0, 0);
-                        P = __builtin_amdgcn_mfma_f32_32x32x16_f16(ahi[i], bhi[j], P, 0, 0, 0);
-                        if constexpr (kPartials) {
+                    for (int i = 0; i < S::SM; ++i)
+#pragma unroll
+                        for (int j = 0; j < S::SN; ++j) {
+                            v16f P = __builtin_amdgcn_mfma_f32_32x32x16_f16(alo[blk][i], blo[blk][j], v16f{}, 0, 0, 0);
+                            P = __builtin_amdgcn_mfma_f32_32x32x16_f16(ahi[blk][i], bhi[blk][j], P, 0, 0, 0);
                             const int64_t n = n0 + (wn * S::SN + j) * 32 + l32;
                             const int64_t b = kb0 + blk;
 #pragma unroll
@@ -457,12 +433,35 @@ __global__ __launch_bounds__(Shape<BM>::kThreads, Shape<BM>::kWavesPerSimd) void
                                 if (m < rows && n < p.N && b < nb)
                                     p.partials[((int64_t)sm.row_pair[m] * p.N + n) * nb + b] = (int32_t)P[r];
                             }
-                        } else {
-                            const v16f Sc = __builtin_amdgcn_mfma_f32_32x32x8f16(as_v[i], bs_v[j], v16f{}, 0, 0, 0);
-#pragma unroll
-                            for (int r = 0; r < 16; ++r) acc[i][j][r] = __builtin_fmaf(P[r], Sc[r], acc[i][j][r]);
                         }
+            } else {
+                // products of step s+1 are issued before the FMAs of step s, so
+                // the matrix cores and the vector ALUs work at the same time
+                constexpr int kSub = S::SM * S::SN, kSteps = kKB * kSub;
+                v16f P[2], Sc[2];
+                auto mm = [&](int st) {
+                    const int blk = st / kSub, t = st % kSub, i = t / S::SN, j = t % S::SN;
+                    v16f q = __builtin_amdgcn_mfma_f32_32x32x16_f16(alo[blk][i], blo[blk][j], v16f{}, 0, 0, 0);
+                    P[st & 1] = __builtin_amdgcn_mfma_f32_32x32x16_f16(ahi[blk][i], bhi[blk][j], q, 0, 0, 0);
+                    Sc[st & 1] = __builtin_amdgcn_mfma_f32_32x32x8f16(as_v[blk][i], bs_v[blk][j], v16f{}, 0, 0, 0);
+                };
+                mm(0);
+#pragma unroll
+                for (int st = 0; st < kSteps; ++st) {
+                    if (st + 1 < kSteps) mm(st + 1);
+                    const int t = st % kSub, i = t / S::SN, j = t % S::SN;
+#pragma unroll
+                    for (int r = 0; r < 16; ++r) acc[i][j][r] = __builtin_fmaf(P[st & 1][r], Sc[st & 1][r], acc[i][j][r]);
+#if 1
+                    if (st + 1 < kSteps) {
+                        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+                        __builtin_amdgcn_sched_group_barrier(0x002, 6, 0);
+                        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+                        __builtin_amdgcn_sched_group_barrier(0x002, 5, 0);
+                        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+                        __builtin_amdgcn_sched_group_barrier(0x002, 5, 0);
                     }
+#endif
                 }
             }
         };
@@ -583,13 +582,6 @@ int64_t grouped_tile_m(const MoeArgs& m)
     return 32;
 }
 
-int64_t grouped_prep_bytes(int64_t act_rows, int64_t K)
-{
-    const int64_t nbp = padded_blocks(K / kQK);
-    auto align = [](int64_t v) { return (v + 255) / 256 * 256; };
-    return align(act_rows * nbp * kBlockF16) + align(act_rows * nbp * 2);
-}
-
 int run_grouped(const MoeArgs& m, const BucketPlan& plan, void* ws, hipStream_t s)
 {
     if (plan.pairs == 0) return FTQ_OK;
@@ -598,23 +590,10 @@ int run_grouped(const MoeArgs& m, const BucketPlan& plan, void* ws, hipStream_t 
     if (st != FTQ_OK) return st;
     uint8_t* base = static_cast<uint8_t*>(ws);
     const int64_t nb = m.K / kQK;
-    auto align = [](int64_t v) { return (v + 255) / 256 * 256; };
-    const int64_t nbp = padded_blocks(nb);
     const int64_t act_rows = m.T * m.top_k / m.act_div;   // tokens, or pairs
-    uint8_t* a16 = base + plan.bytes;
-    uint16_t* d8 = reinterpret_cast<uint16_t*>(a16 + align(act_rows * nbp * kBlockF16));
-
-    // activations -> fp16 codes + scales, padded to whole passes (once per call)
-    const int64_t nblocks = act_rows * nbp;
-    st = launch("prep_activations_kernel", prep_activations_kernel,
-                stride_grid((nblocks + kThreads - 1) / kThreads, lim), kThreads, 0, s,
-                static_cast<const uint8_t*>(m.a), act_rows, nb, a16, d8);
-    if (st != FTQ_OK) return st;
-
     GroupedParams gp{};
     gp.w = static_cast<const uint8_t*>(m.w);
-    gp.a16 = a16;
-    gp.d8 = d8;
+    gp.a = static_cast<const uint8_t*>(m.a);
     gp.out = m.out;
     gp.partials = m.partials;
     gp.offsets = reinterpret_cast<const int32_t*>(base + plan.off_offsets);
@@ -625,10 +604,9 @@ int run_grouped(const MoeArgs& m, const BucketPlan& plan, void* ws, hipStream_t 
     gp.nb = nb;
     gp.top_k = m.top_k;
     gp.act_div = m.act_div;
-    // buffer ranges: 32-bit unsigned byte counts (the narrow variant's a16 is below 4 GiB)
+    // buffer ranges: 32-bit unsigned byte counts (the narrow variant's activations are below 4 GiB)
     auto range32 = [](int64_t bytes) { return (int32_t)(uint32_t)std::min<int64_t>(bytes, UINT32_MAX); };
-    gp.a16_range = range32(act_rows * nbp * kBlockF16);
-    gp.d8_range = range32(act_rows * nbp * 2);
+    gp.a_range = range32(act_rows * nb * kQ8Bytes);
     gp.act = m.act;
     gp.half = m.act ? m.N / 2 : 0;
     if (m.act) {
@@ -654,7 +632,7 @@ int run_grouped(const MoeArgs& m, const BucketPlan& plan, void* ws, hipStream_t 
     // activation offsets fit 32 bits unless the staged activations reach 4 GiB;
     // FTQ_FORCE_WIDE=1 selects the 64-bit variant at any size (tests)
     static const bool force_wide = [] { const char* v = getenv("FTQ_FORCE_WIDE"); return v && v[0] == '1'; }();
-    const bool wide = force_wide || act_rows * nbp * kBlockF16 >= ((int64_t)1 << 32);
+    const bool wide = force_wide || act_rows * nb * kQ8Bytes >= ((int64_t)1 << 32);
     const bool fused = m.act != 0;
     switch (bm) {
     case 128: return launch_grouped<128>(part, fused, vec, wide, gp, grid, s);
