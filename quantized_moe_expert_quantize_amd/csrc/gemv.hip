@@ -258,20 +258,39 @@ __device__ __forceinline__ void store_step(uint8_t* wrow, int l, const Raw<VEC, 
     for (int i = 0; i < Raw<VEC, WT>::kUnits; ++i) d[kLPR * i + l] = R.u[i];
 }
 
+// Output column and weight row of lane row rw of wave `wave` in row tile t.
+// Fused: a tile's 16 rows are the gate and up rows of 8 output columns; in
+// wave w, row rw holds column 8t + 2w + (rw & 1), gate for rw < 2 and up for
+// rw >= 2, so that after the row sums lane l holds the gate and lane l ^ 32
+// the up value of the same column.
+template <bool kFused>
+__device__ __forceinline__ int64_t tile_col(int64_t t, int wave, int rw)
+{
+    if constexpr (kFused) return t * (kRowsPerTile / 2) + wave * (kRowsPerWave / 2) + (rw & 1);
+    return t * kRowsPerTile + wave * kRowsPerWave + rw;
+}
+template <bool kFused>
+__device__ __forceinline__ int64_t tile_row(const GemvParams& p, int64_t t, int wave, int rw)
+{
+    if constexpr (kFused) return (rw >> 1) * p.half + min<int64_t>(tile_col<kFused>(t, wave, rw), p.half - 1);
+    return tile_col<kFused>(t, wave, rw);
+}
+
 // Rows of tiles [t0, t1) of expert e, K blocks [sb, sb+len), for the staged chunk.
 // kMultiSeg: rows span several K segments, so later segments add to the sums
 // already written (a global load inside the loop; kept out of the single
 // segment case so that the weight loads are the only loads in flight there).
 // NPC > 0: exactly NPC pairs are staged (no per-pair guards); NPC == 0: npc
 // (1..8) pairs, guarded at run time.
-// kFused: a tile's 16 rows are the gate and up rows of 8 output columns; in
-// wave w, row rw holds column 8t + 2w + (rw & 1), gate for rw < 2 and up for
-// rw >= 2, so that after the row sums lane l holds the gate and lane l ^ 32
-// the up value of the same column.
-template <int VEC, bool kPartials, bool kMultiSeg, int NPC, bool kFused, int WT>
+// kFused: the rows of a tile are gate and up rows as tile_col describes.
+// `stage` (the pair ids and the staged activation rows of the chunk, ending in
+// a workgroup barrier) runs, for Q4_0, after the loads of the first weight
+// step are issued, which do not depend on it, so that both are in flight
+// together.
+template <int VEC, bool kPartials, bool kMultiSeg, int NPC, bool kFused, int WT, typename Stage>
 __device__ __forceinline__ void stream_tiles(const GemvParams& p, int64_t e, int64_t t0, int64_t t1, int64_t sb, int len,
                                              int npc, const int32_t* plist, uint8_t* wrow, const uint8_t* codes,
-                                             const uint8_t* ds, int l, int rw, int wave)
+                                             const uint8_t* ds, int l, int rw, int wave, Stage&& stage)
 {
     constexpr int kJ = NPC > 0 ? NPC : kPairChunk;
     const int pc = p.pc_cap;
@@ -284,14 +303,8 @@ __device__ __forceinline__ void stream_tiles(const GemvParams& p, int64_t e, int
     const int64_t seg_end = (sb + len) * kBB;   // row bytes up to the segment's end
     auto step_len = [&](int64_t ws) { return (int)min<int64_t>(step_bytes(WT), seg_end - ws * kGroup * kBB); };
     // output column of this lane's row in tile t (the weight row unless fused)
-    auto col_of = [&](int64_t t) {
-        if constexpr (kFused) return t * (kRowsPerTile / 2) + wave * (kRowsPerWave / 2) + (rw & 1);
-        return t * kRowsPerTile + wave * kRowsPerWave + rw;
-    };
-    auto row_of = [&](int64_t t) {
-        if constexpr (kFused) return (rw >> 1) * p.half + min<int64_t>(col_of(t), p.half - 1);
-        return col_of(t);
-    };
+    auto col_of = [&](int64_t t) { return tile_col<kFused>(t, wave, rw); };
+    auto row_of = [&](int64_t t) { return tile_row<kFused>(p, t, wave, rw); };
     // rows past N (last tile only) load row N-1; their sums are never written
     auto src_of = [&](int64_t t, int64_t ws) {
         return wexp + min<int64_t>(row_of(t), p.N - 1) * row_bytes + ws * kGroup * kBB;
@@ -315,7 +328,15 @@ __device__ __forceinline__ void stream_tiles(const GemvParams& p, int64_t e, int
     // unconditional load keeps the loads in flight the same on every path.
     Raw<VEC, WT> R;
     int64_t t = t0, ws = gbeg;
-    load_step<VEC>(src_of(t, ws), step_len(ws), l, R);
+    if constexpr (WT == FTQ_W_Q4_0) {
+        load_step<VEC>(src_of(t, ws), step_len(ws), l, R);
+        stage();
+    } else {
+        // the wider blocks' step buffers would stay live through the staging
+        // and spill: stage first
+        stage();
+        load_step<VEC>(src_of(t, ws), step_len(ws), l, R);
+    }
     while (t < t1) {
         const int64_t n = kFused ? col_of(t) : row_of(t);
         wave_lds_fence();   // the previous step's reads of the buffer come first
@@ -435,6 +456,12 @@ __global__ __launch_bounds__(kThreads, kWavesPerSimd) void moe_gemv_kernel(GemvP
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int l = lane % kLPR, rw = lane / kLPR;   // lane within the row, row within the wave
     const int words = (int)((p.E + 1 + 31) / 32);
+    // scan mode: the first kThreads ids are read once, into registers, and
+    // serve both the routed-bucket bits and the pair lists
+    int32_t id0 = -1;
+    if constexpr (!kBucketed) {
+        if (tid < p.pairs) id0 = p.ids[tid];
+    }
 
     // ---- the routed buckets (experts with pairs, and E for masked pairs) -------
     if constexpr (kBucketed) {
@@ -450,7 +477,8 @@ __global__ __launch_bounds__(kThreads, kWavesPerSimd) void moe_gemv_kernel(GemvP
         for (int w = tid; w < words; w += kThreads) bits[w] = 0;
         __syncthreads();
         for (int64_t q = tid; q < p.pairs; q += kThreads) {
-            const int64_t b = bucket_of(p.ids[q], p.E);
+            const int32_t id = q < kThreads ? id0 : p.ids[q];
+            const int64_t b = bucket_of(id, p.E);
             atomicOr(&bits[b >> 5], 1u << (b & 31));
         }
     }
@@ -485,6 +513,7 @@ __global__ __launch_bounds__(kThreads, kWavesPerSimd) void moe_gemv_kernel(GemvP
             e = uniform((int32_t)(32 * lo + __ffs(m) - 1));
         }
 
+
         // ---- the pair list of this bucket ----------------------------------
         const int32_t* list;
         int64_t count;
@@ -498,7 +527,7 @@ __global__ __launch_bounds__(kThreads, kWavesPerSimd) void moe_gemv_kernel(GemvP
             __syncthreads();
             for (int64_t base = 0; base < p.pairs; base += kThreads) {
                 const int64_t q = base + tid;
-                const bool match = q < p.pairs && bucket_of(p.ids[q], p.E) == e;
+                const bool match = q < p.pairs && bucket_of(base == 0 ? id0 : p.ids[q], p.E) == e;
                 const uint64_t mb = __ballot(match);
                 const int below = __builtin_amdgcn_mbcnt_hi((uint32_t)(mb >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)mb, 0));
                 if (lane == 0) misc[2 + wave] = __popcll(mb);
@@ -516,15 +545,20 @@ __global__ __launch_bounds__(kThreads, kWavesPerSimd) void moe_gemv_kernel(GemvP
 
         for (int64_t c0 = 0; c0 < count; c0 += p.pc_cap) {
             const int npc = (int)min<int64_t>(p.pc_cap, count - c0);
-            __syncthreads();   // the previous chunk is done with plist and the staged rows
-            if (tid < npc) {
-                const int32_t pid = list[c0 + tid];
-                plist[tid] = pid;
-                ptok[tid] = (int32_t)(pid / p.act_div);
-            }
-            __syncthreads();
+            // the chunk's pair ids and tokens (after the previous chunk is done
+            // with them and with the staged rows)
+            auto chunk_ids = [&]() __attribute__((always_inline)) {
+                __syncthreads();
+                if (tid < npc) {
+                    const int32_t pid = list[c0 + tid];
+                    plist[tid] = pid;
+                    ptok[tid] = (int32_t)(pid / p.act_div);
+                }
+                __syncthreads();
+            };
 
             if (e == p.E) {   // masked bucket: zero outputs of tiles [t0, t1)
+                chunk_ids();
                 constexpr int64_t kCols = kFused ? kRowsPerTile / 2 : kRowsPerTile;
                 const int64_t width = kFused ? p.half : p.N;
                 const int64_t r0 = t0 * kCols, r1 = min<int64_t>(t1 * kCols, width);
@@ -543,11 +577,15 @@ __global__ __launch_bounds__(kThreads, kWavesPerSimd) void moe_gemv_kernel(GemvP
             // K segments: one unless the staged rows would not fit the budget.
             for (int64_t sb = 0; sb < nb; sb += p.seg) {
                 const int len = (int)min<int64_t>(p.seg, nb - sb);
-                if (sb > 0) __syncthreads();   // the previous segment's activations are consumed
-                stage_acts(p, ptok, npc, sb, len, codes, ds);
-                __syncthreads();
+                // run by stream_tiles once its first weight loads are out
+                auto stage = [&]() __attribute__((always_inline)) {
+                    if (sb == 0) chunk_ids();
+                    else __syncthreads();   // the previous segment's activations are consumed
+                    stage_acts(p, ptok, npc, sb, len, codes, ds);
+                    __syncthreads();
+                };
                 uint8_t* wrow = lds + L.wt + wave * wave_w(WT) + rw * wrow_pitch(WT);
-#define FTQ_STREAM(NPC) stream_tiles<VEC, kPartials, kMultiSeg, NPC, kFused, WT>(p, e, t0, t1, sb, len, npc, plist, wrow, codes, ds, l, rw, wave)
+#define FTQ_STREAM(NPC) stream_tiles<VEC, kPartials, kMultiSeg, NPC, kFused, WT>(p, e, t0, t1, sb, len, npc, plist, wrow, codes, ds, l, rw, wave, stage)
                 // one or two pairs per expert (decode) without per-pair guards;
                 // more pairs keep the guarded loop, whose guards also stop the
                 // scheduler from interleaving all 8 blocks (which would need
