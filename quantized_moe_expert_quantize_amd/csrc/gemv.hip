@@ -8,8 +8,9 @@
 // HBM-streaming kernel:
 //   * work items are (routed expert, tile of 16 rows); the grid is what fits
 //     on the device at once and each workgroup takes a contiguous share of the
-//     items (at most one item more than any other), so no workgroup waits for
-//     a second round and every routed expert's rows are spread over all CUs;
+//     items of equal cost, an item of an expert with c pairs costing 3 + c
+//     units, so no workgroup waits for a second round, every routed expert's
+//     rows are spread over all CUs, and experts with more pairs get more CUs;
 //   * 16 lanes share a row and walk it in steps of 16 groups of 8 Q4_0 blocks
 //     (2304 bytes).  A step is loaded coalesced: each load instruction of the
 //     16 lanes covers 256 contiguous bytes of the row (16 bytes per lane when
@@ -47,6 +48,11 @@ constexpr int kRowsPerWave = 64 / kLPR;                         // 4
 constexpr int kRowsPerTile = kRowsPerWave * kWaves;             // 16
 constexpr int kGroup = 8;                                       // blocks per lane group (8 blocks: 144 B for Q4_0)
 constexpr int kPairChunk = 8;                                   // pairs served per pass
+// Work split: a (bucket, row tile) item with c pairs costs kItemBase + c units
+// (streaming the tile's weights is worth about three pairs' dot products,
+// measured on decode shapes), and each workgroup takes an equal share of the
+// total cost, so that workgroups on experts with more pairs take fewer tiles.
+constexpr int64_t kItemBase = 3;
 constexpr int kStepGroups = kLPR;                               // groups per row per step
 constexpr int kStepBlocks = kStepGroups * kGroup;               // 128
 
@@ -95,19 +101,19 @@ __device__ __forceinline__ int code_off(int b, int pc) { return 32 * pc * b + 16
 __device__ __forceinline__ int ent_off(int b, int pc) { return 8 * pc * b + 8 * (b >> 3); }
 
 struct LdsLayout {
-    int64_t wt, codes, ds, bits, prefix, plist, misc, list, bytes;
+    int64_t wt, codes, ds, cnt, cost, wsum, plist, misc, list, bytes;
 };
 
 __host__ __device__ constexpr LdsLayout lds_layout(int wt, int64_t E, int64_t seg, int64_t pc_cap, int64_t list_cap)
 {
     LdsLayout l{};
-    const int64_t words = (E + 1 + 31) / 32;
     l.wt = 0;
     l.codes = l.wt + kWaves * wave_w(wt);
     l.ds = l.codes + code_bytes(seg, pc_cap);
-    l.bits = (l.ds + ent_bytes(seg, pc_cap) + 15) / 16 * 16;
-    l.prefix = l.bits + 4 * words;
-    l.plist = l.prefix + 4 * (words + 1);
+    l.cnt = (l.ds + ent_bytes(seg, pc_cap) + 15) / 16 * 16;   // [E+1] pairs per bucket
+    l.cost = (l.cnt + 4 * (E + 1) + 7) / 8 * 8;              // [E+2] cost before each bucket
+    l.wsum = l.cost + 8 * (E + 2);                            // [kWaves] scan partials
+    l.plist = l.wsum + 8 * kWaves;
     l.misc = l.plist + 4 * 2 * kPairChunk;
     l.list = l.misc + 4 * 16;
     l.bytes = l.list + 4 * list_cap;
@@ -446,8 +452,9 @@ __global__ __launch_bounds__(kThreads, kWavesPerSimd) void moe_gemv_kernel(GemvP
     const LdsLayout L = lds_layout(WT, p.E, p.seg, p.pc_cap, p.list_cap);
     uint8_t* codes = lds + L.codes;
     uint8_t* ds = lds + L.ds;
-    uint32_t* bits = reinterpret_cast<uint32_t*>(lds + L.bits);     // routed buckets (E+1 bits)
-    int32_t* prefix = reinterpret_cast<int32_t*>(lds + L.prefix);   // set bits before each word
+    int32_t* cnt = reinterpret_cast<int32_t*>(lds + L.cnt);         // pairs per bucket (E+1)
+    int64_t* cost = reinterpret_cast<int64_t*>(lds + L.cost);       // cost of the buckets before b (E+2)
+    int64_t* wsum = reinterpret_cast<int64_t*>(lds + L.wsum);       // per-wave scan totals
     int32_t* plist = reinterpret_cast<int32_t*>(lds + L.plist);     // [kPairChunk] pair ids
     int32_t* ptok = plist + kPairChunk;                               // [kPairChunk] tokens
     int32_t* misc = reinterpret_cast<int32_t*>(lds + L.misc);
@@ -455,64 +462,86 @@ __global__ __launch_bounds__(kThreads, kWavesPerSimd) void moe_gemv_kernel(GemvP
 
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int l = lane % kLPR, rw = lane / kLPR;   // lane within the row, row within the wave
-    const int words = (int)((p.E + 1 + 31) / 32);
     // scan mode: the first kThreads ids are read once, into registers, and
-    // serve both the routed-bucket bits and the pair lists
+    // serve both the bucket counts and the pair lists
     int32_t id0 = -1;
     if constexpr (!kBucketed) {
         if (tid < p.pairs) id0 = p.ids[tid];
     }
 
-    // ---- the routed buckets (experts with pairs, and E for masked pairs) -------
+    // ---- pairs per bucket (experts, and E for masked pairs) ------------------
     if constexpr (kBucketed) {
-        for (int w = tid; w < words; w += kThreads) {
-            uint32_t m = 0;
-            for (int i = 0; i < 32; ++i) {
-                const int64_t b = 32 * (int64_t)w + i;
-                if (b <= p.E && p.offsets[b + 1] > p.offsets[b]) m |= 1u << i;
-            }
-            bits[w] = m;
-        }
+        for (int64_t b = tid; b <= p.E; b += kThreads) cnt[b] = p.offsets[b + 1] - p.offsets[b];
     } else {
-        for (int w = tid; w < words; w += kThreads) bits[w] = 0;
+        for (int64_t b = tid; b <= p.E; b += kThreads) cnt[b] = 0;
         __syncthreads();
         for (int64_t q = tid; q < p.pairs; q += kThreads) {
             const int32_t id = q < kThreads ? id0 : p.ids[q];
-            const int64_t b = bucket_of(id, p.E);
-            atomicOr(&bits[b >> 5], 1u << (b & 31));
+            atomicAdd(&cnt[bucket_of(id, p.E)], 1);
         }
     }
     __syncthreads();
-    if (tid == 0) {
-        int run = 0;
-        for (int w = 0; w < words; ++w) {
-            prefix[w] = run;
-            run += __popc(bits[w]);
+
+    // ---- exclusive prefix of the bucket costs (row_tiles * (kItemBase + c)) ---
+    int64_t carry = 0;
+    for (int64_t base = 0; base <= p.E; base += kThreads) {
+        const int64_t b = base + tid;
+        const int32_t c = b <= p.E ? cnt[b] : 0;
+        const int64_t v = c > 0 ? p.row_tiles * (kItemBase + c) : 0;
+        int64_t incl = v;
+#pragma unroll
+        for (int o = 1; o < 64; o <<= 1) {
+            const int64_t u = __shfl_up(incl, o);
+            if (lane >= o) incl += u;
         }
-        prefix[words] = run;
+        if (lane == 63) wsum[wave] = incl;
+        __syncthreads();
+        int64_t before = 0, total = 0;
+#pragma unroll
+        for (int w = 0; w < kWaves; ++w) {
+            before += w < wave ? wsum[w] : 0;
+            total += wsum[w];
+        }
+        if (b <= p.E) cost[b] = carry + before + incl - v;
+        if (b == p.E) cost[p.E + 1] = carry + before + incl;
+        carry += total;
+        if (base + kThreads <= p.E) __syncthreads();   // wsum is rewritten by the next chunk
     }
     __syncthreads();
-    const int64_t D = uniform((int32_t)prefix[words]);
-    const int64_t items = D * p.row_tiles;
-    const int64_t i0 = (int64_t)blockIdx.x * items / p.grid, i1 = ((int64_t)blockIdx.x + 1) * items / p.grid;
-    if (i0 >= i1) return;
 
-    for (int64_t d = i0 / p.row_tiles; d * p.row_tiles < i1; ++d) {
-        const int64_t t0 = max<int64_t>(i0 - d * p.row_tiles, 0);
-        const int64_t t1 = min<int64_t>(i1 - d * p.row_tiles, p.row_tiles);
-        // the d-th routed bucket
-        int64_t e = 0;
-        {
-            int lo = 0, hi = words - 1;   // last word with prefix <= d
-            while (lo < hi) {
-                const int mid = (lo + hi + 1) / 2;
-                if (prefix[mid] <= d) lo = mid; else hi = mid - 1;
-            }
-            uint32_t m = bits[lo];
-            for (int64_t k = prefix[lo]; k < d; ++k) m &= m - 1;   // drop the lower set bits
-            e = uniform((int32_t)(32 * lo + __ffs(m) - 1));
+    // ---- this workgroup's share of the cost: the items starting in [x0, x1) ---
+    // Boundaries only need to be the same monotone function of the workgroup
+    // index on both sides of each boundary (0 at the first, C at the last), so
+    // they are computed in double (exact for these magnitudes) and the item
+    // bounds with 32-bit division when the total fits: 64-bit integer
+    // division is a long software sequence on the GPU.
+    const int64_t C = uniform(cost[p.E + 1]);
+    auto share = [&](int64_t g) { return (int64_t)((double)g * (double)C / (double)p.grid); };
+    const int64_t x0 = share(blockIdx.x), x1 = share((int64_t)blockIdx.x + 1);
+    if (x0 >= x1) return;
+    const bool narrow = C < (int64_t(1) << 31);
+    auto ceil_div = [&](int64_t a, int64_t b) -> int64_t {   // a >= 0, 0 < b <= C
+        if (narrow) return (int64_t)(((uint32_t)a + (uint32_t)b - 1u) / (uint32_t)b);
+        return (a + b - 1) / b;
+    };
+    int64_t e_first = 0;
+    {
+        int64_t lo = 0, hi = p.E;   // the last bucket whose cost starts at or before x0
+        while (lo < hi) {
+            const int64_t mid = (lo + hi + 1) / 2;
+            if (cost[mid] <= x0) lo = mid; else hi = mid - 1;
         }
+        e_first = uniform((int32_t)lo);
+    }
 
+    for (int64_t e = e_first; e <= p.E && cost[e] < x1; ++e) {
+        const int64_t c = cnt[e];
+        if (c == 0) continue;
+        const int64_t ci = kItemBase + c, ce = cost[e];
+        // item t of bucket e starts at ce + t * ci
+        const int64_t t0 = uniform((int32_t)(x0 > ce ? ceil_div(x0 - ce, ci) : 0));
+        const int64_t t1 = uniform((int32_t)min<int64_t>(p.row_tiles, ceil_div(x1 - ce, ci)));
+        if (t0 >= t1) continue;
 
         // ---- the pair list of this bucket ----------------------------------
         const int32_t* list;
