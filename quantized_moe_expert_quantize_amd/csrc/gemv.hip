@@ -483,17 +483,30 @@ __global__ __launch_bounds__(kThreads, kWavesPerSimd) void moe_gemv_kernel(GemvP
     __syncthreads();
 
     // ---- exclusive prefix of the bucket costs (row_tiles * (kItemBase + c)) ---
+    auto wave_incl_scan = [&](int64_t v) __attribute__((always_inline)) {
+#pragma unroll
+        for (int o = 1; o < 64; o <<= 1) {
+            const int64_t u = __shfl_up(v, o);
+            if (lane >= o) v += u;
+        }
+        return v;
+    };
+    if (p.E < 64) {   // one wave holds every bucket
+        if (wave == 0) {
+            const int32_t c = lane <= p.E ? cnt[lane] : 0;
+            const int64_t v = c > 0 ? p.row_tiles * (kItemBase + c) : 0;
+            const int64_t incl = wave_incl_scan(v);
+            if (lane <= p.E) cost[lane] = incl - v;
+            if (lane == p.E) cost[p.E + 1] = incl;
+        }
+        __syncthreads();
+    }
     int64_t carry = 0;
-    for (int64_t base = 0; base <= p.E; base += kThreads) {
+    for (int64_t base = 0; p.E >= 64 && base <= p.E; base += kThreads) {
         const int64_t b = base + tid;
         const int32_t c = b <= p.E ? cnt[b] : 0;
         const int64_t v = c > 0 ? p.row_tiles * (kItemBase + c) : 0;
-        int64_t incl = v;
-#pragma unroll
-        for (int o = 1; o < 64; o <<= 1) {
-            const int64_t u = __shfl_up(incl, o);
-            if (lane >= o) incl += u;
-        }
+        const int64_t incl = wave_incl_scan(v);
         if (lane == 63) wsum[wave] = incl;
         __syncthreads();
         int64_t before = 0, total = 0;
@@ -505,9 +518,8 @@ __global__ __launch_bounds__(kThreads, kWavesPerSimd) void moe_gemv_kernel(GemvP
         if (b <= p.E) cost[b] = carry + before + incl - v;
         if (b == p.E) cost[p.E + 1] = carry + before + incl;
         carry += total;
-        if (base + kThreads <= p.E) __syncthreads();   // wsum is rewritten by the next chunk
+        __syncthreads();   // wsum is rewritten by the next chunk; cost is read after the loop
     }
-    __syncthreads();
 
     // ---- this workgroup's share of the cost: the items starting in [x0, x1) ---
     // Boundaries only need to be the same monotone function of the workgroup

@@ -72,6 +72,26 @@ def test_masked_and_duplicate_ids():
         assert np.array_equal(c.partials(path), c.oracle_partials())
 
 
+@pytest.mark.parametrize("T", [40, 700])
+def test_gemv_many_experts_skewed_counts(T):
+    """More than 256 buckets (the GEMV's per-bucket cost prefix runs in several
+    chunks), Zipf-skewed pair counts (the work split by cost gives hot experts
+    more workgroups) and masked ids; T = 40 scans the ids in the kernel, T = 700
+    (4200 pairs) reads the bucketed list."""
+    E, N, K, k = 300, 48, 64, 6
+    ids = Case(E, N, K, T, k, seed=4, kind="zipf").ids.copy()
+    ids[1, 0] = -1
+    ids[T - 1, k - 1] = E + 7
+    c = Case(E, N, K, T, k, seed=4, ids=ids)
+    counts = np.bincount(ids[(ids >= 0) & (ids < E)], minlength=E)
+    say(f"[case] E={E} T={T}: routed experts {np.count_nonzero(counts)}, max pairs per expert {counts.max()}")
+    ref, ab = c.oracle_out()
+    got = c.run(ftq.PATH_GEMV).cpu().numpy()
+    assert_matches_oracle(got, ref, ab, c.nb)
+    assert not got[1 * k].any() and not got[T * k - 1].any()
+    assert np.array_equal(c.partials(ftq.PATH_GEMV), c.oracle_partials())
+
+
 def test_all_ids_masked_gives_zeros():
     E, N, K, T, k = 4, 64, 64, 20, 2
     c = Case(E, N, K, T, k, ids=np.full((T, k), -5, np.int32))
