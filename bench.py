@@ -15,6 +15,7 @@ before timing starts.
     python bench.py --workload mixtral --T 1 --wtype q8_0   # another GGUF weight type (GEMV path)
     python bench.py --mode profile         # a short run for rocprofv3
     python bench.py --summarize-pmc DIR    # HBM traffic from rocprofv3 --pmc runs
+    python bench.py --summarize-trace DB   # kernel table from a rocprofv3 --kernel-trace database
 
 Prints one JSON line.  `value` is milliseconds per step (lower is better);
 `roofline` reports the dominant kernel (the grouped MFMA matmul) against the
@@ -131,6 +132,27 @@ def summarize_pmc(d: str, kernel: str = DOMINANT) -> None:
     print(json.dumps(out, indent=1))
 
 
+def summarize_trace(db: str) -> None:
+    """Per-kernel table (calls, total / average duration, registers, LDS, grid)
+    from a rocprofv3 --kernel-trace database (rocpd SQLite)."""
+    import sqlite3
+    con = sqlite3.connect(db)
+    rows = con.execute(
+        "select name, count(*), sum(duration), avg(duration), max(vgpr_count), max(accum_vgpr_count), "
+        "max(sgpr_count), max(lds_size), max(grid_x), max(workgroup_x) from kernels group by name "
+        "order by sum(duration) desc").fetchall()
+    grand = sum(r[2] for r in rows) or 1
+    print("| kernel | calls | total (us) | average (us) | % of GPU time | arch VGPR | AGPR | SGPR | LDS (B) "
+          "| grid (work-items) | block |")
+    print("|---|---|---|---|---|---|---|---|---|---|---|")
+    for name, n, tot, avg, vg, ag, sg, lds, gx, wx in rows:
+        short = name.replace("ftq::(anonymous namespace)::", "")
+        short = short[5:] if short.startswith("void ") else short
+        short = short.split("(")[0]
+        print(f"| `{short}` | {n} | {tot / 1e3:.1f} | {avg / 1e3:.2f} | {100.0 * tot / grand:.1f} | {vg} | {ag} | {sg} "
+              f"| {lds} | {gx} | {wx} |")
+
+
 def main() -> None:
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
@@ -145,8 +167,12 @@ def main() -> None:
     ap.add_argument("--cpu-sample-tokens", type=int, default=8192, help="tokens the CPU oracle runs (10-30 s on the box)")
     ap.add_argument("--summarize-pmc", metavar="DIR")
     ap.add_argument("--pmc-kernel", default=DOMINANT, help="kernel whose counters --summarize-pmc reports")
+    ap.add_argument("--summarize-trace", metavar="DB", help="per-kernel table from a rocprofv3 --kernel-trace database")
     args = ap.parse_args()
 
+    if args.summarize_trace:
+        summarize_trace(args.summarize_trace)
+        return
     if args.summarize_pmc:
         summarize_pmc(args.summarize_pmc, args.pmc_kernel)
         return
