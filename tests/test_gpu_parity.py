@@ -138,6 +138,41 @@ def test_quantize_q8_1_many_rows_and_ragged():
         assert np.array_equal(got, oracle.quantize_q8_1(x)), (T, K)
 
 
+def _near_tie_blocks():
+    """Blocks whose x/d falls on or within a few ulps of a rounding boundary
+    k + 1/2, for exact and inexact d, and blocks whose d lies outside
+    [2^-100, 2^100] or is subnormal: every place where a quotient formed from a
+    reciprocal could round to a different code than the correctly rounded
+    division."""
+    f32 = np.float32
+    rows = []
+    for amax in (127.0, 1.0, 3.0, 0.3, 1e-3, 7.77e5, 1e-28, 1e32, 1e-32, 1e33, 1e-38, 1e-40):
+        amax = f32(amax)
+        d = f32(amax / f32(127.0))
+        for k0 in (0, 30, 60, 90, 120):
+            vals = [amax]
+            for k in range(k0, k0 + 6):
+                c = f32(f32(k + 0.5) * d)
+                for step in (-2, -1, 0, 1, 2):
+                    v = c
+                    for _ in range(abs(step)):
+                        v = np.nextafter(v, f32(np.inf) if step > 0 else f32(-np.inf))
+                    if abs(v) <= amax:
+                        vals.append(v if (k + step) % 2 == 0 else -v)
+            block = np.zeros(32, f32)
+            vals = vals[:32]
+            block[:len(vals)] = vals
+            rows.append(block)
+    return np.stack(rows)
+
+
+def test_quantize_q8_1_near_ties():
+    import oracle
+    x = _near_tie_blocks()
+    got = ftq.quantize_q8_1(torch.from_numpy(x).cuda()).cpu().numpy()
+    assert np.array_equal(got, oracle.quantize_q8_1(x))
+
+
 def _double_rounding_blocks(n=1 << 20, seed=77):
     """Seeded search (host only) for Q8_1 blocks whose s = d*sum(q) rounds
     differently when taken to fp16 in one step than via fp32.  The oracle holds
