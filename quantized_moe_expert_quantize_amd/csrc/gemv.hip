@@ -8,9 +8,10 @@
 // HBM-streaming kernel:
 //   * work items are (routed expert, tile of 16 rows); the grid is what fits
 //     on the device at once and each workgroup takes a contiguous share of the
-//     items of equal cost, an item of an expert with c pairs costing 3 + c
-//     units, so no workgroup waits for a second round, every routed expert's
-//     rows are spread over all CUs, and experts with more pairs get more CUs;
+//     items of equal cost, an item of an expert with c pairs costing 3 units
+//     per pass over its weights plus c, so no workgroup waits for a second
+//     round, every routed expert's rows are spread over all CUs, and experts
+//     with more pairs get more CUs;
 //   * 16 lanes share a row and walk it in steps of 16 groups of 8 Q4_0 blocks
 //     (2304 bytes).  A step is loaded coalesced: each load instruction of the
 //     16 lanes covers 256 contiguous bytes of the row (16 bytes per lane when
@@ -48,11 +49,17 @@ constexpr int kRowsPerWave = 64 / kLPR;                         // 4
 constexpr int kRowsPerTile = kRowsPerWave * kWaves;             // 16
 constexpr int kGroup = 8;                                       // blocks per lane group (8 blocks: 144 B for Q4_0)
 constexpr int kPairChunk = 8;                                   // pairs served per pass
-// Work split: a (bucket, row tile) item with c pairs costs kItemBase + c units
+// Work split: a (bucket, row tile) item with c pairs costs kItemBase units per
+// pass over its weights (one pass per chunk of at most pc_cap pairs) plus c
 // (streaming the tile's weights is worth about three pairs' dot products,
 // measured on decode shapes), and each workgroup takes an equal share of the
 // total cost, so that workgroups on experts with more pairs take fewer tiles.
 constexpr int64_t kItemBase = 3;
+__device__ __forceinline__ int64_t item_cost(int64_t c, int64_t pc_cap)
+{
+    // counts come from int32 offsets and pc_cap <= 8: 32-bit division suffices
+    return kItemBase * (int64_t)(((uint32_t)c + (uint32_t)pc_cap - 1u) / (uint32_t)pc_cap) + c;
+}
 constexpr int kStepGroups = kLPR;                               // groups per row per step
 constexpr int kStepBlocks = kStepGroups * kGroup;               // 128
 
@@ -69,7 +76,7 @@ __host__ __device__ constexpr int wrow_pitch(int wt) { return step_bytes(wt) + 1
 __host__ __device__ constexpr int wave_w(int wt) { return kRowsPerWave * wrow_pitch(wt); }
 constexpr int kWavesPerSimd = 3;                                // register budget: 3 waves per SIMD
 constexpr int64_t kLdsPerCU = 160 * 1024;
-constexpr int64_t kTargetWGPerCU = 2;                           // LDS is sized so that 2 workgroups fit
+constexpr int64_t kTargetWGPerCU = 2;                           // LDS is sized so that 2 (or 3) workgroups fit
 
 struct GemvParams {
     const uint8_t* w;
@@ -482,7 +489,7 @@ __global__ __launch_bounds__(kThreads, kWavesPerSimd) void moe_gemv_kernel(GemvP
     }
     __syncthreads();
 
-    // ---- exclusive prefix of the bucket costs (row_tiles * (kItemBase + c)) ---
+    // ---- exclusive prefix of the bucket costs (row_tiles * item_cost) ----------
     auto wave_incl_scan = [&](int64_t v) __attribute__((always_inline)) {
 #pragma unroll
         for (int o = 1; o < 64; o <<= 1) {
@@ -494,7 +501,7 @@ __global__ __launch_bounds__(kThreads, kWavesPerSimd) void moe_gemv_kernel(GemvP
     if (p.E < 64) {   // one wave holds every bucket
         if (wave == 0) {
             const int32_t c = lane <= p.E ? cnt[lane] : 0;
-            const int64_t v = c > 0 ? p.row_tiles * (kItemBase + c) : 0;
+            const int64_t v = c > 0 ? p.row_tiles * item_cost(c, p.pc_cap) : 0;
             const int64_t incl = wave_incl_scan(v);
             if (lane <= p.E) cost[lane] = incl - v;
             if (lane == p.E) cost[p.E + 1] = incl;
@@ -505,7 +512,7 @@ __global__ __launch_bounds__(kThreads, kWavesPerSimd) void moe_gemv_kernel(GemvP
     for (int64_t base = 0; p.E >= 64 && base <= p.E; base += kThreads) {
         const int64_t b = base + tid;
         const int32_t c = b <= p.E ? cnt[b] : 0;
-        const int64_t v = c > 0 ? p.row_tiles * (kItemBase + c) : 0;
+        const int64_t v = c > 0 ? p.row_tiles * item_cost(c, p.pc_cap) : 0;
         const int64_t incl = wave_incl_scan(v);
         if (lane == 63) wsum[wave] = incl;
         __syncthreads();
@@ -549,7 +556,7 @@ __global__ __launch_bounds__(kThreads, kWavesPerSimd) void moe_gemv_kernel(GemvP
     for (int64_t e = e_first; e <= p.E && cost[e] < x1; ++e) {
         const int64_t c = cnt[e];
         if (c == 0) continue;
-        const int64_t ci = kItemBase + c, ce = cost[e];
+        const int64_t ci = item_cost(c, p.pc_cap), ce = cost[e];
         // item t of bucket e starts at ce + t * ci
         const int64_t t0 = uniform((int32_t)(x0 > ce ? ceil_div(x0 - ce, ci) : 0));
         const int64_t t1 = uniform((int32_t)min<int64_t>(p.row_tiles, ceil_div(x1 - ce, ci)));
@@ -724,11 +731,23 @@ int run_gemv(const MoeArgs& m, const BucketPlan* plan, const void* ws, hipStream
     // buffers with kTargetWGPerCU workgroups per CU, else the largest multiple
     // of a step (128 blocks) that fits, so that every step is full
     const int64_t fixed = lds_layout(m.wtype, m.E, 0, 0, gp.list_cap).bytes;
-    const int64_t budget = std::max<int64_t>(kLdsPerCU / kTargetWGPerCU - fixed, 0);
-    auto act_bytes = [&](int64_t seg) { return code_bytes(seg, gp.pc_cap) + ent_bytes(seg, gp.pc_cap); };
+    auto act_bytes_pc = [&](int64_t seg, int64_t pc) { return code_bytes(seg, pc) + ent_bytes(seg, pc); };
+    auto act_bytes = [&](int64_t seg) { return act_bytes_pc(seg, gp.pc_cap); };
+    const int64_t avg_pairs = std::max<int64_t>(1, (gp.pairs + m.E - 1) / m.E);
+    // Three workgroups per CU (more streams in flight) when whole activation
+    // rows of the pairs an expert is likely to hold still fit, at least
+    // max(4, 2 * the average per expert) of them, so that an expert's weights
+    // are still streamed once; else two, with more pairs per pass.
+    int64_t budget = std::max<int64_t>(kLdsPerCU / kTargetWGPerCU - fixed, 0);
+    {
+        const int64_t budget3 = std::max<int64_t>(kLdsPerCU / 3 - fixed, 0);
+        int64_t pc3 = gp.pc_cap;
+        while (pc3 > 1 && act_bytes_pc(gp.nb, pc3) > budget3) --pc3;
+        const int64_t want = std::min<int64_t>(gp.pc_cap, std::max<int64_t>(4, 2 * avg_pairs));
+        if (act_bytes_pc(gp.nb, pc3) <= budget3 && pc3 >= want) budget = budget3;
+    }
     // fewer pairs per pass, down to the average per expert, rather than one
     // workgroup per CU (larger weight blocks leave less room for the rows)
-    const int64_t avg_pairs = std::max<int64_t>(1, (gp.pairs + m.E - 1) / m.E);
     while (gp.pc_cap > avg_pairs && act_bytes(gp.nb) > budget) --gp.pc_cap;
     if (m.act) {
         // the activation is applied once a row's sum is complete: stage whole
