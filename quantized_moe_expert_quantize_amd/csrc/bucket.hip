@@ -49,6 +49,40 @@ __global__ __launch_bounds__(kCountThreads) void bucket_count_kernel(
     for (int b = threadIdx.x; b < nbuckets; b += kCountThreads) counts[(int64_t)b * nchunks + c] = hist[b];
 }
 
+// Exclusive prefix of v over the threads of the block, in thread order, plus
+// `carry`; carry becomes carry + the block's total.  wsum: kScanWaves + 1
+// ints of LDS.  Every thread must call it (three barriers).
+constexpr int kScanWaves = kScanThreads / 64;
+__device__ __forceinline__ int32_t block_exclusive_scan(int32_t v, int32_t& carry, int32_t* wsum)
+{
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    int32_t x = v;
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) {
+        const int32_t y = __shfl_up(x, o);
+        if (lane >= o) x += y;
+    }
+    if (lane == 63) wsum[wave] = x;
+    __syncthreads();
+    if (wave == 0) {   // scan of the wave totals, in one wave
+        const int32_t t = lane < kScanWaves ? wsum[lane] : 0;
+        int32_t u = t;
+#pragma unroll
+        for (int o = 1; o < kScanWaves; o <<= 1) {
+            const int32_t y = __shfl_up(u, o);
+            if (lane >= o) u += y;
+        }
+        if (lane < kScanWaves) wsum[lane] = u - t;
+        if (lane == kScanWaves - 1) wsum[kScanWaves] = u;
+    }
+    __syncthreads();
+    const int32_t r = carry + wsum[wave] + x - v;
+    const int32_t total = wsum[kScanWaves];
+    __syncthreads();   // wsum is rewritten by the next call
+    carry += total;
+    return r;
+}
+
 // Pass 2 (one block): flat exclusive scan of counts[nbuckets][nchunks] in
 // place, the bucket offsets (offsets[b] = scanned[b][0], offsets[nbuckets] =
 // pairs) and the exclusive scan of per-bucket tile counts.
@@ -57,12 +91,9 @@ __global__ __launch_bounds__(kScanThreads) void bucket_scan_kernel(
     int32_t* __restrict__ offsets, int32_t* __restrict__ tiles)
 {
     extern __shared__ int32_t off_lds[];          // [nbuckets + 1] bucket offsets
-    __shared__ int32_t wsum[kScanThreads / 64 + 1];
-    __shared__ int32_t carry_s;
-    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    __shared__ int32_t wsum[kScanWaves + 1];
     const int64_t len = (int64_t)nbuckets * nchunks;
-    if (threadIdx.x == 0) carry_s = 0;
-    __syncthreads();
+    int32_t carry = 0;
     for (int64_t base = 0; base < len; base += (int64_t)kScanThreads * kScanPer) {
         const int64_t i0 = base + (int64_t)threadIdx.x * kScanPer;
         int32_t v[kScanPer];
@@ -72,60 +103,35 @@ __global__ __launch_bounds__(kScanThreads) void bucket_scan_kernel(
             v[k] = i0 + k < len ? counts[i0 + k] : 0;
             local += v[k];
         }
-        // inclusive scan of the per-thread totals: within the wave, then over waves
-        int32_t x = local;
-#pragma unroll
-        for (int o = 1; o < 64; o <<= 1) {
-            const int32_t y = __shfl_up(x, o);
-            if (lane >= o) x += y;
-        }
-        if (lane == 63) wsum[wave] = x;
-        __syncthreads();
-        if (threadIdx.x == 0) {
-            int32_t run = carry_s;
-            for (int w = 0; w < kScanThreads / 64; ++w) {
-                const int32_t t = wsum[w];
-                wsum[w] = run;
-                run += t;
-            }
-            wsum[kScanThreads / 64] = run;
-        }
-        __syncthreads();
-        int32_t run = wsum[wave] + x - local;   // exclusive prefix of this thread's run
+        int32_t run = block_exclusive_scan(local, carry, wsum);
+        // bucket and chunk of element i0, then stepped along (one division per pass)
+        int64_t bk = i0 / nchunks, ch = i0 - bk * nchunks;
 #pragma unroll
         for (int k = 0; k < kScanPer; ++k) {
-            const int64_t i = i0 + k;
-            if (i < len) {
-                counts[i] = run;
-                if (i % nchunks == 0) off_lds[i / nchunks] = run;   // first chunk of bucket i / nchunks
+            if (i0 + k < len) {
+                counts[i0 + k] = run;
+                if (ch == 0) off_lds[bk] = run;   // first chunk of bucket bk
             }
             run += v[k];
+            if (++ch == nchunks) {
+                ch = 0;
+                ++bk;
+            }
         }
-        __syncthreads();
-        if (threadIdx.x == 0) carry_s = wsum[kScanThreads / 64];
-        __syncthreads();
     }
-    if (threadIdx.x == 0) off_lds[nbuckets] = carry_s;
+    if (threadIdx.x == 0) off_lds[nbuckets] = carry;
     __syncthreads();
     // bucket offsets, and the tile table from the per-bucket totals
-    int32_t* ntile = off_lds + nbuckets + 1;       // [nbuckets] scratch
     for (int b = threadIdx.x; b <= nbuckets; b += kScanThreads) offsets[b] = off_lds[b];
-    for (int b = threadIdx.x; b < nbuckets; b += kScanThreads) {
-        const int32_t n = off_lds[b + 1] - off_lds[b];
-        ntile[b] = tile_m > 0 ? (n + tile_m - 1) / tile_m : 0;
+    int32_t tcarry = 0;
+    for (int b0 = 0; b0 < nbuckets; b0 += kScanThreads) {
+        const int b = b0 + (int)threadIdx.x;
+        const int32_t n = b < nbuckets ? off_lds[b + 1] - off_lds[b] : 0;
+        const int32_t t = tile_m > 0 ? (int32_t)(((uint32_t)n + (uint32_t)tile_m - 1u) / (uint32_t)tile_m) : 0;
+        const int32_t r = block_exclusive_scan(t, tcarry, wsum);
+        if (b < nbuckets) tiles[b] = r;
     }
-    __syncthreads();
-    if (threadIdx.x == 0) {
-        int32_t run = 0;
-        for (int b = 0; b < nbuckets; ++b) {
-            const int32_t t = ntile[b];
-            ntile[b] = run;
-            run += t;
-        }
-        ntile[nbuckets] = run;
-    }
-    __syncthreads();
-    for (int b = threadIdx.x; b <= nbuckets; b += kScanThreads) tiles[b] = ntile[b];
+    if (threadIdx.x == 0) tiles[nbuckets] = tcarry;
 }
 
 // Lanes of a wave share the per-bucket counters in LDS; the hardware keeps a
@@ -136,24 +142,40 @@ __device__ __forceinline__ void wave_lds_fence() { __builtin_amdgcn_fence(__ATOM
 // Pass 3: one wave per chunk walks its pairs in order, 64 at a time.  A pair's
 // slot is bases[b][c] + (pairs of bucket b earlier in the chunk): the count
 // from earlier steps (an LDS counter per bucket) plus the lanes below it in
-// this step with the same bucket (found with one ballot per key bit).
+// this step with the same bucket (found with one ballot per key bit).  The
+// chunk's ids are loaded up front and its bases staged in LDS, so the walk
+// itself waits on no global memory.
+constexpr int kScatterSteps = kBucketChunk / 64;
+static_assert(kBucketChunk % 64 == 0, "whole steps per chunk");
+
 __global__ __launch_bounds__(64 * kScatterWaves) void bucket_scatter_kernel(
     const int32_t* __restrict__ ids, int64_t pairs, int32_t E, int32_t nbuckets, int64_t nchunks,
     const int32_t* __restrict__ bases, int32_t* __restrict__ sorted)
 {
-    extern __shared__ int32_t seen_all[];        // [kScatterWaves][nbuckets]
+    extern __shared__ int32_t lds_all[];         // [kScatterWaves][2][nbuckets]: counters, chunk bases
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int64_t c = (int64_t)blockIdx.x * kScatterWaves + wave;
     if (c >= nchunks) return;                    // whole waves only: no barrier follows
-    int32_t* seen = seen_all + wave * nbuckets;
-    for (int b = lane; b < nbuckets; b += 64) seen[b] = 0;
+    int32_t* seen = lds_all + (int64_t)wave * 2 * nbuckets;
+    int32_t* cbase = seen + nbuckets;
+    const int64_t base = c * kBucketChunk;
+    int32_t idv[kScatterSteps];
+#pragma unroll
+    for (int st = 0; st < kScatterSteps; ++st) {
+        const int64_t p = base + st * 64 + lane;
+        idv[st] = p < pairs ? ids[p] : 0;
+    }
+    for (int b = lane; b < nbuckets; b += 64) {
+        seen[b] = 0;
+        cbase[b] = bases[(int64_t)b * nchunks + c];
+    }
     wave_lds_fence();
     const uint64_t below = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
-    const int64_t base = c * kBucketChunk;
-    for (int i = 0; i < kBucketChunk; i += 64) {
-        const int64_t p = base + i + lane;
+#pragma unroll
+    for (int st = 0; st < kScatterSteps; ++st) {
+        const int64_t p = base + st * 64 + lane;
         const bool live = p < pairs;
-        const int32_t b = live ? bucket_of(ids[p], E) : -1;
+        const int32_t b = live ? bucket_of(idv[st], E) : -1;
         // lanes holding the same bucket: agree on every key bit (and are live)
         uint64_t same = __ballot(live);
 #pragma unroll
@@ -164,7 +186,7 @@ __global__ __launch_bounds__(64 * kScatterWaves) void bucket_scatter_kernel(
         if (live) {
             const int rank = __popcll(same & below);
             const int32_t prev = seen[b];
-            sorted[bases[(int64_t)b * nchunks + c] + prev + rank] = (int32_t)p;
+            sorted[cbase[b] + prev + rank] = (int32_t)p;
             wave_lds_fence();   // every lane has read seen[] before the leaders update it
             if (rank == 0) seen[b] = prev + __popcll(same);
         }
@@ -203,11 +225,11 @@ int run_bucket(const int32_t* ids, int64_t E, const BucketPlan& plan, void* ws, 
     int st = launch("bucket_count_kernel", bucket_count_kernel, plan.chunks, kCountThreads,
                     sizeof(int32_t) * nb, s, ids, plan.pairs, (int32_t)E, nb, plan.chunks, counts);
     if (st != FTQ_OK) return st;
-    st = launch("bucket_scan_kernel", bucket_scan_kernel, 1, kScanThreads, sizeof(int32_t) * (2 * nb + 2), s,
+    st = launch("bucket_scan_kernel", bucket_scan_kernel, 1, kScanThreads, sizeof(int32_t) * (nb + 1), s,
                 counts, plan.chunks, nb, (int32_t)plan.tile_m, offsets, tiles);
     if (st != FTQ_OK) return st;
     return launch("bucket_scatter_kernel", bucket_scatter_kernel, (plan.chunks + kScatterWaves - 1) / kScatterWaves,
-                  64 * kScatterWaves, sizeof(int32_t) * kScatterWaves * nb, s, ids, plan.pairs, (int32_t)E, nb,
+                  64 * kScatterWaves, sizeof(int32_t) * 2 * kScatterWaves * nb, s, ids, plan.pairs, (int32_t)E, nb,
                   plan.chunks, static_cast<const int32_t*>(counts), sorted);
 }
 

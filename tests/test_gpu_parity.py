@@ -92,6 +92,20 @@ def test_gemv_many_experts_skewed_counts(T):
     assert np.array_equal(c.partials(ftq.PATH_GEMV), c.oracle_partials())
 
 
+def test_most_experts_supported():
+    """E = 4095, the largest expert count the bucket tables take (one pair per
+    expert at most here); both paths, against the oracle."""
+    E, N, K, T, k = 4095, 40, 64, 24, 3
+    ids = Case(E, N, K, T, k, seed=9).ids.copy()
+    ids[0, 0] = E - 1
+    ids[2, 1] = -3
+    c = Case(E, N, K, T, k, seed=9, ids=ids)
+    ref, ab = c.oracle_out()
+    for path in PATHS:
+        assert_matches_oracle(c.run(path).cpu().numpy(), ref, ab, c.nb)
+        assert np.array_equal(c.partials(path), c.oracle_partials())
+
+
 def test_all_ids_masked_gives_zeros():
     E, N, K, T, k = 4, 64, 64, 20, 2
     c = Case(E, N, K, T, k, ids=np.full((T, k), -5, np.int32))
