@@ -238,6 +238,15 @@ def main() -> None:
         ftq.moe_route(ids_d, E, ws, path)
         if marks:
             marks[2].record()
+        matmul()
+        if marks:
+            marks[3].record()
+        if down:
+            ftq.combine_topk(out, gates_d, out=comb)
+            if marks:
+                marks[4].record()
+
+    def matmul():
         if wt != 2:
             ftq.moe_gguf(wq, wt, aq, ids_d, E, N, K, per_pair=down, path=path, out=out, workspace=ws)
         elif down:
@@ -246,12 +255,6 @@ def main() -> None:
             ftq.moe_act_routed(wq, aq, ids_d, E, N, K, act_kind, out, ws, path)
         else:
             ftq.moe_routed(wq, aq, ids_d, E, N, K, out, ws, path)
-        if marks:
-            marks[3].record()
-        if down:
-            ftq.combine_topk(out, gates_d, out=comb)
-            if marks:
-                marks[4].record()
 
     steps = 3 if args.mode == "profile" else args.steps
     warmup = 2 if args.mode == "profile" else args.warmup
@@ -259,7 +262,11 @@ def main() -> None:
         step()
     torch.cuda.synchronize()
 
-    # ---- timed region: exactly `steps` steps --------------------------------
+    # Per-stage marks on eager steps (HIP events between the stages).  At decode
+    # sizes a stage can take less GPU time than the host takes to submit the
+    # next call, so these include submission gaps there; the step time and the
+    # dominant kernel's time below come from graph replays, which keep the GPU
+    # busy.
     marks = [[ev() for _ in range(n_marks)] for _ in range(steps)]
     torch.cuda.synchronize()
     t0 = time.perf_counter()
@@ -267,11 +274,12 @@ def main() -> None:
         step(marks[i])
     torch.cuda.synchronize()
     t1 = time.perf_counter()
-    ms_per_step = (t1 - t0) * 1e3 / steps
+    eager_ms_per_step = (t1 - t0) * 1e3 / steps
     q_ms = statistics.mean(m[0].elapsed_time(m[1]) for m in marks)
     r_ms = statistics.mean(m[1].elapsed_time(m[2]) for m in marks)
-    mm_ms = statistics.mean(m[2].elapsed_time(m[3]) for m in marks)
+    mm_eager_ms = statistics.mean(m[2].elapsed_time(m[3]) for m in marks)
     cb_ms = statistics.mean(m[3].elapsed_time(m[4]) for m in marks) if down else None
+    ref_out = (comb if down else out).clone()
 
     if args.mode == "profile":
         # plain copy of known size for counter calibration: 1 GiB read, 1 GiB written
@@ -280,8 +288,68 @@ def main() -> None:
         for _ in range(3):
             torch.mul(src, 1.0, out=dst)
         torch.cuda.synchronize()
-        print(json.dumps({"mode": "profile", "ms_per_step": ms_per_step, "matmul_ms": mm_ms, "path": path}))
+        print(json.dumps({"mode": "profile", "ms_per_step": eager_ms_per_step, "matmul_ms": mm_eager_ms, "path": path}))
         return
+
+    # One step captured as a HIP graph (every libftq call is capturable; the
+    # library allocates and synchronises nothing), checked bit for bit against
+    # the eager step, then replayed for the timed region.
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        step()
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    g_step = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g_step):
+        step()
+    (comb if down else out).zero_()
+    torch.cuda.synchronize()
+    g_step.replay()
+    torch.cuda.synchronize()
+    if not torch.equal(comb if down else out, ref_out):
+        print("bench.py: the graph-replayed step differs from the eager step", file=sys.stderr)
+        sys.exit(1)
+
+    # the same number of steps as graph replays (the host submits one graph
+    # per step, so decode-size steps are no longer bound by per-call submission)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(steps):
+        g_step.replay()
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    graph_ms_per_step = (t1 - t0) * 1e3 / steps
+    ms_per_step = eager_ms_per_step
+
+    # ---- the dominant kernel's duration ---------------------------------------
+    # A call of 0.2 ms or more keeps the GPU behind the host, so the HIP events
+    # between the stages of the eager steps bracket the kernel itself.  Shorter
+    # calls take less GPU time than the host needs to submit the next one, so
+    # they are timed with HIP events around a graph of R calls on the stream
+    # they run on (per call); this agrees with the kernel trace, where the eager
+    # marks would include submission gaps.
+    R = 20
+    kernel_from_graph = mm_eager_ms < 0.2
+    mm_graph_ms = None
+    if kernel_from_graph:
+        g_mm = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g_mm):
+            for _ in range(R):
+                matmul()
+        torch.cuda.synchronize()
+        per_call = []
+        for i in range(5):
+            a, b = ev(), ev()
+            a.record()
+            g_mm.replay()
+            b.record()
+            torch.cuda.synchronize()
+            per_call.append(a.elapsed_time(b) / R)
+        mm_graph_ms = statistics.median(per_call)
+    mm_ms = mm_graph_ms if kernel_from_graph else mm_eager_ms
+    how = ("HIP events around a graph replay of 20 calls, per call" if kernel_from_graph
+           else "HIP events between the stages of the timed eager steps, mean")
 
     # ---- roofline of the dominant kernel ------------------------------------
     pairs = T * k
@@ -300,7 +368,7 @@ def main() -> None:
         roofline = {"bound": "mfma", "achieved": round(tops, 2), "peak": F16_PEAK_TFLOPS, "unit": "TFLOP/s",
                     "frac": round(tops / F16_PEAK_TFLOPS, 4), "traffic": traffic,
                     "kernel": "moe_grouped_kernel (f16 MFMA on exact integer codes)", "kernel_ms": round(mm_ms, 4),
-                    "kernel_ms_covers": "one routed matmul call: moe_grouped_kernel",
+                    "kernel_ms_covers": "one routed matmul call: moe_grouped_kernel; " + how,
                     "frac_of_int8_peak": round(tops / INT8_PEAK_TOPS, 4),
                     "ops_per_launch": ops, "alg_bytes_per_launch": alg_bytes,
                     "hbm_gbs": round(gbs, 1), "hbm_frac": round(gbs / HBM_PEAK_GBS, 4)}
@@ -308,6 +376,7 @@ def main() -> None:
         roofline = {"bound": "hbm", "achieved": round(gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                     "frac": round(gbs / HBM_PEAK_GBS, 4), "traffic": traffic,
                     "kernel": "moe_gemv_kernel", "kernel_ms": round(mm_ms, 4),
+                    "kernel_ms_covers": "one routed matmul call: moe_gemv_kernel; " + how,
                     "alg_bytes_per_launch": alg_bytes, "ops_per_launch": ops}
 
     # ---- CPU oracle on a bounded sample of the same workload ----------------
@@ -355,7 +424,14 @@ def main() -> None:
                   else f"{args.wtype} x q8_1 (int8 dot4 block dots, fp32 scale-accumulate)"),
         "data": "synthetic",
         "config": dict(wl, T=T, pairs=pairs, path={1: "gemv", 2: "grouped"}[path], wtype=args.wtype),
-        "breakdown_ms": dict({"quantize_q8_1": round(q_ms, 4), "route": round(r_ms, 4), "matmul": round(mm_ms, 4)},
+        "timing": "value: wall clock over the timed steps issued eagerly; graph_ms_per_step: the same number of "
+                  "steps as replays of one captured step graph (bit-identical output checked); breakdown: HIP events "
+                  "between the stages of the eager steps (below 0.2 ms a stage includes host submission gaps), "
+                  "matmul as roofline.kernel_ms_covers says",
+        "graph_ms_per_step": round(graph_ms_per_step, 4),
+        "breakdown_ms": dict({"quantize_q8_1": round(q_ms, 4), "route": round(r_ms, 4), "matmul": round(mm_ms, 4),
+                              "matmul_eager_marks": round(mm_eager_ms, 4),
+                              "matmul_graph_per_call": round(mm_graph_ms, 4) if mm_graph_ms is not None else None},
                              **({"combine_topk": round(cb_ms, 4)} if down else {})),
         "throughput": dict({"tokens_per_s": round(T / (ms_per_step / 1e3), 1), "matmul_TOPS": round(tops, 2),
                             "matmul_alg_GBps": round(gbs, 1)},
