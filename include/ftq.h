@@ -136,7 +136,8 @@ int64_t ftq_moe_workspace_bytes(int64_t E, int64_t N, int64_t K, int64_t T, int6
  *   path:     FTQ_PATH_AUTO, FTQ_PATH_GEMV or FTQ_PATH_GROUPED.  Both paths
  *             compute the same values; each is deterministic and batch
  *             invariant (a row's bits do not depend on the other rows).
- * Limits: K % 32 == 0; E, N, top_k >= 1; top_k <= E; T >= 0 (T == 0: no-op);
+ * Limits: K % 32 == 0; E, N, top_k >= 1; top_k <= E; E <= 4095 (the bucket
+ * tables live in LDS: FTQ_ERR_UNSUPPORTED above); T >= 0 (T == 0: no-op);
  * T*top_k < 2^31.  Output offsets use 64-bit arithmetic throughout.
  */
 int ftq_moe_q4_0_q8_1(const void* w, const void* a, const int32_t* topk_ids, float* out,
@@ -251,7 +252,8 @@ int ftq_moe_combine_topk(const float* y, const float* gates, float* out, int64_t
  *   out:  fp32 [T*top_k][N/2], row p = t*top_k + j; masked pairs give zero rows.
  * Errors: N odd or act unknown: FTQ_ERR_INVALID_ARG.  FTQ_ERR_UNSUPPORTED when
  * one expert's weights reach 4 GiB (grouped path) or when one activation row
- * does not fit the GEMV path's on-chip staging (K beyond about 45 000).
+ * does not fit the GEMV path's on-chip staging (K beyond 33 056 with 8 experts,
+ * 32 000 with 128; the per-expert tables share the budget).
  * ftq_moe_q4_0_q8_1_act_routed takes pairs routed by ftq_moe_route, as
  * ftq_moe_q4_0_q8_1_routed does.
  */

@@ -728,8 +728,8 @@ int run_gemv(const MoeArgs& m, const BucketPlan* plan, const void* ws, hipStream
     // a bucket never holds more than T*top_k pairs
     gp.pc_cap = (int)std::min<int64_t>(kPairChunk, gp.pairs);
     // K segment: whole rows when the staged activations fit next to the weight
-    // buffers with kTargetWGPerCU workgroups per CU, else the largest multiple
-    // of a step (128 blocks) that fits, so that every step is full
+    // buffers with the chosen workgroups per CU (below), else the largest
+    // multiple of a step (128 blocks) that fits, so that every step is full
     const int64_t fixed = lds_layout(m.wtype, m.E, 0, 0, gp.list_cap).bytes;
     auto act_bytes_pc = [&](int64_t seg, int64_t pc) { return code_bytes(seg, pc) + ent_bytes(seg, pc); };
     auto act_bytes = [&](int64_t seg) { return act_bytes_pc(seg, gp.pc_cap); };

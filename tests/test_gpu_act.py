@@ -143,6 +143,19 @@ def test_fused_errors_are_reported():
         ftq.moe_act(w_odd, aq, ids, 4, 63, 64, ftq.ACT_SILU)
 
 
+def test_fused_gemv_row_length_limit():
+    """The fused GEMV stages whole activation rows on chip: with 8 experts a row
+    of K = 33 056 (1033 blocks) fits next to the weight buffers and one block
+    more does not, which the call reports as FTQ_ERR_UNSUPPORTED."""
+    c = Case(8, 4, 33056, 1, 2, seed=2)
+    y, ab = c.oracle_out()
+    assert_act_matches(run_act(c, ftq.ACT_SILU, ftq.PATH_GEMV).cpu().numpy(), y, ab, c.nb, ftq.ACT_SILU)
+    c = Case(8, 4, 33088, 1, 2, seed=2)
+    with pytest.raises(ftq.FtqError) as err:
+        run_act(c, ftq.ACT_SILU, ftq.PATH_GEMV)
+    assert err.value.status == 4   # FTQ_ERR_UNSUPPORTED
+
+
 FULL = [
     # name, E, N (gate + up rows), K, top_k, T, routing, sampled pairs
     ("mixtral_gate_up_T8", 8, 28672, 4096, 2, 8, "uniform", 6),
