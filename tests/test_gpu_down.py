@@ -169,7 +169,8 @@ def _combine_bound(gates, y, ab_y=None, nb=0):
     return bound
 
 
-@pytest.mark.parametrize("shape", [(1, 1, 1), (5, 2, 4), (37, 8, 131), (300, 8, 1408), (64, 2, 4096), (1000, 3, 7)])
+@pytest.mark.parametrize("shape", [(1, 1, 1), (5, 2, 4), (37, 8, 131), (300, 8, 1408), (64, 2, 4096), (1000, 3, 7),
+                                   (9, 1, 8), (40, 4, 64), (33, 6, 128), (21, 5, 96)])
 def test_combine_matches_oracle(shape):
     T, k, N = shape
     say(f"[combine] T={T} top_k={k} N={N}")
