@@ -8,7 +8,7 @@
 // HBM-streaming kernel:
 //   * work items are (routed expert, tile of 16 rows); the grid is what fits
 //     on the device at once and each workgroup takes a contiguous share of the
-//     items of equal cost, an item of an expert with c pairs costing 3 units
+//     items of equal cost, an item of an expert with c pairs costing 1-3 units
 //     per pass over its weights plus c, so no workgroup waits for a second
 //     round, every routed expert's rows are spread over all CUs, and experts
 //     with more pairs get more CUs;
@@ -49,16 +49,18 @@ constexpr int kRowsPerWave = 64 / kLPR;                         // 4
 constexpr int kRowsPerTile = kRowsPerWave * kWaves;             // 16
 constexpr int kGroup = 8;                                       // blocks per lane group (8 blocks: 144 B for Q4_0)
 constexpr int kPairChunk = 8;                                   // pairs served per pass
-// Work split: a (bucket, row tile) item with c pairs costs kItemBase units per
-// pass over its weights (one pass per chunk of at most pc_cap pairs) plus c
-// (streaming the tile's weights is worth about three pairs' dot products,
-// measured on decode shapes), and each workgroup takes an equal share of the
-// total cost, so that workgroups on experts with more pairs take fewer tiles.
-constexpr int64_t kItemBase = 3;
-__device__ __forceinline__ int64_t item_cost(int64_t c, int64_t pc_cap)
+// Work split: a (bucket, row tile) item with c pairs costs `base` units per
+// pass over its weights (one pass per chunk of at most pc_cap pairs) plus c,
+// and each workgroup takes an equal share of the total cost, so that
+// workgroups on experts with more pairs take fewer tiles.  Measured on decode
+// shapes, streaming a tile's weights is worth about three pairs' dot products
+// with two workgroups per CU and about one with three (more streams in flight).
+constexpr int64_t kItemBase2PerCU = 3;
+constexpr int64_t kItemBase3PerCU = 1;
+__device__ __forceinline__ int64_t item_cost(int64_t c, int64_t pc_cap, int64_t base)
 {
     // counts come from int32 offsets and pc_cap <= 8: 32-bit division suffices
-    return kItemBase * (int64_t)(((uint32_t)c + (uint32_t)pc_cap - 1u) / (uint32_t)pc_cap) + c;
+    return base * (int64_t)(((uint32_t)c + (uint32_t)pc_cap - 1u) / (uint32_t)pc_cap) + c;
 }
 constexpr int kStepGroups = kLPR;                               // groups per row per step
 constexpr int kStepBlocks = kStepGroups * kGroup;               // 128
@@ -93,6 +95,7 @@ struct GemvParams {
     int64_t grid;             // workgroups launched
     int64_t seg;              // K blocks staged per pass (a multiple of 8)
     int pc_cap;               // activation rows staged per pass (<= kPairChunk)
+    int64_t item_base;        // cost of one pass over a tile's weights, in pairs
     int list_cap;             // scan mode: LDS slots for the pair list
 };
 
@@ -501,7 +504,7 @@ __global__ __launch_bounds__(kThreads, kWavesPerSimd) void moe_gemv_kernel(GemvP
     if (p.E < 64) {   // one wave holds every bucket
         if (wave == 0) {
             const int32_t c = lane <= p.E ? cnt[lane] : 0;
-            const int64_t v = c > 0 ? p.row_tiles * item_cost(c, p.pc_cap) : 0;
+            const int64_t v = c > 0 ? p.row_tiles * item_cost(c, p.pc_cap, p.item_base) : 0;
             const int64_t incl = wave_incl_scan(v);
             if (lane <= p.E) cost[lane] = incl - v;
             if (lane == p.E) cost[p.E + 1] = incl;
@@ -512,7 +515,7 @@ __global__ __launch_bounds__(kThreads, kWavesPerSimd) void moe_gemv_kernel(GemvP
     for (int64_t base = 0; p.E >= 64 && base <= p.E; base += kThreads) {
         const int64_t b = base + tid;
         const int32_t c = b <= p.E ? cnt[b] : 0;
-        const int64_t v = c > 0 ? p.row_tiles * item_cost(c, p.pc_cap) : 0;
+        const int64_t v = c > 0 ? p.row_tiles * item_cost(c, p.pc_cap, p.item_base) : 0;
         const int64_t incl = wave_incl_scan(v);
         if (lane == 63) wsum[wave] = incl;
         __syncthreads();
@@ -556,7 +559,7 @@ __global__ __launch_bounds__(kThreads, kWavesPerSimd) void moe_gemv_kernel(GemvP
     for (int64_t e = e_first; e <= p.E && cost[e] < x1; ++e) {
         const int64_t c = cnt[e];
         if (c == 0) continue;
-        const int64_t ci = item_cost(c, p.pc_cap), ce = cost[e];
+        const int64_t ci = item_cost(c, p.pc_cap, p.item_base), ce = cost[e];
         // item t of bucket e starts at ce + t * ci
         const int64_t t0 = uniform((int32_t)(x0 > ce ? ceil_div(x0 - ce, ci) : 0));
         const int64_t t1 = uniform((int32_t)min<int64_t>(p.row_tiles, ceil_div(x1 - ce, ci)));
@@ -770,6 +773,7 @@ int run_gemv(const MoeArgs& m, const BucketPlan* plan, const void* ws, hipStream
     // grid: the workgroups that are resident at once (LDS and registers permitting)
     const int64_t by_lds = std::max<int64_t>(1, kLdsPerCU / lds);
     const int64_t per_cu = std::min<int64_t>(by_lds, kWavesPerSimd * 4 / kWaves);
+    gp.item_base = per_cu >= 3 ? kItemBase3PerCU : kItemBase2PerCU;
     const int64_t max_items = (std::min<int64_t>(m.E, gp.pairs) + 1) * gp.row_tiles;
     gp.grid = std::max<int64_t>(1, std::min<int64_t>((int64_t)lim.cu_count * per_cu, max_items));
     // widest load unit that keeps every step aligned: 16 bytes when K/32 is a
