@@ -109,15 +109,35 @@ int ftq_quantize_q4_0(const float* w, int64_t rows, int64_t K, void* y, hipStrea
 /*
  * The path FTQ_PATH_AUTO takes for these sizes (FTQ_PATH_GEMV or
  * FTQ_PATH_GROUPED), or -FTQ_ERR_INVALID_ARG for invalid sizes.  Pure host
- * arithmetic: the choice never depends on device data, so a batch and any
- * split of it into halves of similar size take the same path.
+ * arithmetic on E, T and top_k: the choice never reads device data, so no
+ * call has to wait for the GPU and every call stays capturable in a graph
+ * ("Current Bug: CuTeDSLMoERunner", Bug 8b and Cudagraph Constraints: a host
+ * readback of device values breaks capture).  Rule: the GEMV path when
+ * T*top_k <= 4096 and the pairs per expert T*top_k/E are at most 4 (E <= 16)
+ * or 1.5 (E > 16); the grouped path otherwise.
+ * Bit equality of a batch and its split halves (FreeToken PR #185, Test) holds
+ * on each forced path.  Under FTQ_PATH_AUTO it holds when the batch and its
+ * halves fall on the same side of the rule, which is not the case just above
+ * the crossover: with 128 experts and top_k = 8, T = 25..48 runs grouped and
+ * its halves run the GEMV; with 8 experts and top_k = 2, T = 17..32.  The two
+ * paths sum in different orders, so their bits differ there (both within the
+ * stated tolerance of the exact result).
  */
 int ftq_moe_select_path(int64_t E, int64_t N, int64_t K, int64_t T, int64_t top_k);
 
 /*
  * Exact workspace size in bytes that ftq_moe_q4_0_q8_1 needs for these sizes
  * and this path (FTQ_PATH_AUTO resolved as above); 0 means none.  Returns -1
- * for invalid sizes.  Host arithmetic only.
+ * for invalid sizes (ftq_last_error says why).  Host arithmetic only, from the
+ * same sizes the call takes, so the caller can allocate it once per shape.
+ * The bound is exact rather than a guess at a maximum because buffers sized
+ * from the wrong bound are what broke the expert-sorted runner of "Current
+ * Bug: CuTeDSLMoERunner" (Bug 9: a padded buffer too small, indexed out of
+ * bounds; Bug 15: buffers sized for the largest batch, out of memory; Bug 16:
+ * a buffer sized for max_tokens*top_k where the layout needed
+ * num_experts*max_chunks*128).  What it holds: per-chunk bucket counts, the
+ * per-expert segment and tile offsets and the sorted pair list, each 256-byte
+ * aligned; it grows with T*top_k and E, not with N or K.
  */
 int64_t ftq_moe_workspace_bytes(int64_t E, int64_t N, int64_t K, int64_t T, int64_t top_k, int path);
 
@@ -134,8 +154,11 @@ int64_t ftq_moe_workspace_bytes(int64_t E, int64_t N, int64_t K, int64_t T, int6
  *             256-byte aligned (may be NULL when that is 0).  Its contents on
  *             entry do not matter; calls sharing one workspace must not overlap.
  *   path:     FTQ_PATH_AUTO, FTQ_PATH_GEMV or FTQ_PATH_GROUPED.  Both paths
- *             compute the same values; each is deterministic and batch
- *             invariant (a row's bits do not depend on the other rows).
+ *             compute the same exact block products and sum them in fp32,
+ *             in different orders.  Each forced path is deterministic and
+ *             batch invariant: a row's bits depend neither on the other rows
+ *             nor on the batch size.  Which path FTQ_PATH_AUTO takes does
+ *             depend on the batch size (ftq_moe_select_path).
  * Limits: K % 32 == 0; E, N, top_k >= 1; top_k <= E; E <= 4095 (the bucket
  * tables live in LDS: FTQ_ERR_UNSUPPORTED above); T >= 0 (T == 0: no-op);
  * T*top_k < 2^31.  Output offsets use 64-bit arithmetic throughout.
@@ -231,8 +254,6 @@ int ftq_moe_q4_0_q8_1_pairs_partials(const void* w, const void* a_pairs, const i
 int ftq_moe_combine_topk(const float* y, const float* gates, float* out, int64_t T, int64_t top_k,
                          int64_t N, hipStream_t stream);
 
-/* Message for the last failing call on this thread ("" if none).  The pointer
- * stays valid until the next ftq_* call on the same thread. */
 /*
  * The first layer of an expert FFN with its gated activation fused into the
  * matmul's epilogue: the GEMV's output feeds gelu_tanh_and_mul in FreeToken
@@ -244,8 +265,13 @@ int ftq_moe_combine_topk(const float* y, const float* gates, float* out, int64_t
  *
  *   out[p][c] = act(y[p][c]) * y[p][N/2 + c],  y[p][n] the plain matmul value
  *
- * computed in fp32 from the matmul's fp32 gate and up values (expf / tanhf),
- * without writing y.  Arguments are those of ftq_moe_q4_0_q8_1 (per-token
+ * computed in fp32 from the matmul's fp32 gate and up values, without writing
+ * y.  Both activations are evaluated as x * 1/(1 + e^-z), with z = x for SiLU
+ * and z = 2 sqrt(2/pi) (x + 0.044715 x^3) for the tanh form of GELU (the same
+ * function, since (1 + tanh(z/2))/2 = 1/(1 + e^-z)); e^-z is one hardware
+ * base-2 exponential and the quotient one hardware reciprocal.  Relative to the
+ * exact activation of the fp32 inputs the result is within 9 u (|act(x)| + |x|),
+ * u = 2^-24, which the tests check together with the matmul's own bound.  Arguments are those of ftq_moe_q4_0_q8_1 (per-token
  * activations, the same workspace: ftq_moe_workspace_bytes(E, N, K, ...)), plus
  *   N:    weight rows per expert, even (gate and up halves);
  *   act:  FTQ_ACT_SILU or FTQ_ACT_GELU_TANH;
@@ -300,6 +326,13 @@ int ftq_moe_gguf_q8_1_partials(const void* w, int wtype, const void* a, const in
                                int act_per_pair, void* workspace, size_t workspace_bytes, int path,
                                hipStream_t stream);
 
+/*
+ * Message for the last failing call on this thread ("" if none): for a
+ * rejected launch it names the kernel, grid, block and LDS bytes and the HIP
+ * error (FreeToken PR #185, Fix: report the geometry of a failed launch).  The
+ * pointer stays valid until the next ftq_* call on the same thread; every call
+ * clears it on entry.
+ */
 const char* ftq_last_error(void);
 
 /* Library version string, e.g. "ftq 0.1.0 gfx950". */
@@ -313,6 +346,18 @@ const char* ftq_version(void);
  * operation.
  */
 void ftq_debug_force_block_threads(int threads);
+
+/*
+ * Checking aid: the on-chip plan the GEMV path makes for these sizes, host
+ * arithmetic only (no device is touched).  *seg: K/32 blocks staged per
+ * segment (less than K/32 when a row is streamed in several K segments, which
+ * happens when the activation rows of the pairs served per pass do not fit in
+ * LDS next to the weight buffers); *pairs_per_pass: activation rows staged per
+ * pass; *wg_per_cu: workgroups per CU.  wtype as ftq_wtype, act 0 or FTQ_ACT_*.
+ * Returns FTQ_OK, or the error the matmul would return for these sizes.
+ */
+int ftq_debug_gemv_plan(int64_t E, int64_t N, int64_t K, int64_t T, int64_t top_k, int wtype, int act,
+                        int64_t* seg, int64_t* pairs_per_pass, int64_t* wg_per_cu);
 
 #ifdef __cplusplus
 }

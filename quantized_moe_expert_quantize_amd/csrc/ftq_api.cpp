@@ -380,4 +380,21 @@ const char* ftq_version(void) { return "ftq 0.1.0 gfx950"; }
 
 void ftq_debug_force_block_threads(int threads) { g_forced_threads = threads > 0 ? threads : 0; }
 
+int ftq_debug_gemv_plan(int64_t E, int64_t N, int64_t K, int64_t T, int64_t top_k, int wtype, int act, int64_t* seg,
+                        int64_t* pairs_per_pass, int64_t* wg_per_cu)
+{
+    clear_error();
+    int st = check_sizes(E, N, K, T, top_k);
+    if (st != FTQ_OK) return st;
+    if (!seg || !pairs_per_pass || !wg_per_cu) { set_error("null output pointer"); return FTQ_ERR_INVALID_ARG; }
+    MoeArgs m{};
+    m.E = E; m.N = N; m.K = K; m.T = T; m.top_k = top_k; m.act = act; m.wtype = wtype;
+    const GemvPlan g = plan_gemv(m, T * top_k > kGemvScanMaxPairs);
+    if (!g.fits) { set_error("a fused activation row of K = %lld does not fit on chip", (long long)K); return FTQ_ERR_UNSUPPORTED; }
+    *seg = g.seg;
+    *pairs_per_pass = g.pc_cap;
+    *wg_per_cu = g.per_cu;
+    return FTQ_OK;
+}
+
 }  // extern "C"

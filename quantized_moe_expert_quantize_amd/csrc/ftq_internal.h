@@ -122,6 +122,15 @@ __device__ __forceinline__ float gated_act(int act, float x)
 // GEMV path; `bucketed` selects the pair list from the workspace (else the
 // kernel scans the ids itself).
 int run_gemv(const MoeArgs& m, const BucketPlan* plan, const void* ws, hipStream_t s);
+
+// The GEMV's on-chip plan, host arithmetic of the sizes alone: activation rows
+// staged per pass, K blocks per segment (seg < K/32: rows are streamed in
+// several K segments), LDS bytes and workgroups per CU.
+struct GemvPlan {
+    int64_t pc_cap = 0, seg = 0, lds = 0, per_cu = 0, item_base = 0, list_cap = 0;
+    bool fits = false;   // false: a fused activation's whole row does not fit
+};
+GemvPlan plan_gemv(const MoeArgs& m, bool bucketed);
 constexpr int64_t kGemvScanMaxPairs = 4096;
 
 // Device helper.  Values every lane holds the same copy of (read from LDS or from global memory

@@ -26,10 +26,14 @@
 //     of a row (reading blocks 8 apart) hit distinct banks;
 //   * per block the integer partial is 8 v_dot4_i32_i8 on the raw nibbles
 //     started from -8*sum(q8) (exact), then one fp32 FMA with the exact scale
-//     product d4*d8; the 16 lane sums are combined with a fixed xor-shuffle
-//     tree, and K segments (only for rows longer than the staging budget) are
-//     added in order.  Nothing depends on the batch or the grid, so a row's
-//     bits do not change when the batch is split.
+//     product d4*d8.  The summation order is fixed by the row alone: in each
+//     step of 128 blocks a lane sums its 8 blocks in order from zero, the 16
+//     lane sums are combined with a fixed xor-shuffle tree, and the step sums
+//     are added in ascending order.  K segments (rows longer than the staging
+//     budget, whose length depends on the batch) start and end on step
+//     boundaries and continue the same running sum through the output, so a
+//     row's bits depend neither on the grid nor on the batch: split halves of
+//     a batch reproduce it bit for bit.
 // The pair list of an expert is either scanned from topk_ids (small batches)
 // or read from the bucketed list.  Masked pairs (ids outside [0, E)) form one
 // more "expert" whose items write zero rows.
@@ -334,9 +338,10 @@ __device__ __forceinline__ void stream_tiles(const GemvParams& p, int64_t e, int
         }
     };
 
-    float acc[kJ];
+    float acc[kJ];   // this lane's sum over its blocks of the current step
+    float rs[kJ];    // the row's running sum over the steps so far
 #pragma unroll
-    for (int j = 0; j < kJ; ++j) acc[j] = 0.0f;
+    for (int j = 0; j < kJ; ++j) acc[j] = rs[j] = 0.0f;
 
     // Steps: (tile t, first group ws of the step); the loads of the next step
     // are in flight while the current one is computed.  Past the range the
@@ -355,6 +360,15 @@ __device__ __forceinline__ void stream_tiles(const GemvParams& p, int64_t e, int
     }
     while (t < t1) {
         const int64_t n = kFused ? col_of(t) : row_of(t);
+        if constexpr (kMultiSeg && !kPartials) {
+            // a later K segment continues the running sum that the earlier
+            // segments left in the output (same order as one segment)
+            if (sb > 0 && ws == gbeg) {
+#pragma unroll
+                for (int j = 0; j < kJ; ++j)
+                    rs[j] = (n < p.N && (NPC > 0 || j < npc)) ? p.out[(int64_t)plist[j] * p.N + n] : 0.0f;
+            }
+        }
         wave_lds_fence();   // the previous step's reads of the buffer come first
         store_step<VEC>(wrow, l, R);
         wave_lds_fence();   // and this step's writes before its reads
@@ -415,37 +429,34 @@ __device__ __forceinline__ void stream_tiles(const GemvParams& p, int64_t e, int
                 }
             }
         }
+        if constexpr (!kPartials) {
+            // end of a step: the 16 lane sums by a fixed xor tree (every lane of
+            // the row gets the same value), added to the row's running sum
+#pragma unroll
+            for (int j = 0; j < kJ; ++j) {
+                float v = acc[j];
+                v += __shfl_xor(v, 8);
+                v += __shfl_xor(v, 4);
+                v += __shfl_xor(v, 2);
+                v += __shfl_xor(v, 1);
+                acc[j] = 0.0f;
+                const bool first = ws == gbeg && !(kMultiSeg && sb > 0);
+                rs[j] = first ? v : rs[j] + v;
+            }
+        }
         if (t2 != t) {   // the tile's rows are complete (wave-uniform)
             if constexpr (kFused) {
 #pragma unroll
                 for (int j = 0; j < kJ; ++j) {
-                    float v = acc[j];
-                    v += __shfl_xor(v, 8);
-                    v += __shfl_xor(v, 4);
-                    v += __shfl_xor(v, 2);
-                    v += __shfl_xor(v, 1);
+                    const float v = rs[j];
                     const float up = __shfl_xor(v, 32);
-                    acc[j] = 0.0f;
                     if (n < p.half && rw < 2 && l == 0 && (NPC > 0 || j < npc))
                         p.out[(int64_t)plist[j] * p.half + n] = gated_act(p.act, v) * up;
                 }
             } else if constexpr (!kPartials) {
 #pragma unroll
                 for (int j = 0; j < kJ; ++j) {
-                    float v = acc[j];
-                    v += __shfl_xor(v, 8);
-                    v += __shfl_xor(v, 4);
-                    v += __shfl_xor(v, 2);
-                    v += __shfl_xor(v, 1);
-                    acc[j] = 0.0f;
-                    if (n < p.N && l == 0 && (NPC > 0 || j < npc)) {
-                        float* o = p.out + (int64_t)plist[j] * p.N + n;
-                        if constexpr (kMultiSeg) {
-                            *o = sb == 0 ? v : *o + v;
-                        } else {
-                            *o = v;
-                        }
-                    }
+                    if (n < p.N && l == 0 && (NPC > 0 || j < npc)) p.out[(int64_t)plist[j] * p.N + n] = rs[j];
                 }
             }
         }
@@ -697,6 +708,61 @@ int launch_wtype(int wtype, int vec, const GemvParams& gp, size_t lds, hipStream
 
 }  // namespace
 
+GemvPlan plan_gemv(const MoeArgs& m, bool bucketed)
+{
+    GemvPlan g{};
+    const int64_t nb = m.K / kQK;
+    const int64_t pairs = m.T * m.top_k;
+    g.list_cap = bucketed ? 0 : pairs;   // scan mode: the caller keeps pairs <= kGemvScanMaxPairs
+    // a bucket never holds more than T*top_k pairs
+    g.pc_cap = std::min<int64_t>(kPairChunk, std::max<int64_t>(pairs, 1));
+    // K segment: whole rows when the staged activations fit next to the weight
+    // buffers with the chosen workgroups per CU (below), else the largest
+    // multiple of a step (128 blocks) that fits, so that every step is full
+    const int64_t fixed = lds_layout(m.wtype, m.E, 0, 0, g.list_cap).bytes;
+    auto act_bytes_pc = [&](int64_t seg, int64_t pc) { return code_bytes(seg, pc) + ent_bytes(seg, pc); };
+    auto act_bytes = [&](int64_t seg) { return act_bytes_pc(seg, g.pc_cap); };
+    const int64_t avg_pairs = std::max<int64_t>(1, (pairs + m.E - 1) / m.E);
+    // Three workgroups per CU (more streams in flight) when whole activation
+    // rows of the pairs an expert is likely to hold still fit, at least
+    // max(4, 2 * the average per expert) of them, so that an expert's weights
+    // are still streamed once; else two, with more pairs per pass.
+    int64_t budget = std::max<int64_t>(kLdsPerCU / kTargetWGPerCU - fixed, 0);
+    {
+        const int64_t budget3 = std::max<int64_t>(kLdsPerCU / 3 - fixed, 0);
+        int64_t pc3 = g.pc_cap;
+        while (pc3 > 1 && act_bytes_pc(nb, pc3) > budget3) --pc3;
+        const int64_t want = std::min<int64_t>(g.pc_cap, std::max<int64_t>(4, 2 * avg_pairs));
+        if (act_bytes_pc(nb, pc3) <= budget3 && pc3 >= want) budget = budget3;
+    }
+    // fewer pairs per pass, down to the average per expert, rather than one
+    // workgroup per CU (larger weight blocks leave less room for the rows)
+    while (g.pc_cap > avg_pairs && act_bytes(nb) > budget) --g.pc_cap;
+    if (m.act) {
+        // the activation is applied once a row's sum is complete: stage whole
+        // rows, with fewer pairs per pass if need be
+        while (g.pc_cap > 1 && act_bytes(nb) > budget) --g.pc_cap;
+        if (act_bytes(nb) > budget) {
+            g.fits = false;
+            return g;
+        }
+    }
+    if (act_bytes(nb) <= budget) {
+        g.seg = nb;
+    } else {
+        int64_t seg = kStepBlocks;
+        while (seg + kStepBlocks < nb && act_bytes(seg + kStepBlocks) <= budget) seg += kStepBlocks;
+        g.seg = seg;
+    }
+    g.lds = lds_layout(m.wtype, m.E, g.seg, g.pc_cap, g.list_cap).bytes;
+    // workgroups resident per CU (LDS and registers permitting)
+    const int64_t by_lds = std::max<int64_t>(1, kLdsPerCU / g.lds);
+    g.per_cu = std::min<int64_t>(by_lds, kWavesPerSimd * 4 / kWaves);
+    g.item_base = g.per_cu >= 3 ? kItemBase3PerCU : kItemBase2PerCU;
+    g.fits = true;
+    return g;
+}
+
 int run_gemv(const MoeArgs& m, const BucketPlan* plan, const void* ws, hipStream_t s)
 {
     GemvParams gp{};
@@ -724,58 +790,20 @@ int run_gemv(const MoeArgs& m, const BucketPlan* plan, const void* ws, hipStream
         const uint8_t* base = static_cast<const uint8_t*>(ws);
         gp.offsets = reinterpret_cast<const int32_t*>(base + plan->off_offsets);
         gp.sorted = reinterpret_cast<const int32_t*>(base + plan->off_sorted);
-        gp.list_cap = 0;
-    } else {
-        gp.list_cap = (int)gp.pairs;   // the caller keeps pairs <= kGemvScanMaxPairs
     }
-    // a bucket never holds more than T*top_k pairs
-    gp.pc_cap = (int)std::min<int64_t>(kPairChunk, gp.pairs);
-    // K segment: whole rows when the staged activations fit next to the weight
-    // buffers with the chosen workgroups per CU (below), else the largest
-    // multiple of a step (128 blocks) that fits, so that every step is full
-    const int64_t fixed = lds_layout(m.wtype, m.E, 0, 0, gp.list_cap).bytes;
-    auto act_bytes_pc = [&](int64_t seg, int64_t pc) { return code_bytes(seg, pc) + ent_bytes(seg, pc); };
-    auto act_bytes = [&](int64_t seg) { return act_bytes_pc(seg, gp.pc_cap); };
-    const int64_t avg_pairs = std::max<int64_t>(1, (gp.pairs + m.E - 1) / m.E);
-    // Three workgroups per CU (more streams in flight) when whole activation
-    // rows of the pairs an expert is likely to hold still fit, at least
-    // max(4, 2 * the average per expert) of them, so that an expert's weights
-    // are still streamed once; else two, with more pairs per pass.
-    int64_t budget = std::max<int64_t>(kLdsPerCU / kTargetWGPerCU - fixed, 0);
-    {
-        const int64_t budget3 = std::max<int64_t>(kLdsPerCU / 3 - fixed, 0);
-        int64_t pc3 = gp.pc_cap;
-        while (pc3 > 1 && act_bytes_pc(gp.nb, pc3) > budget3) --pc3;
-        const int64_t want = std::min<int64_t>(gp.pc_cap, std::max<int64_t>(4, 2 * avg_pairs));
-        if (act_bytes_pc(gp.nb, pc3) <= budget3 && pc3 >= want) budget = budget3;
+    const GemvPlan g = plan_gemv(m, bucketed);
+    if (!g.fits) {
+        set_error("fused activation on the GEMV path: one activation row of K = %lld does not fit on chip",
+                  (long long)m.K);
+        return FTQ_ERR_UNSUPPORTED;
     }
-    // fewer pairs per pass, down to the average per expert, rather than one
-    // workgroup per CU (larger weight blocks leave less room for the rows)
-    while (gp.pc_cap > avg_pairs && act_bytes(gp.nb) > budget) --gp.pc_cap;
-    if (m.act) {
-        // the activation is applied once a row's sum is complete: stage whole
-        // rows, with fewer pairs per pass if need be
-        while (gp.pc_cap > 1 && act_bytes(gp.nb) > budget) --gp.pc_cap;
-        if (act_bytes(gp.nb) > budget) {
-            set_error("fused activation on the GEMV path: one activation row of K = %lld does not fit on chip",
-                      (long long)m.K);
-            return FTQ_ERR_UNSUPPORTED;
-        }
-    }
-    if (act_bytes(gp.nb) <= budget) {
-        gp.seg = gp.nb;
-    } else {
-        int64_t seg = kStepBlocks;
-        while (seg + kStepBlocks < gp.nb && act_bytes(seg + kStepBlocks) <= budget) seg += kStepBlocks;
-        gp.seg = seg;
-    }
-    const int64_t lds = lds_layout(m.wtype, m.E, gp.seg, gp.pc_cap, gp.list_cap).bytes;
-    // grid: the workgroups that are resident at once (LDS and registers permitting)
-    const int64_t by_lds = std::max<int64_t>(1, kLdsPerCU / lds);
-    const int64_t per_cu = std::min<int64_t>(by_lds, kWavesPerSimd * 4 / kWaves);
-    gp.item_base = per_cu >= 3 ? kItemBase3PerCU : kItemBase2PerCU;
+    gp.list_cap = (int)g.list_cap;
+    gp.pc_cap = (int)g.pc_cap;
+    gp.seg = g.seg;
+    gp.item_base = g.item_base;
+    const int64_t lds = g.lds;
     const int64_t max_items = (std::min<int64_t>(m.E, gp.pairs) + 1) * gp.row_tiles;
-    gp.grid = std::max<int64_t>(1, std::min<int64_t>((int64_t)lim.cu_count * per_cu, max_items));
+    gp.grid = std::max<int64_t>(1, std::min<int64_t>((int64_t)lim.cu_count * g.per_cu, max_items));
     // widest load unit that keeps every step aligned: 16 bytes when K/32 is a
     // multiple of 8 (whole lane groups), 4 when every block boundary that a
     // step starts or ends on is 4-byte aligned, else 2 (Q4_0 only)

@@ -31,7 +31,7 @@ EXPORTS = (
     "ftq_moe_q4_0_q8_1_act", "ftq_moe_q4_0_q8_1_act_routed",
     "ftq_moe_gguf_q8_1", "ftq_moe_gguf_q8_1_partials",
     "ftq_last_error", "ftq_version",
-    "ftq_debug_force_block_threads",
+    "ftq_debug_force_block_threads", "ftq_debug_gemv_plan",
 )
 
 
@@ -88,6 +88,8 @@ def lib() -> ctypes.CDLL:
     L.ftq_version.restype = ctypes.c_char_p
     L.ftq_debug_force_block_threads.argtypes = [I32]
     L.ftq_debug_force_block_threads.restype = None
+    L.ftq_debug_gemv_plan.argtypes = [I64, I64, I64, I64, I64, I32, I32, P, P, P]
+    L.ftq_debug_gemv_plan.restype = I32
     _lib = L
     return L
 
@@ -146,6 +148,15 @@ def quantize_q4_0(w: torch.Tensor, out: torch.Tensor | None = None, stream=None)
     _check(lib().ftq_quantize_q4_0(_dev(w, "w", torch.float32), rows, K, _out(out, rows * (K // QK) * Q4_0_BYTES, "out", torch.uint8),
                                    _stream(stream)))
     return out
+
+
+def gemv_plan(E: int, N: int, K: int, T: int, top_k: int, wtype: int = 2, act: int = 0) -> dict:
+    """The GEMV path's on-chip plan for these sizes (host arithmetic): K blocks
+    per segment, activation rows per pass, workgroups per CU."""
+    seg, pc, per_cu = ctypes.c_int64(), ctypes.c_int64(), ctypes.c_int64()
+    _check(lib().ftq_debug_gemv_plan(E, N, K, T, top_k, wtype, act, ctypes.addressof(seg), ctypes.addressof(pc),
+                                     ctypes.addressof(per_cu)))
+    return {"seg": seg.value, "pairs_per_pass": pc.value, "wg_per_cu": per_cu.value}
 
 
 def select_path(E: int, N: int, K: int, T: int, top_k: int) -> int:

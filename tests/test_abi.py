@@ -149,3 +149,30 @@ def test_pairs_and_combine_validate_before_any_launch():
     for T_, k_, N_ in ((-1, 2, 16), (3, 0, 16), (3, 2, 0)):
         assert L.ftq_moe_combine_topk(base, base, base, T_, k_, N_, None) == ftq.ERR_INVALID_ARG
     assert L.ftq_moe_combine_topk(base, base, base, 2 ** 40, 8, 2 ** 20, None) == ftq.ERR_UNSUPPORTED
+
+
+# Mixtral down projection (mlxcel PR #652, Summary: mixtral-8x7b; the second
+# layer's K is the expert width 14336): at T = 12 and 16 an expert holds 3-4
+# pairs and their staged rows exceed the LDS budget, so the GEMV streams each
+# row in K segments.  The GPU tests of those shapes rely on this plan.
+KSEG_SHAPES = [(8, 4096, 14336, 12, 2), (8, 4096, 14336, 16, 2), (8, 96, 14336, 16, 2), (4, 48, 20480, 8, 2)]
+
+
+@pytest.mark.parametrize("shape", KSEG_SHAPES)
+def test_gemv_plan_streams_long_rows_in_segments(shape):
+    E, N, K, T, k = shape
+    plan = ftq.gemv_plan(E, N, K, T, k)
+    nb = K // 32
+    assert plan["seg"] < nb and plan["seg"] % 128 == 0, plan
+    assert plan["pairs_per_pass"] >= 3
+
+
+def test_gemv_plan_one_segment_for_decode_rows():
+    # the halves of the T = 16 batch (T = 8) stage whole rows: one segment
+    assert ftq.gemv_plan(8, 4096, 14336, 8, 2)["seg"] == 14336 // 32
+    assert ftq.gemv_plan(8, 14336, 4096, 1, 2)["seg"] == 4096 // 32
+    assert ftq.gemv_plan(128, 1408, 2816, 16, 8)["seg"] == 2816 // 32
+    # a fused activation needs whole rows: one segment or an error
+    assert ftq.gemv_plan(8, 28672, 4096, 8, 2, act=1)["seg"] == 4096 // 32
+    with pytest.raises(ftq.FtqError):
+        ftq.gemv_plan(8, 64, 33056 + 32, 1, 2, act=1)

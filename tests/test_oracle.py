@@ -427,6 +427,48 @@ def test_gelu_tanh_identities_and_distance_to_erf_gelu():
     assert abs(oracle.act(oracle.ACT_GELU_TANH, 9.0) - 9.0) < 1e-12       # saturates to x
 
 
+def _act_grid():
+    rng = np.random.default_rng(11)
+    return np.concatenate([np.linspace(-9.0, 9.0, 1801), rng.standard_normal(2000) * 3, [-20.0, -0.0, 20.0]])
+
+
+def test_activations_match_torch_float64_to_a_few_ulps():
+    """The oracle's SiLU and tanh-form GELU against torch's own float64
+    implementations (an independent code base): agreement within a few fp64
+    ulps of (|x| + 1) everywhere on a grid over +-9 and random points pins
+    every constant of both formulas (FreeToken PR #185, Problem: the
+    gelu_tanh_and_mul after the GEMV; "Current Bug: CuTeDSLMoERunner", Bug 6:
+    SiLU * up)."""
+    import torch
+    import torch.nn.functional as F
+    xs = _act_grid()
+    tol = 32 * U64 * (np.abs(xs) + 1)
+    tx = torch.from_numpy(xs)
+    ref_gelu = F.gelu(tx, approximate="tanh").numpy()
+    ref_silu = F.silu(tx).numpy()
+    g = np.array([oracle.act(oracle.ACT_GELU_TANH, x) for x in xs])
+    s = np.array([oracle.act(oracle.ACT_SILU, x) for x in xs])
+    assert np.all(np.abs(g - ref_gelu) <= tol)
+    assert np.all(np.abs(s - ref_silu) <= tol)
+
+
+def test_activation_pin_rejects_mistyped_constants():
+    """The tolerance of the torch comparison is tight enough that a dropped
+    digit of the cubic coefficient or a rounded sqrt(2/pi) fails it (the
+    distance-to-erf check alone passes 0.0447 and 0.04471)."""
+    import torch
+    import torch.nn.functional as F
+    xs = _act_grid()
+    tol = 32 * U64 * (np.abs(xs) + 1)
+    ref = F.gelu(torch.from_numpy(xs), approximate="tanh").numpy()
+    k = np.sqrt(2.0 / np.pi)
+    for kk, c in ((k, 0.0447), (k, 0.04471), (0.8, 0.044715), (k, 0.44715)):
+        wrong = 0.5 * xs * (1.0 + np.tanh(kk * (xs + c * xs ** 3)))
+        assert np.any(np.abs(wrong - ref) > tol), (kk, c)
+    right = 0.5 * xs * (1.0 + np.tanh(k * (xs + 0.044715 * xs ** 3)))
+    assert np.all(np.abs(right - ref) <= tol)
+
+
 def test_act_and_mul_takes_gate_from_the_first_half():
     y = np.array([[np.log(3.0), -1.0, 2.0, 5.0],
                   [0.0, 2.5, 7.0, -3.0]])
