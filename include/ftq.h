@@ -168,6 +168,26 @@ int ftq_moe_q4_0_q8_1(const void* w, const void* a, const int32_t* topk_ids, flo
                       void* workspace, size_t workspace_bytes, int path, hipStream_t stream);
 
 /*
+ * ftq_moe_q4_0_q8_1 for callers that cannot allocate device memory: code under
+ * HIP graph capture, tight serving loops, harnesses that forbid hipMalloc.  It
+ * takes no workspace argument: the workspace that ftq_moe_q4_0_q8_1 would need
+ * lives in a fixed 4 MiB array that the library holds on each device it runs
+ * on, until the process ends.  Arguments, results, path choice and errors are
+ * those of ftq_moe_q4_0_q8_1 (the results are bit-identical to it), and:
+ *   - FTQ_ERR_UNSUPPORTED when ftq_moe_workspace_bytes(E, N, K, T, top_k, path)
+ *     exceeds 4 MiB (e.g. above about 900 000 pairs with 128 experts);
+ *   - FTQ_ERR_HIP if the array's device address cannot be obtained (looked up
+ *     once per device, on the first call with that device current).
+ * Nothing is allocated or freed and nothing needs clearing between calls.  All
+ * calls on one device share the array: calls that may overlap on one device
+ * (several streams or host threads) race on it and must be serialised by the
+ * caller.
+ */
+int ftq_moe_q4_0_q8_1_noalloc(const void* w, const void* a, const int32_t* topk_ids, float* out,
+                              int64_t E, int64_t N, int64_t K, int64_t T, int64_t top_k, int path,
+                              hipStream_t stream);
+
+/*
  * The same matmul split in two, so that one routing can serve several matmuls
  * over the same (token, top-k) pairs (e.g. an expert FFN's up- and
  * down-projections) and each half can be timed on its own.

@@ -219,6 +219,30 @@ int64_t workspace_bytes(int64_t E, int64_t N, int64_t K, int64_t T, int64_t top_
 }
 
 }  // namespace
+
+int moe_q4_0_q8_1_call(const void* w, const void* a, const int32_t* ids, float* out, int64_t E, int64_t N, int64_t K,
+                       int64_t T, int64_t top_k, void* ws, size_t ws_bytes, int path, hipStream_t stream)
+{
+    return moe_common(w, a, ids, out, nullptr, E, N, K, T, top_k, ws, ws_bytes, path, stream, kRoute | kMatmul);
+}
+
+int64_t moe_workspace_need(int64_t E, int64_t N, int64_t K, int64_t T, int64_t top_k, int path, int* status)
+{
+    clear_error();
+    *status = check_sizes(E, N, K, T, top_k);
+    if (*status != FTQ_OK) return -1;
+    const int rp = resolve_path(path, E, T, top_k);
+    if (rp < 0) {
+        set_error("unknown path %d", path);
+        *status = FTQ_ERR_INVALID_ARG;
+        return -1;
+    }
+    if (T == 0) return 0;
+    bool bucketed = false;
+    const BucketPlan plan = plan_for(rp, E, N, K, T, top_k, &bucketed);
+    return bucketed ? plan.bytes : 0;
+}
+
 }  // namespace ftq
 
 using namespace ftq;

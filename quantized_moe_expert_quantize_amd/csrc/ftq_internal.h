@@ -148,6 +148,13 @@ __device__ __forceinline__ int64_t uniform(int64_t v)
 int run_grouped(const MoeArgs& m, const BucketPlan& plan, void* ws, hipStream_t s);
 int64_t grouped_tile_m(const MoeArgs& m);
 
+// ftq_moe_q4_0_q8_1 with its validation, for entry points that supply the
+// workspace themselves; and the workspace it needs (status: FTQ_OK or the
+// validation error).
+int moe_q4_0_q8_1_call(const void* w, const void* a, const int32_t* ids, float* out, int64_t E, int64_t N, int64_t K,
+                       int64_t T, int64_t top_k, void* ws, size_t ws_bytes, int path, hipStream_t stream);
+int64_t moe_workspace_need(int64_t E, int64_t N, int64_t K, int64_t T, int64_t top_k, int path, int* status);
+
 // Top-k weighted combine of per-pair rows into per-token rows.
 int run_combine_topk(const float* y, const float* gates, float* out, int64_t T, int64_t top_k, int64_t N,
                      hipStream_t s);

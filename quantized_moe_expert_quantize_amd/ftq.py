@@ -31,7 +31,7 @@ EXPORTS = (
     "ftq_moe_q4_0_q8_1_act", "ftq_moe_q4_0_q8_1_act_routed",
     "ftq_moe_gguf_q8_1", "ftq_moe_gguf_q8_1_partials",
     "ftq_last_error", "ftq_version",
-    "ftq_debug_force_block_threads", "ftq_debug_gemv_plan",
+    "ftq_debug_force_block_threads", "ftq_debug_gemv_plan", "ftq_moe_q4_0_q8_1_noalloc",
 )
 
 
@@ -90,6 +90,8 @@ def lib() -> ctypes.CDLL:
     L.ftq_debug_force_block_threads.restype = None
     L.ftq_debug_gemv_plan.argtypes = [I64, I64, I64, I64, I64, I32, I32, P, P, P]
     L.ftq_debug_gemv_plan.restype = I32
+    L.ftq_moe_q4_0_q8_1_noalloc.argtypes = [P, P, P, P, I64, I64, I64, I64, I64, I32, P]
+    L.ftq_moe_q4_0_q8_1_noalloc.restype = I32
     _lib = L
     return L
 
@@ -207,6 +209,18 @@ def moe(w: torch.Tensor, a: torch.Tensor, topk_ids: torch.Tensor, E: int, N: int
         _dev(w, "w", torch.uint8), _dev(a, "a", torch.uint8), _dev(topk_ids, "topk_ids", torch.int32),
         _out(out, T * top_k * N, "out", torch.float32), E, N, K, T, top_k,
         ws.data_ptr() if ws is not None else None, ws_n, path, _stream(stream)))
+    return out
+
+
+def moe_noalloc(w: torch.Tensor, a: torch.Tensor, topk_ids: torch.Tensor, E: int, N: int, K: int,
+                out: torch.Tensor, path: int = PATH_AUTO, stream=None) -> torch.Tensor:
+    """moe() through ftq_moe_q4_0_q8_1_noalloc: no workspace, the library's
+    fixed per-device scratch instead.  `out` is the caller's (nothing here
+    allocates device memory)."""
+    T, top_k = _moe_args(w, a, topk_ids, E, N, K)
+    _check(lib().ftq_moe_q4_0_q8_1_noalloc(
+        _dev(w, "w", torch.uint8), _dev(a, "a", torch.uint8), _dev(topk_ids, "topk_ids", torch.int32),
+        _out(out, T * top_k * N, "out", torch.float32), E, N, K, T, top_k, path, _stream(stream)))
     return out
 
 
