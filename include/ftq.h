@@ -368,6 +368,19 @@ const char* ftq_version(void);
 void ftq_debug_force_block_threads(int threads);
 
 /*
+ * Comparison hook: which kernel the grouped path launches for later calls on
+ * this host thread.  0 (the default): exact block partials on int8 MFMAs
+ * (v_mfma_i32_32x32x32_i8 on the nibble codes minus 8 and the Q8_1 codes),
+ * converted to fp32 before the scale FMA.  1: the same partials as two fp16
+ * MFMAs (the codes are exact in fp16).  2: the fp16 partials in a
+ * warp-specialised kernel (loader and MMA waves paced by LDS counters instead
+ * of workgroup barriers; 128-row tiles only, else as 1).  All three produce
+ * the same integer partials and the same fp32 outputs bit for bit; they differ
+ * in speed only.  Returns FTQ_OK, or FTQ_ERR_INVALID_ARG for another value.
+ */
+int ftq_debug_grouped_kernel(int variant);
+
+/*
  * Checking aid: the on-chip plan the GEMV path makes for these sizes, host
  * arithmetic only (no device is touched).  *seg: K/32 blocks staged per
  * segment (less than K/32 when a row is streamed in several K segments, which

@@ -88,9 +88,10 @@ __device__ __forceinline__ int32_t block_exclusive_scan(int32_t v, int32_t& carr
 // pairs) and the exclusive scan of per-bucket tile counts.
 __global__ __launch_bounds__(kScanThreads) void bucket_scan_kernel(
     int32_t* __restrict__ counts, int64_t nchunks, int32_t nbuckets, int32_t tile_m,
-    int32_t* __restrict__ offsets, int32_t* __restrict__ tiles)
+    int32_t* __restrict__ offsets, int32_t* __restrict__ tiles, int4* __restrict__ tdesc)
 {
-    extern __shared__ int32_t off_lds[];          // [nbuckets + 1] bucket offsets
+    extern __shared__ int32_t off_lds[];          // [nbuckets + 1] bucket offsets, then [nbuckets + 1] tile offsets
+    int32_t* tiles_lds = off_lds + nbuckets + 1;
     __shared__ int32_t wsum[kScanWaves + 1];
     const int64_t len = (int64_t)nbuckets * nchunks;
     int32_t carry = 0;
@@ -129,9 +130,28 @@ __global__ __launch_bounds__(kScanThreads) void bucket_scan_kernel(
         const int32_t n = b < nbuckets ? off_lds[b + 1] - off_lds[b] : 0;
         const int32_t t = tile_m > 0 ? (int32_t)(((uint32_t)n + (uint32_t)tile_m - 1u) / (uint32_t)tile_m) : 0;
         const int32_t r = block_exclusive_scan(t, tcarry, wsum);
-        if (b < nbuckets) tiles[b] = r;
+        if (b < nbuckets) {
+            tiles[b] = r;
+            tiles_lds[b] = r;
+        }
     }
-    if (threadIdx.x == 0) tiles[nbuckets] = tcarry;
+    if (threadIdx.x == 0) {
+        tiles[nbuckets] = tcarry;
+        tiles_lds[nbuckets] = tcarry;
+    }
+    if (tile_m <= 0) return;
+    __syncthreads();
+    // One descriptor per tile {bucket, first slot, rows, 0}, so that the matmul
+    // finds a tile's expert and pairs with one load instead of a search.
+    for (int32_t mt = threadIdx.x; mt < tcarry; mt += kScanThreads) {
+        int lo = 0, hi = nbuckets;   // the last bucket b with tiles[b] <= mt
+        while (hi - lo > 1) {
+            const int mid = (lo + hi) >> 1;
+            if (tiles_lds[mid] <= mt) lo = mid; else hi = mid;
+        }
+        const int32_t slot0 = off_lds[lo] + (mt - tiles_lds[lo]) * tile_m;
+        tdesc[mt] = int4{lo, slot0, min(tile_m, off_lds[lo + 1] - slot0), 0};
+    }
 }
 
 // Lanes of a wave share the per-bucket counters in LDS; the hardware keeps a
@@ -209,6 +229,9 @@ BucketPlan make_bucket_plan(int64_t pairs, int64_t E, int64_t tile_m)
     p.off_offsets = off; off = align(off + 4 * (p.buckets + 1));
     p.off_tiles = off;   off = align(off + 4 * (p.buckets + 1));
     p.off_sorted = off;  off = align(off + 4 * pairs);
+    // tile descriptors: at most sum over buckets of ceil(count / tile_m) tiles
+    p.max_tiles = tile_m > 0 ? (pairs + p.buckets * (tile_m - 1)) / tile_m : 0;
+    p.off_tdesc = off;   off = align(off + 16 * p.max_tiles);
     p.bytes = off;
     return p;
 }
@@ -221,12 +244,13 @@ int run_bucket(const int32_t* ids, int64_t E, const BucketPlan& plan, void* ws, 
     int32_t* offsets = reinterpret_cast<int32_t*>(base + plan.off_offsets);
     int32_t* tiles = reinterpret_cast<int32_t*>(base + plan.off_tiles);
     int32_t* sorted = reinterpret_cast<int32_t*>(base + plan.off_sorted);
+    int4* tdesc = reinterpret_cast<int4*>(base + plan.off_tdesc);
     const int32_t nb = (int32_t)plan.buckets;
     int st = launch("bucket_count_kernel", bucket_count_kernel, plan.chunks, kCountThreads,
                     sizeof(int32_t) * nb, s, ids, plan.pairs, (int32_t)E, nb, plan.chunks, counts);
     if (st != FTQ_OK) return st;
-    st = launch("bucket_scan_kernel", bucket_scan_kernel, 1, kScanThreads, sizeof(int32_t) * (nb + 1), s,
-                counts, plan.chunks, nb, (int32_t)plan.tile_m, offsets, tiles);
+    st = launch("bucket_scan_kernel", bucket_scan_kernel, 1, kScanThreads, sizeof(int32_t) * 2 * (nb + 1), s,
+                counts, plan.chunks, nb, (int32_t)plan.tile_m, offsets, tiles, tdesc);
     if (st != FTQ_OK) return st;
     return launch("bucket_scatter_kernel", bucket_scatter_kernel, (plan.chunks + kScatterWaves - 1) / kScatterWaves,
                   64 * kScatterWaves, sizeof(int32_t) * 2 * kScatterWaves * nb, s, ids, plan.pairs, (int32_t)E, nb,

@@ -10,6 +10,7 @@ namespace ftq {
 namespace {
 thread_local std::string g_error;
 thread_local int g_forced_threads = 0;
+thread_local int g_grouped_variant = kGroupedI8;
 
 constexpr int kMaxDevices = 64;
 std::mutex g_lim_mu;
@@ -34,6 +35,8 @@ void set_error(const char* fmt, ...)
 void clear_error() { g_error.clear(); }
 
 int forced_block_threads() { return g_forced_threads; }
+
+int grouped_kernel_variant() { return g_grouped_variant; }
 
 int device_limits(DeviceLimits* out)
 {
@@ -403,6 +406,17 @@ const char* ftq_last_error(void) { return g_error.c_str(); }
 const char* ftq_version(void) { return "ftq 0.1.0 gfx950"; }
 
 void ftq_debug_force_block_threads(int threads) { g_forced_threads = threads > 0 ? threads : 0; }
+
+int ftq_debug_grouped_kernel(int variant)
+{
+    clear_error();
+    if (variant < kGroupedI8 || variant > kGroupedF16Ws) {
+        set_error("grouped kernel variant %d: expected 0 (int8), 1 (fp16) or 2 (fp16, warp-specialised)", variant);
+        return FTQ_ERR_INVALID_ARG;
+    }
+    g_grouped_variant = variant;
+    return FTQ_OK;
+}
 
 int ftq_debug_gemv_plan(int64_t E, int64_t N, int64_t K, int64_t T, int64_t top_k, int wtype, int act, int64_t* seg,
                         int64_t* pairs_per_pass, int64_t* wg_per_cu)

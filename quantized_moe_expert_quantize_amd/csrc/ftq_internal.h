@@ -32,6 +32,9 @@ struct DeviceLimits {
 int device_limits(DeviceLimits* out);   // FTQ_OK or FTQ_ERR_HIP
 
 int forced_block_threads();             // test hook value (0 = off)
+// grouped-path kernel choice (ftq_debug_grouped_kernel; int8 MFMAs by default)
+enum GroupedKernel { kGroupedI8 = 0, kGroupedF16 = 1, kGroupedF16Ws = 2 };
+int grouped_kernel_variant();
 
 // Launch `kernel` with a 1-D grid, after checking the geometry against the
 // device limits, and check the launch right after it is issued.  `name`
@@ -86,6 +89,8 @@ struct BucketPlan {
     int64_t off_offsets = 0;  // int32 [buckets + 1]: start slot of each bucket
     int64_t off_tiles = 0;    // int32 [buckets + 1]: first tile of each bucket
     int64_t off_sorted = 0;   // int32 [pairs]: pair ids grouped by bucket, ascending within one
+    int64_t max_tiles = 0;    // grouped tiles at most (0: no tile table)
+    int64_t off_tdesc = 0;    // int32x4 [max_tiles]: per tile {bucket, first slot, rows, 0}
     int64_t bytes = 0;
 };
 constexpr int kBucketChunk = 1024;   // pairs per wave in the counting and scatter passes

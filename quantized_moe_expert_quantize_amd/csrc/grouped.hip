@@ -59,6 +59,8 @@ typedef _Float16 v4h __attribute__((ext_vector_type(4)));
 typedef _Float16 h2 __attribute__((ext_vector_type(2)));
 typedef float v16f __attribute__((ext_vector_type(16)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef int v4i __attribute__((ext_vector_type(4)));
+typedef int v16i __attribute__((ext_vector_type(16)));
 
 constexpr int kThreads = 256;
 constexpr int kBN = 128;          // weight rows per tile
@@ -79,6 +81,20 @@ constexpr int kBufferFlags = 0x00020000;      // raw buffer resource: 32-bit dat
 __device__ __forceinline__ int row_swizzle(int r) { return (r & 7) ^ ((r >> 3) & 1); }
 __device__ __forceinline__ int lds_chunk(int r, int c) { return r * kRowBytes + ((c ^ row_swizzle(r)) << 4); }
 
+// int8 variant: a staged row is the 2 x 32 int8 codes of a pass (64 bytes, 4
+// chunks); chunk c of row r sits at chunk c ^ ((r >> 1) & 3), so that 8
+// consecutive rows reading one logical chunk cover all 8 16-byte slots of 128
+// bytes (2 rows per 128 bytes, 4 chunk positions).
+constexpr int kRowBytesI8 = kKB * 32;
+__device__ __forceinline__ int row_swizzle_i8(int r) { return (r >> 1) & 3; }
+__device__ __forceinline__ int lds_chunk_i8(int r, int c) { return r * kRowBytesI8 + ((c ^ row_swizzle_i8(r)) << 4); }
+
+// Four Q4_0 nibbles (the low or high nibbles of four bytes, already masked to
+// 0..15) to the signed int8 values q - 8 in the same bytes: v + 0x78 stays
+// below 0x100 in every byte (no carries), and flipping bit 7 then gives
+// v - 8 modulo 256.
+__device__ __forceinline__ uint32_t nibbles_minus8(uint32_t v) { return (v + 0x78787878u) ^ 0x80808080u; }
+
 // Buffer resource over `range` bytes from `base` (range: a 32-bit unsigned
 // count carried in an int).  Both arguments must be wave-uniform: a resource
 // the compiler thinks divergent costs a loop per load.
@@ -95,6 +111,7 @@ struct GroupedParams {
     const int32_t* offsets;   // [E+2]
     const int32_t* tiles;     // [E+2]
     const int32_t* sorted;
+    const int4* tdesc;        // per M tile {bucket, first slot, rows, 0}
     int64_t E, N, nb, top_k, nbuckets, n_tiles_n, max_mt;
     int64_t act_div;          // activation row of pair p: p / act_div
     int32_t a_range;          // bytes of a (32-bit unsigned count; narrow variant only: below 4 GiB)
@@ -123,10 +140,15 @@ struct Shape {
     static_assert(SM >= 1 && SN >= 1, "tile shape");
 };
 
-template <int BM>
+template <int BM, bool kI8 = false>
 struct Smem {
-    uint8_t a[2][BM * kRowBytes];
-    uint8_t b[2][kBN * kRowBytes];
+    static constexpr int RB = kI8 ? kRowBytesI8 : kRowBytes;
+    // the fused epilogue exchanges BM x (kBN/2 + 4) floats through the stage
+    // buffers; the int8 buffers are smaller, so they are padded up to that
+    static constexpr int kStage = 2 * (BM + kBN) * RB, kExchange = BM * (kBN / 2 + 4) * 4;
+    uint8_t a[2][BM * RB];
+    uint8_t b[2][kBN * RB];
+    uint8_t pad[kExchange > kStage ? kExchange - kStage : 16];
     uint2 as[2][kKB][BM];        // {fp16 scale bits, 0} of the A rows
     uint2 bs[2][kKB][kBN + 1];   // {fp16 scale bits, 0} of the weight rows; entry kBN stays zero
     int32_t row_pair[BM];
@@ -179,12 +201,13 @@ __device__ __forceinline__ int64_t xcd_remap(int64_t bid, int64_t G)
     return xcd * q + min<int64_t>(xcd, r) + local;
 }
 
-template <int BM, int VEC, bool kWide, bool kPartials, bool kFused>
+template <int BM, int VEC, bool kWide, bool kPartials, bool kFused, bool kI8>
 __global__ __launch_bounds__(Shape<BM>::kThreads, Shape<BM>::kWavesPerSimd) void moe_grouped_kernel(GroupedParams p)
 {
     using S = Shape<BM>;
     constexpr int kThreads = S::kThreads;
-    __shared__ __align__(16) Smem<BM> sm;
+    constexpr int RB = Smem<BM, kI8>::RB;
+    __shared__ __align__(16) Smem<BM, kI8> sm;
 
     // the wave index is uniform per wave: say so, so that what derives from it
     // (sub-tile counts, loop control) stays in scalar registers
@@ -267,7 +290,7 @@ __global__ __launch_bounds__(Shape<BM>::kThreads, Shape<BM>::kWavesPerSimd) void
         const AOff a_off_g = (AOff)(((int64_t)sm.row_tok[am < rows ? am : 0] * nb + ablk) * kQ8Bytes);
         int a_lds[4];
 #pragma unroll
-        for (int j = 0; j < 4; ++j) a_lds[j] = lds_chunk(am, ablk * 4 + j);
+        for (int j = 0; j < 4; ++j) a_lds[j] = kI8 ? lds_chunk_i8(am, ablk * 2 + (j & 1)) : lds_chunk(am, ablk * 4 + j);
         // B: one block (18 B) of one weight row per thread of the first
         // kBN * kKB threads; bh is uniform per wave
         static_assert(kBN * kKB <= kThreads, "one weight block per thread");
@@ -286,7 +309,7 @@ __global__ __launch_bounds__(Shape<BM>::kThreads, Shape<BM>::kWavesPerSimd) void
         }
         int b_lds[4];
 #pragma unroll
-        for (int i = 0; i < 4; ++i) b_lds[i] = lds_chunk(bn, bh * 4 + i);
+        for (int i = 0; i < 4; ++i) b_lds[i] = kI8 ? lds_chunk_i8(bn, bh * 2 + (i & 1)) : lds_chunk(bn, bh * 4 + i);
 
         u32x4 ra0, ra1;
         uint32_t ra2;
@@ -332,15 +355,21 @@ __global__ __launch_bounds__(Shape<BM>::kThreads, Shape<BM>::kWavesPerSimd) void
         };
         auto commit = [&](int buf) {
             if (a_thread) {
-                // 32 int8 codes -> fp16 in the order of nibbles_to_f16: chunk j holds
-                // codes 4j..4j+3 (word j) and 16+4j..16+4j+3 (word 4+j)
                 const uint32_t cw[8] = {ra0.y, ra0.z, ra0.w, ra1.x, ra1.y, ra1.z, ra1.w, ra2};
+                if constexpr (kI8) {
+                    // the codes as they are: chunk 0 holds codes 0..15, chunk 1 codes 16..31
+                    *reinterpret_cast<u32x4*>(&sm.a[buf][a_lds[0]]) = u32x4{cw[0], cw[1], cw[2], cw[3]};
+                    *reinterpret_cast<u32x4*>(&sm.a[buf][a_lds[1]]) = u32x4{cw[4], cw[5], cw[6], cw[7]};
+                } else {
+                    // 32 int8 codes -> fp16 in the order of nibbles_to_f16: chunk j holds
+                    // codes 4j..4j+3 (word j) and 16+4j..16+4j+3 (word 4+j)
 #pragma unroll
-                for (int j = 0; j < 4; ++j) {
-                    uint32_t o[4];
-                    int8_pairs_to_f16(cw[j], i8_magic, o[0], o[1]);
-                    int8_pairs_to_f16(cw[4 + j], i8_magic, o[2], o[3]);
-                    *reinterpret_cast<u32x4*>(&sm.a[buf][a_lds[j]]) = u32x4{o[0], o[1], o[2], o[3]};
+                    for (int j = 0; j < 4; ++j) {
+                        uint32_t o[4];
+                        int8_pairs_to_f16(cw[j], i8_magic, o[0], o[1]);
+                        int8_pairs_to_f16(cw[4 + j], i8_magic, o[2], o[3]);
+                        *reinterpret_cast<u32x4*>(&sm.a[buf][a_lds[j]]) = u32x4{o[0], o[1], o[2], o[3]};
+                    }
                 }
                 sm.as[buf][ablk][am] = uint2{ra_ok ? (ra0.x & 0xffffu) : 0u, 0u};
             }
@@ -358,11 +387,24 @@ __global__ __launch_bounds__(Shape<BM>::kThreads, Shape<BM>::kWavesPerSimd) void
                 dbits = rb[0];
                 qs[0] = rb[1]; qs[1] = rb[2]; qs[2] = rb[3]; qs[3] = rb[4];
             }
+            if constexpr (kI8) {
+                // byte i of the nibbles holds element i (low) and i + 16 (high):
+                // chunk 0 gets elements 0..15, chunk 1 elements 16..31, as q - 8
+                u32x4 lo, hi;
 #pragma unroll
-            for (int j = 0; j < 4; ++j) {
-                uint32_t o[4];
-                nibbles_to_f16(qs[j], nib_mask, nib_magic, o);
-                *reinterpret_cast<u32x4*>(&sm.b[buf][b_lds[j]]) = u32x4{o[0], o[1], o[2], o[3]};
+                for (int j = 0; j < 4; ++j) {
+                    lo[j] = nibbles_minus8(qs[j] & 0x0f0f0f0fu);
+                    hi[j] = nibbles_minus8((qs[j] >> 4) & 0x0f0f0f0fu);
+                }
+                *reinterpret_cast<u32x4*>(&sm.b[buf][b_lds[0]]) = lo;
+                *reinterpret_cast<u32x4*>(&sm.b[buf][b_lds[1]]) = hi;
+            } else {
+#pragma unroll
+                for (int j = 0; j < 4; ++j) {
+                    uint32_t o[4];
+                    nibbles_to_f16(qs[j], nib_mask, nib_magic, o);
+                    *reinterpret_cast<u32x4*>(&sm.b[buf][b_lds[j]]) = u32x4{o[0], o[1], o[2], o[3]};
+                }
             }
             sm.bs[buf][bh][bn] = uint2{rb_ok ? dbits : 0u, 0u};
         };
@@ -376,9 +418,16 @@ __global__ __launch_bounds__(Shape<BM>::kThreads, Shape<BM>::kWavesPerSimd) void
         for (int blk = 0; blk < kKB; ++blk)
 #pragma unroll
             for (int s2 = 0; s2 < 2; ++s2) {
-                const int c = (blk * 4 + 2 * half + s2) ^ row_swizzle(l32);
-                frag_a[blk][s2] = (wm * S::SM * 32 + l32) * kRowBytes + (c << 4);
-                frag_b[blk][s2] = (wn * S::SN * 32 + l32) * kRowBytes + (c << 4);
+                if constexpr (kI8) {
+                    // one chunk per block: the lane's half of the block's 32 codes
+                    const int c = (blk * 2 + half) ^ row_swizzle_i8(l32);
+                    frag_a[blk][s2] = (wm * S::SM * 32 + l32) * RB + (c << 4);
+                    frag_b[blk][s2] = (wn * S::SN * 32 + l32) * RB + (c << 4);
+                } else {
+                    const int c = (blk * 4 + 2 * half + s2) ^ row_swizzle(l32);
+                    frag_a[blk][s2] = (wm * S::SM * 32 + l32) * kRowBytes + (c << 4);
+                    frag_b[blk][s2] = (wn * S::SN * 32 + l32) * kRowBytes + (c << 4);
+                }
             }
         const int as_row = wm * S::SM * 32 + l32;
         int bs_row[S::SN];
@@ -396,8 +445,75 @@ __global__ __launch_bounds__(Shape<BM>::kThreads, Shape<BM>::kWavesPerSimd) void
 #pragma unroll
                 for (int k = 0; k < 16; ++k) acc[i][j][k] = 0.0f;
 
+        // One staged pass, int8 codes: per sub-tile and block the exact integer
+        // partial from one v_mfma_i32_32x32x32_i8, converted to fp32 (exact:
+        // |P| < 2^24), then one FMA with the scale product from the f16 MFMA
+        auto compute_i8 = [&](int buf, int64_t kb0) {
+            if (!wave_rows) return;
+            v4i ai[kKB][S::SM], bi[kKB][S::SN];
+            v4h as_v[kKB][S::SM], bs_v[kKB][S::SN];
+#pragma unroll
+            for (int blk = 0; blk < kKB; ++blk) {
+#pragma unroll
+                for (int ii = 0; ii < S::SM; ++ii) {
+                    ai[blk][ii] = *reinterpret_cast<const v4i*>(&sm.a[buf][frag_a[blk][0] + ii * 32 * RB]);
+                    as_v[blk][ii] = __builtin_bit_cast(v4h, sm.as[buf][blk][as_row + ii * 32]);
+                }
+#pragma unroll
+                for (int jj = 0; jj < S::SN; ++jj) {
+                    bi[blk][jj] = *reinterpret_cast<const v4i*>(&sm.b[buf][frag_b[blk][0] + jj * 32 * RB]);
+                    bs_v[blk][jj] = __builtin_bit_cast(v4h, sm.bs[buf][blk][bs_row[jj]]);
+                }
+            }
+            if constexpr (kPartials) {
+#pragma unroll
+                for (int blk = 0; blk < kKB; ++blk)
+#pragma unroll
+                    for (int i = 0; i < S::SM; ++i)
+#pragma unroll
+                        for (int j = 0; j < S::SN; ++j) {
+                            const v16i P = __builtin_amdgcn_mfma_i32_32x32x32_i8(ai[blk][i], bi[blk][j], v16i{}, 0, 0, 0);
+                            const int64_t n = n0 + (wn * S::SN + j) * 32 + l32;
+                            const int64_t b = kb0 + blk;
+#pragma unroll
+                            for (int r = 0; r < 16; ++r) {
+                                const int m = (wm * S::SM + i) * 32 + 8 * (r / 4) + 4 * half + (r % 4);
+                                if (m < rows && n < p.N && b < nb)
+                                    p.partials[((int64_t)sm.row_pair[m] * p.N + n) * nb + b] = P[r];
+                            }
+                        }
+            } else {
+                constexpr int kSub = S::SM * S::SN, kSteps = kKB * kSub;
+                v16i P[2];
+                v16f Sc[2];
+                auto mm = [&](int st) {
+                    const int blk = st / kSub, t = st % kSub, i = t / S::SN, j = t % S::SN;
+                    P[st & 1] = __builtin_amdgcn_mfma_i32_32x32x32_i8(ai[blk][i], bi[blk][j], v16i{}, 0, 0, 0);
+                    Sc[st & 1] = __builtin_amdgcn_mfma_f32_32x32x8f16(as_v[blk][i], bs_v[blk][j], v16f{}, 0, 0, 0);
+                };
+                mm(0);
+#pragma unroll
+                for (int st = 0; st < kSteps; ++st) {
+                    if (st + 1 < kSteps) mm(st + 1);
+                    const int t = st % kSub, i = t / S::SN, j = t % S::SN;
+#pragma unroll
+                    for (int r = 0; r < 16; ++r)
+                        acc[i][j][r] = __builtin_fmaf((float)P[st & 1][r], Sc[st & 1][r], acc[i][j][r]);
+                    if (st + 1 < kSteps) {
+                        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+                        __builtin_amdgcn_sched_group_barrier(0x002, 16, 0);
+                        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+                        __builtin_amdgcn_sched_group_barrier(0x002, 16, 0);
+                    }
+                }
+            }
+        };
         // One staged pass: kKB blocks from LDS buffer `buf`
         auto compute = [&](int buf, int64_t kb0) {
+            if constexpr (kI8) {
+                compute_i8(buf, kb0);
+                return;
+            }
             if (!wave_rows) return;
             v8h alo[kKB][S::SM], ahi[kKB][S::SM], blo[kKB][S::SN], bhi[kKB][S::SN];
             v4h as_v[kKB][S::SM], bs_v[kKB][S::SN];
@@ -487,7 +603,7 @@ __global__ __launch_bounds__(Shape<BM>::kThreads, Shape<BM>::kWavesPerSimd) void
             // the up rows of the same columns: exchange through LDS, which the
             // K loop no longer uses (its last barrier has passed)
             constexpr int kXPitch = kBN / 2 + 4;   // floats per exchanged row
-            static_assert(BM * kXPitch * 4 <= (int)(sizeof(sm.a) + sizeof(sm.b)), "exchange fits the stage buffers");
+            static_assert(BM * kXPitch * 4 <= (int)(sizeof(sm.a) + sizeof(sm.b) + sizeof(sm.pad)), "exchange fits the stage buffers");
             float* xch = reinterpret_cast<float*>(&sm.a[0][0]);
             int l32e = l32, halfe = half;
             __asm__ volatile("" : "+v"(l32e), "+v"(halfe));
@@ -544,24 +660,629 @@ __global__ __launch_bounds__(Shape<BM>::kThreads, Shape<BM>::kWavesPerSimd) void
     }
 }
 
-template <int BM, bool kPartials, bool kFused>
+// ---- the warp-specialised tile kernel (128-row tiles) ---------------------------
+//
+// One workgroup of 8 waves per CU, persistent over its share of the tiles.
+// Waves 4-7 (producers, one per SIMD) load the Q8_1 and Q4_0 blocks of a
+// stage (two quantisation blocks of the tile), widen them to fp16 in the
+// layout above and write them into a ring of kRing stages in LDS.  Waves 0-3
+// (consumers, one per SIMD) read their fragments from the ring and run the
+// matrix products and the scale-accumulate.  The two sides are paced by
+// per-stage counters in LDS instead of workgroup barriers: a producer waits
+// until all consumers have released the slot it is about to overwrite, a
+// consumer until all producers have filled the stage it is about to read.  So
+// on every SIMD one wave issues matrix products while the other converts and
+// stages, and the loads of the next kLoadAhead stages are always in flight.
+// Every wait is bounded (kSpinLimit polls): a broken invariant ends in wrong
+// results, never in a hung GPU.
+//
+// Consumer c holds a 64 x 64 part of the tile: M sub-tiles i = 0, 1 cover tile
+// rows (2i + c/2) * 32 .. +31 (interleaved, so that a ragged tile's rows are
+// shared by both consumer pairs), N sub-tiles j = 0, 1 cover weight rows
+// (c%2) * 64 + j * 32 .. +31.  With the fused activation sub-tile j = 0 holds
+// the gate rows and j = 1 the up rows of the same 32 output columns, so gate
+// and up of an output meet in one lane's registers.  Within a stage the
+// products of step s + 1 are issued among the scale-accumulates of step s, in
+// a fixed order the compiler is not allowed to change, and the fragments of
+// the next block are read while the current one is multiplied.
+namespace ws {
+
+constexpr int kThreads = 512;            // 4 consumer + 4 producer waves
+constexpr int kBM = 128;
+constexpr int kRing = 4;                 // stages in LDS (kKB blocks each)
+constexpr int kLoadAhead = kRing;        // stages of loads in flight per producer thread (divides or is a multiple of kRing)
+constexpr int kTabs = kRing + kLoadAhead + 2;   // see the producer's table writes
+constexpr int kConsumers = 4;
+constexpr int kProducers = 4;
+constexpr int kSpinLimit = 1 << 16;     // about 5 ms per wait at most
+
+struct Smem {
+    uint8_t a[kRing][kBM * kRowBytes];
+    uint8_t b[kRing][kBN * kRowBytes];
+    uint2 as[kRing][kKB][kBM];           // {fp16 scale bits, 0} of the A rows
+    uint2 bs[kRing][kKB][kBN + 1];       // ... of the weight rows; entry kBN stays zero
+    int32_t pid[kTabs][kBM];             // pair of each tile row, per tile in flight
+    int32_t desc[kTabs][4];              // rows, first slot, first column of the tile
+    int32_t ready[kRing];                // producer waves that have filled the slot, in total
+    int32_t empty[kRing];                // consumer waves that have released the slot, in total
+};
+
+// Wait until *ctr >= target (LDS, written by other waves of the workgroup).
+__device__ __forceinline__ void wait_at_least(int32_t* ctr, int32_t target)
+{
+    for (int spins = 0; spins < kSpinLimit; ++spins) {
+        const int32_t v = uniform(__hip_atomic_load(ctr, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP));
+        if (v >= target) break;
+        __builtin_amdgcn_s_sleep(1);
+    }
+    __asm__ volatile("" ::: "memory");   // the stage's LDS accesses stay after the wait
+}
+
+// Count this wave in: its LDS reads (consumer) or writes (producer) of the
+// stage have completed before the counter moves.
+__device__ __forceinline__ void arrive(int32_t* ctr, int lane)
+{
+    __asm__ volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+    if (lane == 0) __hip_atomic_fetch_add(ctr, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+}
+
+// The tiles of this workgroup, in order: each XCD takes a contiguous range of
+// the work items (so an expert's weights and a group's activation rows are
+// shared in that XCD's L2) and its workgroups take the items of the range in
+// turn.
+struct WorkIter {
+    int64_t cur, end, step;
+    __device__ __forceinline__ void init(int64_t work)
+    {
+        const int64_t G = gridDim.x;
+        if (G >= kXcds && G % kXcds == 0) {
+            const int64_t x = blockIdx.x % kXcds, li = blockIdx.x / kXcds;
+            cur = x * work / kXcds + li;
+            end = (x + 1) * work / kXcds;
+            step = G / kXcds;
+        } else {
+            cur = blockIdx.x;
+            end = work;
+            step = G;
+        }
+    }
+};
+
+// Logical work item -> (M tile, N tile): groups of kGroupM M tiles, N tiles inner.
+__device__ __forceinline__ void item_tiles(int64_t L, int64_t total_tiles, int64_t ntn, int64_t& mt, int64_t& nt)
+{
+    const uint32_t per = (uint32_t)(kGroupM * ntn);
+    const uint32_t Lu = (uint32_t)L;   // work < 2^31 (checked on the host)
+    const uint32_t grp = Lu / per, rem = Lu - grp * per;
+    const uint32_t mt0 = grp * kGroupM;
+    const uint32_t gsz = (uint32_t)min<int64_t>(kGroupM, total_tiles - mt0);
+    const uint32_t n = rem / gsz;
+    nt = n;
+    mt = mt0 + (rem - n * gsz);
+}
+
+struct TileInfo {
+    int64_t bucket, slot0, n0;
+    int rows;
+};
+
+__device__ __forceinline__ TileInfo tile_info(const GroupedParams& p, int64_t mt, int64_t nt, int64_t col_tile)
+{
+    int lo = 0, hi = (int)p.nbuckets;   // the last bucket b with tiles[b] <= mt
+    while (hi - lo > 1) {
+        const int mid = (lo + hi) >> 1;
+        if (p.tiles[mid] <= mt) lo = mid; else hi = mid;
+    }
+    TileInfo t;
+    t.bucket = lo;
+    t.slot0 = p.offsets[lo] + (mt - p.tiles[lo]) * kBM;
+    t.rows = (int)min<int64_t>(kBM, p.offsets[lo + 1] - t.slot0);
+    t.n0 = nt * col_tile;
+    return t;
+}
+
+// Weight row that tile row bn reads: the plain tile's row n0 + bn (relative to
+// the tile base), or (fused) the gate / up row of output column
+// n0 + (bn/64)*32 + bn%32 relative to the expert's first row.  Rows past the
+// matrix read a valid row and are never stored.
+template <bool kFused>
+__device__ __forceinline__ uint32_t weight_row_offset(const GroupedParams& p, int64_t n0, int bn)
+{
+    if constexpr (kFused) {
+        const int64_t c = n0 + (bn / 64) * 32 + bn % 32;
+        const int64_t row = c < p.half ? ((bn / 32) % 2 ? p.half : 0) + c : 0;
+        return (uint32_t)(row * p.nb * kQ4Bytes);
+    } else {
+        return (uint32_t)((n0 + bn < p.N ? bn : 0) * p.nb * kQ4Bytes);
+    }
+}
+
+template <int VEC, bool kWide, bool kPartials, bool kFused>
+__global__ __launch_bounds__(kThreads, 2) void moe_grouped_ws_kernel(GroupedParams p)
+{
+    __shared__ __align__(16) Smem sm;
+    const int tid = threadIdx.x, lane = tid & 63, wave = uniform((int32_t)(tid >> 6));
+    const int64_t nb = p.nb;
+    const int64_t nstages = padded_blocks(nb) / kKB;
+    const int64_t real_tiles = p.tiles[p.E];          // tiles of buckets 0..E-1; the masked bucket's follow
+    const int64_t total_tiles = p.tiles[p.nbuckets];
+    const int64_t work = total_tiles * p.n_tiles_n;
+    constexpr int64_t kColTile = kFused ? kBN / 2 : kBN;
+
+    for (int i = tid; i < kRing; i += kThreads) { sm.ready[i] = 0; sm.empty[i] = 0; }
+    for (int i = tid; i < kRing * kKB; i += kThreads) sm.bs[i / kKB][i % kKB][kBN] = uint2{0u, 0u};
+    __syncthreads();   // the only workgroup barrier: the roles never meet again
+
+    if (wave >= kConsumers) {
+        // ================================ producers ================================
+        const int pt = tid - kConsumers * 64;          // 0..255
+        const int am = pt / kKB, ablk = pt % kKB;      // A: tile row am, block ablk of a stage
+        const int bn = pt / kKB, bh = pt % kKB;        // B: tile row bn, block bh
+        uint32_t nib_mask = 0x000f000fu, nib_magic = 0x64006400u, i8_magic = 0x64646464u;
+        __asm__ volatile("" : "+v"(nib_mask), "+v"(nib_magic), "+v"(i8_magic));
+        const __amdgpu_buffer_rsrc_t ars = make_rsrc(p.a, p.a_range);
+        using AOff = typename std::conditional<kWide, int64_t, uint32_t>::type;
+
+        // Load cursor: the stage whose loads are issued next.  Entering a tile
+        // waits on no memory: the descriptor of the tile after next and the
+        // row pairs of the next tile are loaded one tile ahead (vector loads,
+        // so that the counter updates' LDS waits do not wait for them).
+        WorkIter li;
+        li.init(work);
+        auto find_real = [&](int64_t c) -> int64_t {   // the first real tile's item at or after c
+            for (; c < li.end; c += li.step) {
+                int64_t mt, nt;
+                item_tiles(c, total_tiles, p.n_tiles_n, mt, nt);
+                if (mt < real_tiles) break;
+            }
+            return c;
+        };
+        const __amdgpu_buffer_rsrc_t drs = make_rsrc(p.tdesc, (int32_t)(uint32_t)min<int64_t>(16 * total_tiles, UINT32_MAX));
+        const __amdgpu_buffer_rsrc_t srs = make_rsrc(p.sorted, (int32_t)(uint32_t)min<int64_t>(4 * (int64_t)p.offsets[p.nbuckets], UINT32_MAX));
+        auto load_desc = [&](int64_t item) -> int4 {
+            if (item >= li.end) return int4{0, 0, 0, 0};
+            int64_t mt, nt;
+            item_tiles(item, total_tiles, p.n_tiles_n, mt, nt);
+            return __builtin_bit_cast(int4, __builtin_amdgcn_raw_buffer_load_b128(drs, (uint32_t)(mt * 16), 0, 0));
+        };
+        auto load_pid = [&](int4 d) -> int32_t {   // this thread's row pair of the tile with descriptor d
+            const int32_t sl = uniform(d.y), rw = uniform(d.z);
+            return (int32_t)__builtin_amdgcn_raw_buffer_load_b32(srs, (uint32_t)(4 * (sl + (am < rw ? am : 0))), 0, 0);
+        };
+        int64_t nx1 = find_real(li.cur);           // next tile to enter
+        int4 nx1_d = load_desc(nx1);
+        int32_t nx1_pid = nx1 < li.end ? load_pid(nx1_d) : 0;
+        int64_t nx2 = nx1 < li.end ? find_real(nx1 + li.step) : li.end;
+        int4 nx2_d = load_desc(nx2);
+        int64_t l_kb0 = 0;
+        bool l_valid = false;
+        int64_t l_rseq = 0;                      // real tiles entered so far
+        AOff a_off_g = 0;
+        uint32_t bg_off = 0;
+        __amdgpu_buffer_rsrc_t wrs = make_rsrc(p.w, 0);
+        auto l_enter = [&]() {
+            l_valid = nx1 < li.end;
+            if (!l_valid) return;
+            int64_t mt, nt;
+            item_tiles(nx1, total_tiles, p.n_tiles_n, mt, nt);
+            const int64_t bucket = uniform(nx1_d.x), slot0 = uniform(nx1_d.y);
+            const int rows = uniform(nx1_d.z);
+            const int64_t n0 = nt * kColTile;
+            const int32_t pid = nx1_pid;
+            const int32_t tok = (int32_t)((uint32_t)pid / (uint32_t)p.act_div);
+            a_off_g = (AOff)(((int64_t)tok * nb + ablk) * kQ8Bytes);
+            const uint8_t* wtile = p.w + (bucket * p.N + (kFused ? 0 : n0)) * nb * kQ4Bytes;
+            wrs = make_rsrc(wtile, p.wtile_range);
+            bg_off = weight_row_offset<kFused>(p, n0, bn);
+            const int tab = (int)(l_rseq % kTabs);
+            if (ablk == 0) sm.pid[tab][am] = pid;
+            if (pt == 0) {
+                sm.desc[tab][0] = rows;
+                sm.desc[tab][1] = (int32_t)slot0;
+                sm.desc[tab][2] = (int32_t)n0;
+            }
+            ++l_rseq;
+            l_kb0 = 0;
+            // move the lookahead on
+            nx1 = nx2;
+            nx1_d = nx2_d;
+            if (nx1 < li.end) nx1_pid = load_pid(nx1_d);
+            nx2 = nx1 < li.end ? find_real(nx1 + li.step) : li.end;
+            nx2_d = load_desc(nx2);
+        };
+        auto l_advance = [&]() {
+            l_kb0 += kKB;
+            if (l_kb0 >= kKB * nstages) l_enter();
+        };
+
+        u32x4 ra0[kLoadAhead], ra1[kLoadAhead];
+        uint32_t ra2[kLoadAhead], rb[kLoadAhead][5];
+        auto issue = [&](int set) {
+            const int64_t kb0 = l_kb0;
+            const bool ok = kb0 + ablk < nb;
+            const AOff voff = ok ? a_off_g : a_off_g - kQ8Bytes;
+            if constexpr (kWide) {
+                typedef u32x4 u32x4_a4 __attribute__((aligned(4)));
+                const uint8_t* abase = p.a + kb0 * kQ8Bytes + voff;
+                ra0[set] = *reinterpret_cast<const u32x4_a4*>(abase);
+                ra1[set] = *reinterpret_cast<const u32x4_a4*>(abase + 16);
+                ra2[set] = *reinterpret_cast<const uint32_t*>(abase + 32);
+            } else {
+                const int soff = uniform((int32_t)(kb0 * kQ8Bytes));
+                ra0[set] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(ars, voff, soff, 0));
+                ra1[set] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(ars, voff + 16, soff, 0));
+                ra2[set] = __builtin_amdgcn_raw_buffer_load_b32(ars, voff + 32, soff, 0);
+            }
+            const bool bok = kb0 + bh < nb;
+            const int wsoff = uniform((int32_t)(kb0 * kQ4Bytes));
+            if constexpr (VEC == 4) {
+                const u32x4 w4 = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(wrs, bg_off + 16 * bh, wsoff, 0));
+                rb[set][0] = w4.x; rb[set][1] = w4.y; rb[set][2] = w4.z; rb[set][3] = w4.w;
+                rb[set][4] = __builtin_amdgcn_raw_buffer_load_b32(wrs, bg_off + 16 * bh + 16, wsoff, 0);
+            } else {
+                const uint32_t boff = bg_off + (uint32_t)((bok ? bh : nb - 1 - kb0) * kQ4Bytes);
+                rb[set][0] = __builtin_amdgcn_raw_buffer_load_b16(wrs, boff, wsoff, 0);
+#pragma unroll
+                for (int i = 0; i < 4; ++i)
+                    rb[set][1 + i] = (uint32_t)__builtin_amdgcn_raw_buffer_load_b16(wrs, boff + 2 + 4 * i, wsoff, 0) |
+                                     ((uint32_t)__builtin_amdgcn_raw_buffer_load_b16(wrs, boff + 4 + 4 * i, wsoff, 0) << 16);
+            }
+        };
+
+        // LDS write offsets of this thread (within a slot)
+        int a_lds[4], b_lds[4];
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            a_lds[j] = lds_chunk(am, ablk * 4 + j);
+            b_lds[j] = lds_chunk(bn, bh * 4 + j);
+        }
+        auto commit = [&](int set, int slot, int64_t kb0) {
+            const bool ok = kb0 + ablk < nb;
+            const uint32_t cw[8] = {ra0[set].y, ra0[set].z, ra0[set].w, ra1[set].x, ra1[set].y, ra1[set].z, ra1[set].w, ra2[set]};
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                uint32_t o[4];
+                int8_pairs_to_f16(cw[j], i8_magic, o[0], o[1]);
+                int8_pairs_to_f16(cw[4 + j], i8_magic, o[2], o[3]);
+                *reinterpret_cast<u32x4*>(&sm.a[slot][a_lds[j]]) = u32x4{o[0], o[1], o[2], o[3]};
+            }
+            sm.as[slot][ablk][am] = uint2{ok ? (ra0[set].x & 0xffffu) : 0u, 0u};
+            const bool bok = kb0 + bh < nb;
+            uint32_t dbits, qs[4];
+            if constexpr (VEC == 4) {
+                const bool first = bh == 0;
+                dbits = first ? (rb[set][0] & 0xffffu) : (rb[set][0] >> 16);
+                qs[0] = first ? __builtin_amdgcn_alignbit(rb[set][1], rb[set][0], 16) : rb[set][1];
+                qs[1] = first ? __builtin_amdgcn_alignbit(rb[set][2], rb[set][1], 16) : rb[set][2];
+                qs[2] = first ? __builtin_amdgcn_alignbit(rb[set][3], rb[set][2], 16) : rb[set][3];
+                qs[3] = first ? __builtin_amdgcn_alignbit(rb[set][4], rb[set][3], 16) : rb[set][4];
+            } else {
+                dbits = rb[set][0];
+                qs[0] = rb[set][1]; qs[1] = rb[set][2]; qs[2] = rb[set][3]; qs[3] = rb[set][4];
+            }
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                uint32_t o[4];
+                nibbles_to_f16(qs[j], nib_mask, nib_magic, o);
+                *reinterpret_cast<u32x4*>(&sm.b[slot][b_lds[j]]) = u32x4{o[0], o[1], o[2], o[3]};
+            }
+            sm.bs[slot][bh][bn] = uint2{bok ? dbits : 0u, 0u};
+        };
+
+        // commit cursor: only the block index of the stage matters to a commit
+        WorkIter ci;
+        ci.init(work);
+        bool c_valid;
+        auto c_enter = [&]() {
+            for (; ci.cur < ci.end; ci.cur += ci.step) {
+                int64_t mt, nt;
+                item_tiles(ci.cur, total_tiles, p.n_tiles_n, mt, nt);
+                if (mt < real_tiles) break;
+            }
+            c_valid = ci.cur < ci.end;
+        };
+        int64_t c_kb0 = 0;
+
+        l_enter();
+        c_enter();
+#pragma unroll
+        for (int s = 0; s < kLoadAhead; ++s) {
+            if (l_valid) {
+                issue(s);
+                l_advance();
+            }
+        }
+        // unrolled so that the slot (u % kRing) and the load set (u % kLoadAhead)
+        // are constants
+        constexpr int kUnroll = kRing > kLoadAhead ? kRing : kLoadAhead;
+        static_assert(kUnroll % kRing == 0 && kUnroll % kLoadAhead == 0, "ring and load depth divide the unroll");
+        for (int64_t g = 0; c_valid; g += kUnroll) {
+#pragma unroll
+            for (int u = 0; u < kUnroll; ++u) {
+                if (!c_valid) break;
+                const int slot = u % kRing, set = u % kLoadAhead;
+                const int64_t use = (g + u) / kRing;
+                wait_at_least(&sm.empty[slot], (int32_t)(kConsumers * use));
+                commit(set, slot, c_kb0);
+                arrive(&sm.ready[slot], lane);
+                if (l_valid) {
+                    issue(set);
+                    l_advance();
+                }
+                c_kb0 += kKB;
+                if (c_kb0 >= kKB * nstages) {
+                    c_kb0 = 0;
+                    ci.cur += ci.step;
+                    c_enter();
+                }
+            }
+        }
+        return;
+    }
+
+    // ================================== consumers ==================================
+    const int wm = wave / 2, wn = wave % 2;
+    const int half = lane >> 5, l32 = lane & 31;
+    // per-lane LDS offsets within a stage slot; M sub-tile i adds i * 64 rows and
+    // N sub-tile j adds j * 32 rows (immediates)
+    const int sw = row_swizzle(l32);
+    int fa[kKB][2], fb[kKB][2];
+#pragma unroll
+    for (int blk = 0; blk < kKB; ++blk)
+#pragma unroll
+        for (int s2 = 0; s2 < 2; ++s2) {
+            const int c = (blk * 4 + 2 * half + s2) ^ sw;
+            fa[blk][s2] = (wm * 32 + l32) * kRowBytes + (c << 4);
+            fb[blk][s2] = (wn * 64 + l32) * kRowBytes + (c << 4);
+        }
+    const int as_row = wm * 32 + l32;
+    const int bs_row0 = half ? kBN : wn * 64 + l32;
+    const int bs_row1 = half ? kBN : wn * 64 + 32 + l32;
+
+    // One fragment set: the pieces of block q are reloaded with block q+1's as
+    // soon as their last product of block q has been issued.
+    v8h Alo[2], Ahi[2], Blo[2], Bhi[2];
+    v4h AS[2], BS[2];
+    auto load_a = [&](int slot, int blk, int i) __attribute__((always_inline)) {
+        Alo[i] = *reinterpret_cast<const v8h*>(&sm.a[slot][fa[blk][0] + i * 64 * kRowBytes]);
+        Ahi[i] = *reinterpret_cast<const v8h*>(&sm.a[slot][fa[blk][1] + i * 64 * kRowBytes]);
+        AS[i] = __builtin_bit_cast(v4h, sm.as[slot][blk][as_row + i * 64]);
+    };
+    auto load_b = [&](int slot, int blk, int j) __attribute__((always_inline)) {
+        Blo[j] = *reinterpret_cast<const v8h*>(&sm.b[slot][fb[blk][0] + j * 32 * kRowBytes]);
+        Bhi[j] = *reinterpret_cast<const v8h*>(&sm.b[slot][fb[blk][1] + j * 32 * kRowBytes]);
+        BS[j] = __builtin_bit_cast(v4h, sm.bs[slot][blk][j ? bs_row1 : bs_row0]);
+    };
+
+    v16f acc[2][2];
+    WorkIter wi;
+    wi.init(work);
+    int64_t g = 0;       // stages consumed so far (all tiles)
+    int64_t rseq = 0;    // real tiles consumed so far
+    for (; wi.cur < wi.end; wi.cur += wi.step) {
+        int64_t mt, nt;
+        item_tiles(wi.cur, total_tiles, p.n_tiles_n, mt, nt);
+        if (mt >= real_tiles) {
+            // masked pairs (ids outside [0, E)): zero rows, read straight from the pair list
+            const int64_t E = p.E;
+            const int64_t slot0 = p.offsets[E] + (mt - p.tiles[E]) * kBM;
+            const int rows = (int)min<int64_t>(kBM, p.offsets[E + 1] - slot0);
+            const int64_t n0 = nt * kColTile;
+            const int64_t width = kFused ? p.half : p.N;
+            for (int i = tid; i < rows * kColTile; i += kConsumers * 64) {
+                const int m = i / (int)kColTile, n = i - m * (int)kColTile;
+                if (n0 + n >= width) continue;
+                const int64_t o = (int64_t)p.sorted[slot0 + m] * width + n0 + n;
+                if constexpr (kPartials) {
+                    for (int64_t b = 0; b < nb; ++b) p.partials[o * nb + b] = 0;
+                } else {
+                    p.out[o] = 0.0f;
+                }
+            }
+            continue;
+        }
+        const int tab = (int)(rseq % kTabs);
+        ++rseq;
+        // the first stage of the tile is filled (and with it the tile's tables)
+        wait_at_least(&sm.ready[g % kRing], (int32_t)(kProducers * (g / kRing + 1)));
+        const int rows = uniform(sm.desc[tab][0]);
+        const int64_t n0 = uniform(sm.desc[tab][2]);
+        // live M sub-tiles of this consumer: i with (2i + wm) * 32 < rows
+        const int SML = (wm * 32 < rows ? 1 : 0) + (64 + wm * 32 < rows ? 1 : 0);
+#pragma unroll
+        for (int i = 0; i < 2; ++i)
+#pragma unroll
+            for (int j = 0; j < 2; ++j)
+#pragma unroll
+                for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
+
+        if (SML == 0 || kPartials) {
+            // nothing to multiply (no live rows), or the checking variant
+            for (int64_t s = 0; s < nstages; ++s, ++g) {
+                const int slot = (int)(g % kRing);
+                wait_at_least(&sm.ready[slot], (int32_t)(kProducers * (g / kRing + 1)));
+                if constexpr (kPartials) {
+#pragma unroll
+                    for (int blk = 0; blk < kKB; ++blk) {
+                        const int64_t b = s * kKB + blk;
+#pragma unroll
+                        for (int i = 0; i < 2; ++i) {
+                            if (i >= SML) continue;
+                            load_a(slot, blk, i);
+#pragma unroll
+                            for (int j = 0; j < 2; ++j) {
+                                load_b(slot, blk, j);
+                                v16f P = __builtin_amdgcn_mfma_f32_32x32x16_f16(Alo[i], Blo[j], v16f{}, 0, 0, 0);
+                                P = __builtin_amdgcn_mfma_f32_32x32x16_f16(Ahi[i], Bhi[j], P, 0, 0, 0);
+                                const int64_t n = n0 + wn * 64 + j * 32 + l32;
+#pragma unroll
+                                for (int r = 0; r < 16; ++r) {
+                                    const int m = (2 * i + wm) * 32 + 8 * (r / 4) + 4 * half + (r % 4);
+                                    if (m < rows && n < p.N && b < nb)
+                                        p.partials[((int64_t)sm.pid[tab][m] * p.N + n) * nb + b] = (int32_t)P[r];
+                                }
+                            }
+                        }
+                    }
+                }
+                arrive(&sm.empty[slot], lane);
+            }
+        } else {
+            auto run = [&](auto sml_c) __attribute__((always_inline)) {
+                constexpr int SM = decltype(sml_c)::value;
+                constexpr int kSub = SM * 2;   // steps per block: (i, j) = (t / 2, t % 2)
+                v16f P[2], Sc[2];
+                auto fmas = [&](int t, int r0, int r1) __attribute__((always_inline)) {
+                    const int i = t / 2, j = t % 2;
+#pragma unroll
+                    for (int r = r0; r < r1; ++r) acc[i][j][r] = __builtin_fmaf(P[t & 1][r], Sc[t & 1][r], acc[i][j][r]);
+                };
+                // step t of a block: the products of step nt (of this block, or
+                // step 0 of the next block) interleaved with step t's
+                // scale-accumulate, in this order:
+                //   P1(nt) 5 FMA(t)  P2(nt) 5 FMA(t)  S(nt) 6 FMA(t)
+                auto step = [&](int t, bool issue, int ntt) __attribute__((always_inline)) {
+                    const int i = ntt / 2, j = ntt % 2, b = ntt & 1;
+                    if (issue) P[b] = __builtin_amdgcn_mfma_f32_32x32x16_f16(Alo[i], Blo[j], v16f{}, 0, 0, 0);
+                    __builtin_amdgcn_sched_barrier(0);
+                    fmas(t, 0, 5);
+                    __builtin_amdgcn_sched_barrier(0);
+                    if (issue) P[b] = __builtin_amdgcn_mfma_f32_32x32x16_f16(Ahi[i], Bhi[j], P[b], 0, 0, 0);
+                    __builtin_amdgcn_sched_barrier(0);
+                    fmas(t, 5, 10);
+                    __builtin_amdgcn_sched_barrier(0);
+                    if (issue) Sc[b] = __builtin_amdgcn_mfma_f32_32x32x8f16(AS[i], BS[j], v16f{}, 0, 0, 0);
+                    __builtin_amdgcn_sched_barrier(0);
+                    fmas(t, 10, 16);
+                    __builtin_amdgcn_sched_barrier(0);
+                };
+                // one block: kNext says whether another block of the tile follows
+                // (in slot nslot, block nblk); its pieces are reloaded as this
+                // block's last products that use them are issued
+                auto block = [&](auto next_c, int nslot, int nblk) __attribute__((always_inline)) {
+                    constexpr bool kNext = decltype(next_c)::value;
+#pragma unroll
+                    for (int t = 0; t < kSub; ++t) {
+                        if (t + 1 < kSub) step(t, true, t + 1);
+                        else step(t, kNext, 0);
+                        if constexpr (kNext) {
+                            if (t == 0) {
+                                load_a(nslot, nblk, 0);   // last used by step 1's products
+                                if (SM == 1) { load_b(nslot, nblk, 0); load_b(nslot, nblk, 1); }
+                            }
+                            if (SM == 2 && t == 1) load_b(nslot, nblk, 0);
+                            if (SM == 2 && t == 2) { load_a(nslot, nblk, 1); load_b(nslot, nblk, 1); }
+                        }
+                    }
+                };
+                // prologue: block 0 of the tile's first stage, and its first products
+                {
+                    const int slot = (int)(g % kRing);
+#pragma unroll
+                    for (int i = 0; i < SM; ++i) load_a(slot, 0, i);
+                    load_b(slot, 0, 0);
+                    load_b(slot, 0, 1);
+                    P[0] = __builtin_amdgcn_mfma_f32_32x32x16_f16(Alo[0], Blo[0], v16f{}, 0, 0, 0);
+                    P[0] = __builtin_amdgcn_mfma_f32_32x32x16_f16(Ahi[0], Bhi[0], P[0], 0, 0, 0);
+                    Sc[0] = __builtin_amdgcn_mfma_f32_32x32x8f16(AS[0], BS[0], v16f{}, 0, 0, 0);
+                }
+                // The wait for the next stage comes first, so that the stage's
+                // steps are one straight run of code that nothing is moved
+                // across (its pieces are read during this stage's block 1).
+                for (int64_t s = 0; s + 1 < nstages; ++s) {
+                    const int slot = (int)(g % kRing), nslot = (int)((g + 1) % kRing);
+                    wait_at_least(&sm.ready[nslot], (int32_t)(kProducers * ((g + 1) / kRing + 1)));
+                    block(std::true_type{}, slot, 1);
+                    block(std::true_type{}, nslot, 0);
+                    arrive(&sm.empty[slot], lane);
+                    ++g;
+                }
+                {
+                    const int slot = (int)(g % kRing);
+                    block(std::true_type{}, slot, 1);
+                    block(std::false_type{}, slot, 0);
+                    arrive(&sm.empty[slot], lane);
+                    ++g;
+                }
+            };
+            if (SML == 2) run(std::integral_constant<int, 2>{});
+            else run(std::integral_constant<int, 1>{});
+        }
+
+        if constexpr (!kPartials) {
+            // epilogue: rows of tile row m = (2i + wm) * 32 + 8 (r/4) + 4 half + r%4
+            int l32e = l32, halfe = half;
+            __asm__ volatile("" : "+v"(l32e), "+v"(halfe));
+#pragma unroll
+            for (int i = 0; i < 2; ++i) {
+                if (i >= SML) continue;
+#pragma unroll
+                for (int q4 = 0; q4 < 4; ++q4) {
+                    const int mb = (2 * i + wm) * 32 + 8 * q4 + 4 * halfe;
+                    const int4 pids = *reinterpret_cast<const int4*>(&sm.pid[tab][mb]);
+                    const int32_t pv[4] = {pids.x, pids.y, pids.z, pids.w};
+#pragma unroll
+                    for (int r4 = 0; r4 < 4; ++r4) {
+                        const int m = mb + r4, r = 4 * q4 + r4;
+                        if (m >= rows) continue;
+                        if constexpr (kFused) {
+                            const int64_t c = n0 + wn * 32 + l32e;
+                            if (c < p.half)
+                                __builtin_nontemporal_store(gated_act(p.act, acc[i][0][r]) * acc[i][1][r],
+                                                            &p.out[(int64_t)pv[r4] * p.half + c]);
+                        } else {
+#pragma unroll
+                            for (int j = 0; j < 2; ++j) {
+                                const int64_t n = n0 + wn * 64 + j * 32 + l32e;
+                                if (n < p.N) __builtin_nontemporal_store(acc[i][j][r], &p.out[(int64_t)pv[r4] * p.N + n]);
+                            }
+                        }
+                    }
+                }
+            }
+        }
+    }
+}
+
+}  // namespace ws
+
+template <int BM, bool kPartials, bool kFused, bool kI8>
 int launch_grouped_v(int vec, bool wide, const GroupedParams& gp, int64_t grid, hipStream_t s)
 {
     constexpr int kT = Shape<BM>::kThreads;
     if (vec == 4) {
-        return wide ? launch("moe_grouped_kernel<4,wide>", moe_grouped_kernel<BM, 4, true, kPartials, kFused>, grid, kT, 0, s, gp)
-                    : launch("moe_grouped_kernel<4>", moe_grouped_kernel<BM, 4, false, kPartials, kFused>, grid, kT, 0, s, gp);
+        return wide ? launch("moe_grouped_kernel<4,wide>", moe_grouped_kernel<BM, 4, true, kPartials, kFused, kI8>, grid, kT, 0, s, gp)
+                    : launch("moe_grouped_kernel<4>", moe_grouped_kernel<BM, 4, false, kPartials, kFused, kI8>, grid, kT, 0, s, gp);
     }
-    return wide ? launch("moe_grouped_kernel<2,wide>", moe_grouped_kernel<BM, 2, true, kPartials, kFused>, grid, kT, 0, s, gp)
-                : launch("moe_grouped_kernel<2>", moe_grouped_kernel<BM, 2, false, kPartials, kFused>, grid, kT, 0, s, gp);
+    return wide ? launch("moe_grouped_kernel<2,wide>", moe_grouped_kernel<BM, 2, true, kPartials, kFused, kI8>, grid, kT, 0, s, gp)
+                : launch("moe_grouped_kernel<2>", moe_grouped_kernel<BM, 2, false, kPartials, kFused, kI8>, grid, kT, 0, s, gp);
 }
 
-template <int BM>
+template <bool kPartials, bool kFused>
+int launch_ws_v(int vec, bool wide, const GroupedParams& gp, int64_t grid, hipStream_t s)
+{
+    constexpr int kT = ws::kThreads;
+    if (vec == 4) {
+        return wide ? launch("moe_grouped_ws_kernel<4,wide>", ws::moe_grouped_ws_kernel<4, true, kPartials, kFused>, grid, kT, 0, s, gp)
+                    : launch("moe_grouped_ws_kernel<4>", ws::moe_grouped_ws_kernel<4, false, kPartials, kFused>, grid, kT, 0, s, gp);
+    }
+    return wide ? launch("moe_grouped_ws_kernel<2,wide>", ws::moe_grouped_ws_kernel<2, true, kPartials, kFused>, grid, kT, 0, s, gp)
+                : launch("moe_grouped_ws_kernel<2>", ws::moe_grouped_ws_kernel<2, false, kPartials, kFused>, grid, kT, 0, s, gp);
+}
+
+int launch_ws(bool part, bool fused, int vec, bool wide, const GroupedParams& gp, int64_t grid, hipStream_t s)
+{
+    if (part) return launch_ws_v<true, false>(vec, wide, gp, grid, s);
+    if (fused) return launch_ws_v<false, true>(vec, wide, gp, grid, s);
+    return launch_ws_v<false, false>(vec, wide, gp, grid, s);
+}
+
+template <int BM, bool kI8>
 int launch_grouped(bool part, bool fused, int vec, bool wide, const GroupedParams& gp, int64_t grid, hipStream_t s)
 {
-    if (part) return launch_grouped_v<BM, true, false>(vec, wide, gp, grid, s);
-    if (fused) return launch_grouped_v<BM, false, true>(vec, wide, gp, grid, s);
-    return launch_grouped_v<BM, false, false>(vec, wide, gp, grid, s);
+    if (part) return launch_grouped_v<BM, true, false, kI8>(vec, wide, gp, grid, s);
+    if (fused) return launch_grouped_v<BM, false, true, kI8>(vec, wide, gp, grid, s);
+    return launch_grouped_v<BM, false, false, kI8>(vec, wide, gp, grid, s);
 }
 
 }  // namespace
@@ -599,6 +1320,7 @@ int run_grouped(const MoeArgs& m, const BucketPlan& plan, void* ws, hipStream_t 
     gp.offsets = reinterpret_cast<const int32_t*>(base + plan.off_offsets);
     gp.tiles = reinterpret_cast<const int32_t*>(base + plan.off_tiles);
     gp.sorted = reinterpret_cast<const int32_t*>(base + plan.off_sorted);
+    gp.tdesc = reinterpret_cast<const int4*>(base + plan.off_tdesc);
     gp.E = m.E;
     gp.N = m.N;
     gp.nb = nb;
@@ -634,10 +1356,26 @@ int run_grouped(const MoeArgs& m, const BucketPlan& plan, void* ws, hipStream_t 
     static const bool force_wide = [] { const char* v = getenv("FTQ_FORCE_WIDE"); return v && v[0] == '1'; }();
     const bool wide = force_wide || act_rows * nb * kQ8Bytes >= ((int64_t)1 << 32);
     const bool fused = m.act != 0;
+    // the block partials on int8 MFMAs by default; the fp16-MFMA kernels stay
+    // selectable through ftq_debug_grouped_kernel for comparisons and tests
+    const int variant = grouped_kernel_variant();
+    const int64_t work_bound = gp.max_mt * gp.n_tiles_n;
+    if (variant == kGroupedF16Ws && bm == 128 && work_bound < INT32_MAX) {
+        int64_t g = std::min<int64_t>(work_bound, lim.cu_count);
+        if (g >= kXcds) g -= g % kXcds;
+        return launch_ws(part, fused, vec, wide, gp, std::max<int64_t>(g, 1), s);
+    }
+    if (variant == kGroupedI8) {
+        switch (bm) {
+        case 128: return launch_grouped<128, true>(part, fused, vec, wide, gp, grid, s);
+        case 64: return launch_grouped<64, true>(part, fused, vec, wide, gp, grid, s);
+        default: return launch_grouped<32, true>(part, fused, vec, wide, gp, grid, s);
+        }
+    }
     switch (bm) {
-    case 128: return launch_grouped<128>(part, fused, vec, wide, gp, grid, s);
-    case 64: return launch_grouped<64>(part, fused, vec, wide, gp, grid, s);
-    default: return launch_grouped<32>(part, fused, vec, wide, gp, grid, s);
+    case 128: return launch_grouped<128, false>(part, fused, vec, wide, gp, grid, s);
+    case 64: return launch_grouped<64, false>(part, fused, vec, wide, gp, grid, s);
+    default: return launch_grouped<32, false>(part, fused, vec, wide, gp, grid, s);
     }
 }
 

@@ -18,6 +18,8 @@ LIB_PATH = os.path.join(_PKG, "libftq.so")
 OK, ERR_INVALID_ARG, ERR_WORKSPACE, ERR_LAUNCH, ERR_UNSUPPORTED, ERR_HIP = range(6)
 PATH_AUTO, PATH_GEMV, PATH_GROUPED = 0, 1, 2
 ACT_SILU, ACT_GELU_TANH = 1, 2
+# grouped-path kernels (same bits, different speed); GROUPED_I8 is the default
+GROUPED_I8, GROUPED_F16, GROUPED_F16_WS = 0, 1, 2
 # weight block types (GGUF type ids) and their block bytes
 W_Q4_0, W_Q4_1, W_Q5_0, W_Q5_1, W_Q8_0 = 2, 3, 6, 7, 8
 W_BLOCK_BYTES = {W_Q4_0: 18, W_Q4_1: 20, W_Q5_0: 22, W_Q5_1: 24, W_Q8_0: 34}
@@ -31,7 +33,7 @@ EXPORTS = (
     "ftq_moe_q4_0_q8_1_act", "ftq_moe_q4_0_q8_1_act_routed",
     "ftq_moe_gguf_q8_1", "ftq_moe_gguf_q8_1_partials",
     "ftq_last_error", "ftq_version",
-    "ftq_debug_force_block_threads", "ftq_debug_gemv_plan", "ftq_moe_q4_0_q8_1_noalloc",
+    "ftq_debug_force_block_threads", "ftq_debug_grouped_kernel", "ftq_debug_gemv_plan", "ftq_moe_q4_0_q8_1_noalloc",
 )
 
 
@@ -88,6 +90,8 @@ def lib() -> ctypes.CDLL:
     L.ftq_version.restype = ctypes.c_char_p
     L.ftq_debug_force_block_threads.argtypes = [I32]
     L.ftq_debug_force_block_threads.restype = None
+    L.ftq_debug_grouped_kernel.argtypes = [I32]
+    L.ftq_debug_grouped_kernel.restype = I32
     L.ftq_debug_gemv_plan.argtypes = [I64, I64, I64, I64, I64, I32, I32, P, P, P]
     L.ftq_debug_gemv_plan.restype = I32
     L.ftq_moe_q4_0_q8_1_noalloc.argtypes = [P, P, P, P, I64, I64, I64, I64, I64, I32, P]
@@ -159,6 +163,12 @@ def gemv_plan(E: int, N: int, K: int, T: int, top_k: int, wtype: int = 2, act: i
     _check(lib().ftq_debug_gemv_plan(E, N, K, T, top_k, wtype, act, ctypes.addressof(seg), ctypes.addressof(pc),
                                      ctypes.addressof(per_cu)))
     return {"seg": seg.value, "pairs_per_pass": pc.value, "wg_per_cu": per_cu.value}
+
+
+def grouped_kernel(variant: int):
+    """Select the grouped path's kernel for later calls on this thread
+    (GROUPED_I8, GROUPED_F16 or GROUPED_F16_WS)."""
+    _check(lib().ftq_debug_grouped_kernel(variant))
 
 
 def select_path(E: int, N: int, K: int, T: int, top_k: int) -> int:
