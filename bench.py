@@ -17,12 +17,16 @@ before timing starts.
     python bench.py --summarize-pmc DIR    # HBM traffic from rocprofv3 --pmc runs
     python bench.py --summarize-trace DB   # kernel table from a rocprofv3 --kernel-trace database
 
-Prints one JSON line.  `value` is milliseconds per step (lower is better);
-`roofline` reports the dominant kernel (the grouped MFMA matmul) against the
-dense fp16 MFMA peak (its contraction runs on f16 MFMA over exact integer
-codes) using its algorithmic operation count, timed with HIP events on the
-stream it runs on; `cpu_baseline` is the CPU oracle on a bounded
-sample of the same workload.
+Prints one JSON line.  `value` is milliseconds per step (lower is better),
+wall clock over the timed steps with the inputs resident in HBM (warm caches);
+`step_ms` gives the median, minimum and maximum of the same steps from HIP
+events, warm and cold (each cold step after a 1 GiB write that evicts the L2
+and the 256 MB last-level cache); `roofline` reports the dominant kernel (the
+grouped matmul: against the dense int8 MFMA peak, its block products run on
+int8 MFMAs) using its algorithmic operation count, timed with HIP events on the
+stream it runs on; `decode` adds the GEMV path at Mixtral-8x7B decode shapes
+(T = 1 and 8) against the HBM roofline, warm and cold; `cpu_baseline` is the
+CPU oracle on a bounded sample of the same workload, with the host CPU named.
 """
 from __future__ import annotations
 
@@ -30,6 +34,7 @@ import argparse
 import glob
 import json
 import os
+import platform
 import statistics
 import sys
 import time
@@ -68,9 +73,111 @@ WORKLOADS = {
 # tokens on a Tesla T4 (FreeToken PR #185, Performance), the faster of two runs.
 PAGES_MS_T8191 = 705.8
 HBM_PEAK_GBS = 8000.0           # MI355X HBM3E
-F16_PEAK_TFLOPS = 2500.0        # MI355X dense fp16 MFMA (the grouped kernel's contraction type)
-INT8_PEAK_TOPS = 5000.0         # MI355X dense int8 MFMA (context: an int8 formulation's ceiling)
+F16_PEAK_TFLOPS = 2500.0        # MI355X dense fp16 MFMA (context: the fp16 formulation's ceiling)
+INT8_PEAK_TOPS = 5000.0         # MI355X dense int8 MFMA (the grouped kernel's block products)
 DOMINANT = "moe_grouped_kernel"
+SCRUB_BYTES = 1 << 30           # written before each cold step: larger than the L2s and the 256 MB MALL
+# decode records carried on every bench line: the GEMV at Mixtral-8x7B's
+# up-projection shape (mlxcel PR #652, Summary) at one and eight tokens
+DECODE = (("mixtral", 1), ("mixtral", 8))
+
+
+def cpu_model() -> str:
+    try:
+        with open("/proc/cpuinfo") as fh:
+            for line in fh:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return platform.processor() or "unknown"
+
+
+def _stats(xs):
+    return {"median": round(statistics.median(xs), 4), "min": round(min(xs), 4), "max": round(max(xs), 4),
+            "n": len(xs)}
+
+
+def _cold_times(fn, scrub, reps):
+    """HIP-event time of fn() right after a write of the scrub buffer, reps
+    times.  The scrub keeps the GPU busy while the host enqueues fn, so the
+    events bracket fn's kernels, not host submission."""
+    import torch
+    out = []
+    for i in range(reps):
+        scrub.fill_(float(i))
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record()
+        fn()
+        b.record()
+        torch.cuda.synchronize()
+        out.append(a.elapsed_time(b))
+    return out
+
+
+def decode_record(name: str, T: int, scrub, reps: int = 10) -> dict:
+    """The GEMV path at a decode shape: one routed matmul call, warm (graph of
+    20 calls, per call, 5 replays) and cold (after a 1 GiB scrub, reps calls),
+    against the HBM roofline of its algorithmic bytes."""
+    import numpy as np
+    import torch
+    from quantized_moe_expert_quantize_amd import ftq, inputs
+    wl, _ = WORKLOADS[name]
+    E, N, K, k = wl["E"], wl["N"], wl["K"], wl["top_k"]
+    dev = scrub.device
+    # weights N(0, 0.02) from torch's seeded device generator, Q4_0 by libftq
+    # (the GEMV's time does not depend on the values; this keeps set-up short)
+    gen = torch.Generator(device=dev)
+    gen.manual_seed(wl["seed"])
+    wq = torch.empty((E, N, K // 32 * 18), dtype=torch.uint8, device=dev)
+    for e in range(E):
+        w = torch.randn((N, K), generator=gen, device=dev, dtype=torch.float32) * 0.02
+        wq[e] = ftq.quantize_q4_0(w).view(N, K // 32 * 18)
+        del w
+    ids = inputs.routing(T, E, k, seed=wl["seed"], kind=wl["routing"])
+    aq = ftq.quantize_q8_1(torch.from_numpy(inputs.activations(T, K, seed=wl["seed"])).to(dev))
+    ids_d = torch.from_numpy(ids).to(dev)
+    path = ftq.select_path(E, N, K, T, k)
+    out = torch.empty((T * k, N), dtype=torch.float32, device=dev)
+    need = ftq.workspace_bytes(E, N, K, T, k, path)
+    ws = torch.empty(max(need, 256), dtype=torch.uint8, device=dev) if need else None
+    ftq.moe_route(ids_d, E, ws, path)
+
+    def call():
+        ftq.moe_routed(wq, aq, ids_d, E, N, K, out, ws, path)
+
+    for _ in range(3):
+        call()
+    torch.cuda.synchronize()
+    R = 20
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        for _ in range(R):
+            call()
+    torch.cuda.synchronize()
+    warm = []
+    for _ in range(5):
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record()
+        g.replay()
+        b.record()
+        torch.cuda.synchronize()
+        warm.append(a.elapsed_time(b) / R)
+    cold = _cold_times(call, scrub, reps)
+    alg = _algorithmic_bytes(E, N, K, T, k, ids)
+    wm, cm = statistics.median(warm), statistics.median(cold)
+    return {"workload": wl["workload"], "T": T, "pairs": T * k, "path": {1: "gemv", 2: "grouped"}[path],
+            "kernel": "moe_gemv_kernel" if path == ftq.PATH_GEMV else "moe_grouped_kernel",
+            "alg_bytes_per_launch": alg,
+            "warm_us": {k_: round(v * 1e3, 2) for k_, v in _stats(warm).items() if k_ != "n"},
+            "cold_us": {k_: round(v * 1e3, 2) for k_, v in _stats(cold).items() if k_ != "n"},
+            "roofline": {"bound": "hbm", "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                         "achieved_warm": round(alg / (wm / 1e3) / 1e9, 1),
+                         "frac_warm": round(alg / (wm / 1e3) / 1e9 / HBM_PEAK_GBS, 4),
+                         "achieved_cold": round(alg / (cm / 1e3) / 1e9, 1),
+                         "frac_cold": round(alg / (cm / 1e3) / 1e9 / HBM_PEAK_GBS, 4)},
+            "timing": "warm: HIP events around a graph replay of 20 calls, per call, 5 replays; cold: HIP events "
+                      f"around one call right after a 1 GiB write, {reps} calls"}
 
 
 def traffic_file(kernel: str, workload: str, T: int) -> str:
@@ -132,6 +239,29 @@ def summarize_pmc(d: str, kernel: str = DOMINANT) -> None:
     print(json.dumps(out, indent=1))
 
 
+def summarize_counters(d: str, kernel: str = DOMINANT) -> None:
+    """Median per-dispatch value of every counter that rocprofv3 --pmc runs
+    under d collected for the kernels whose name contains `kernel`, with the
+    derived utilisations (SQ cycle counters are per SE summed; GRBM_GUI_ACTIVE
+    is the kernel's GPU cycles)."""
+    import csv
+    per = {}
+    for f in glob.glob(os.path.join(d, "**", "*counter_collection.csv"), recursive=True):
+        with open(f) as fh:
+            for row in csv.DictReader(fh):
+                if kernel not in row.get("Kernel_Name", ""):
+                    continue
+                key = (f, row.get("Dispatch_Id") or row.get("Correlation_Id"))
+                c = per.setdefault(row["Counter_Name"], {})
+                c[key] = c.get(key, 0.0) + float(row["Counter_Value"])
+    med = {c: statistics.median(v.values()) for c, v in per.items()}
+    print("| counter | median per dispatch | dispatches |")
+    print("|---|---|---|")
+    for c in sorted(med):
+        print(f"| {c} | {med[c]:.6g} | {len(per[c])} |")
+    return med
+
+
 def summarize_trace(db: str) -> None:
     """Per-kernel table (calls, total / average duration, registers, LDS, grid)
     from a rocprofv3 --kernel-trace database (rocpd SQLite)."""
@@ -164,10 +294,13 @@ def main() -> None:
     ap.add_argument("--wtype", choices=sorted(WTYPES), default="q4_0",
                     help="weight block type (not q4_0: random valid blocks, GEMV path, plain layers only)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-decode", action="store_true", help="skip the Mixtral decode records")
+    ap.add_argument("--cold-steps", type=int, default=10, help="steps timed after a 1 GiB cache scrub each")
     ap.add_argument("--cpu-sample-tokens", type=int, default=8192, help="tokens the CPU oracle runs (10-30 s on the box)")
     ap.add_argument("--summarize-pmc", metavar="DIR")
     ap.add_argument("--pmc-kernel", default=DOMINANT, help="kernel whose counters --summarize-pmc reports")
     ap.add_argument("--summarize-trace", metavar="DB", help="per-kernel table from a rocprofv3 --kernel-trace database")
+    ap.add_argument("--summarize-counters", metavar="DIR", help="median per-dispatch counters of --pmc-kernel under DIR")
     args = ap.parse_args()
 
     if args.summarize_trace:
@@ -175,6 +308,9 @@ def main() -> None:
         return
     if args.summarize_pmc:
         summarize_pmc(args.summarize_pmc, args.pmc_kernel)
+        return
+    if args.summarize_counters:
+        summarize_counters(args.summarize_counters, args.pmc_kernel)
         return
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
@@ -321,6 +457,12 @@ def main() -> None:
     t1 = time.perf_counter()
     graph_ms_per_step = (t1 - t0) * 1e3 / steps
     ms_per_step = eager_ms_per_step
+    # per-step GPU time of the timed eager steps (HIP events at the step's ends)
+    warm_steps = [m[0].elapsed_time(m[-1]) for m in marks]
+    # cold steps: each after a 1 GiB write, which leaves none of the step's
+    # inputs in the L2s or the last-level cache
+    scrub = torch.empty(SCRUB_BYTES // 4, dtype=torch.float32, device=dev)
+    cold_steps = _cold_times(step, scrub, args.cold_steps) if args.cold_steps > 0 else None
 
     # ---- the dominant kernel's duration ---------------------------------------
     # A call of 0.2 ms or more keeps the GPU behind the host, so the HIP events
@@ -365,11 +507,12 @@ def main() -> None:
         if rec.get("lib_sha256") == _lib_hash() and rec.get("T") == T:
             traffic = rec.get("bytes_per_launch")
     if path == ftq.PATH_GROUPED:
-        roofline = {"bound": "mfma", "achieved": round(tops, 2), "peak": F16_PEAK_TFLOPS, "unit": "TFLOP/s",
-                    "frac": round(tops / F16_PEAK_TFLOPS, 4), "traffic": traffic,
-                    "kernel": "moe_grouped_kernel (f16 MFMA on exact integer codes)", "kernel_ms": round(mm_ms, 4),
+        roofline = {"bound": "mfma", "achieved": round(tops, 2), "peak": INT8_PEAK_TOPS, "unit": "TOP/s",
+                    "frac": round(tops / INT8_PEAK_TOPS, 4), "traffic": traffic,
+                    "kernel": "moe_grouped_kernel (int8 MFMA block products, fp32 scale-accumulate)",
+                    "kernel_ms": round(mm_ms, 4),
                     "kernel_ms_covers": "one routed matmul call: moe_grouped_kernel; " + how,
-                    "frac_of_int8_peak": round(tops / INT8_PEAK_TOPS, 4),
+                    "frac_of_f16_peak": round(tops / F16_PEAK_TFLOPS, 4),
                     "ops_per_launch": ops, "alg_bytes_per_launch": alg_bytes,
                     "hbm_gbs": round(gbs, 1), "hbm_frac": round(gbs / HBM_PEAK_GBS, 4)}
     else:
@@ -378,6 +521,11 @@ def main() -> None:
                     "kernel": "moe_gemv_kernel", "kernel_ms": round(mm_ms, 4),
                     "kernel_ms_covers": "one routed matmul call: moe_gemv_kernel; " + how,
                     "alg_bytes_per_launch": alg_bytes, "ops_per_launch": ops}
+
+    # ---- decode records: the GEMV at Mixtral decode shapes -------------------
+    decode = None
+    if not args.no_decode:
+        decode = [decode_record(name, t, scrub) for name, t in DECODE]
 
     # ---- CPU oracle on a bounded sample of the same workload ----------------
     cpu = None
@@ -403,7 +551,7 @@ def main() -> None:
             oracle.moe(ow, oa, np.ascontiguousarray(ids[:ts]), E, N, K, ts, k)
         c1 = time.perf_counter()
         cpu = {"value": round((c1 - c0) * 1e3 * T / ts, 1), "unit": "ms", "cores": oracle.num_threads(),
-               "kind": "oracle",
+               "kind": "oracle", "cpu_model": cpu_model(),
                "sample": f"Q8_1 quantisation + matmul{' + combine' if down else (' + activation' if fused else '')} "
                          f"of the first {ts} of {T} "
                          f"tokens ({ts * k} of {pairs} pairs), "
@@ -420,7 +568,7 @@ def main() -> None:
         "higher_is_better": False,
         "scaling": "weak",
         "vs_baseline": round(ms_per_step / PAGES_MS_T8191, 6) if args.workload == "page1" and T == DEFAULT_T else None,
-        "dtype": ("q4_0 x q8_1 (exact integer block dots on f16 MFMA, fp32 scale-accumulate)" if path == ftq.PATH_GROUPED
+        "dtype": ("q4_0 x q8_1 (exact integer block dots on int8 MFMA, fp32 scale-accumulate)" if path == ftq.PATH_GROUPED
                   else f"{args.wtype} x q8_1 (int8 dot4 block dots, fp32 scale-accumulate)"),
         "data": "synthetic",
         "config": dict(wl, T=T, pairs=pairs, path={1: "gemv", 2: "grouped"}[path], wtype=args.wtype),
@@ -429,6 +577,9 @@ def main() -> None:
                   "between the stages of the eager steps (below 0.2 ms a stage includes host submission gaps), "
                   "matmul as roofline.kernel_ms_covers says",
         "graph_ms_per_step": round(graph_ms_per_step, 4),
+        "step_ms": {"warm": _stats(warm_steps), "cold": _stats(cold_steps) if cold_steps else None,
+                    "how": "HIP events at the ends of each step; warm: the timed eager steps; cold: each step right "
+                           "after a 1 GiB write (no input left in the L2s or the last-level cache)"},
         "breakdown_ms": dict({"quantize_q8_1": round(q_ms, 4), "route": round(r_ms, 4), "matmul": round(mm_ms, 4),
                               "matmul_eager_marks": round(mm_eager_ms, 4),
                               "matmul_graph_per_call": round(mm_graph_ms, 4) if mm_graph_ms is not None else None},
@@ -440,6 +591,8 @@ def main() -> None:
                               if down else {})),
         "roofline": roofline,
         "cpu_baseline": cpu,
+        "decode": decode,
+        "host_cpu": cpu_model(),
         "lib_sha256": _lib_hash()[:16],
     }
     print(json.dumps(result))

@@ -82,11 +82,15 @@ __device__ __forceinline__ int row_swizzle(int r) { return (r & 7) ^ ((r >> 3) &
 __device__ __forceinline__ int lds_chunk(int r, int c) { return r * kRowBytes + ((c ^ row_swizzle(r)) << 4); }
 
 // int8 variant: a staged row is the 2 x 32 int8 codes of a pass (64 bytes, 4
-// chunks); chunk c of row r sits at chunk c ^ ((r >> 1) & 3), so that 8
-// consecutive rows reading one logical chunk cover all 8 16-byte slots of 128
-// bytes (2 rows per 128 bytes, 4 chunk positions).
+// chunks); chunk c of row r sits at chunk c ^ g(r), g(r) = gray((r >> 1) & 3)
+// ^ ((r >> 3) & 1), gray(x) = x ^ (x >> 1).  Reading one logical chunk, 8
+// consecutive rows then cover the 8 16-byte slots of 128 bytes and 16
+// consecutive rows the 16 slots of 256 bytes; the stage writes (two chunks of
+// each of 8 rows per 16 lanes) likewise.  So fragment reads and stage writes
+// are free of bank conflicts for 8 or 16 lanes served per clock (the
+// (r >> 1) & 3 swizzle alone is conflict-free for 8 only).
 constexpr int kRowBytesI8 = kKB * 32;
-__device__ __forceinline__ int row_swizzle_i8(int r) { return (r >> 1) & 3; }
+__device__ __forceinline__ int row_swizzle_i8(int r) { return ((r >> 1) & 3) ^ ((r >> 2) & 1) ^ ((r >> 3) & 1); }
 __device__ __forceinline__ int lds_chunk_i8(int r, int c) { return r * kRowBytesI8 + ((c ^ row_swizzle_i8(r)) << 4); }
 
 // Four Q4_0 nibbles (the low or high nibbles of four bytes, already masked to
