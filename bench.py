@@ -12,7 +12,7 @@ before timing starts.
     python bench.py [--steps K] [--warmup W] [--T tokens]
     python bench.py --workload page1_down  # the second layer: per-pair rows + combine
     python bench.py --workload page1_act   # the first layer with act(gate) * up fused
-    python bench.py --workload mixtral --T 1 --wtype q8_0   # another GGUF weight type (GEMV path)
+    python bench.py --workload mixtral --T 1 --wtype q8_0   # another GGUF weight type (random valid blocks)
     python bench.py --mode profile         # a short run for rocprofv3
     python bench.py --summarize-pmc DIR    # HBM traffic from rocprofv3 --pmc runs
     python bench.py --summarize-trace DB   # kernel table from a rocprofv3 --kernel-trace database
@@ -292,7 +292,7 @@ def main() -> None:
     ap.add_argument("--T", type=int, default=None, help="tokens (default: the workload's own)")
     ap.add_argument("--mode", choices=["bench", "profile"], default="bench")
     ap.add_argument("--wtype", choices=sorted(WTYPES), default="q4_0",
-                    help="weight block type (not q4_0: random valid blocks, GEMV path, plain layers only)")
+                    help="weight block type (not q4_0: random valid blocks, plain layers only; q5_* on the GEMV path)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-decode", action="store_true", help="skip the Mixtral decode records")
     ap.add_argument("--cold-steps", type=int, default=10, help="steps timed after a 1 GiB cache scrub each")
@@ -353,7 +353,7 @@ def main() -> None:
         wq = torch.from_numpy(inputs.gguf_blocks(wt, E, N, K, seed=seed)).to(dev)
     x = torch.from_numpy(x32).to(dev)
     ids_d = torch.from_numpy(ids).to(dev)
-    path = ftq.select_path(E, N, K, T, k) if wt == 2 else ftq.PATH_GEMV
+    path = ftq.PATH_GEMV if wt in ftq.GEMV_ONLY else ftq.select_path(E, N, K, T, k)
     gates_d = torch.from_numpy(gates).to(dev)
     aq = torch.empty((act_rows, K // 32 * 36), dtype=torch.uint8, device=dev)
     out = torch.empty((T * k, out_cols), dtype=torch.float32, device=dev)
@@ -568,7 +568,7 @@ def main() -> None:
         "higher_is_better": False,
         "scaling": "weak",
         "vs_baseline": round(ms_per_step / PAGES_MS_T8191, 6) if args.workload == "page1" and T == DEFAULT_T else None,
-        "dtype": ("q4_0 x q8_1 (exact integer block dots on int8 MFMA, fp32 scale-accumulate)" if path == ftq.PATH_GROUPED
+        "dtype": (f"{args.wtype} x q8_1 (exact integer block dots on int8 MFMA, fp32 scale-accumulate)" if path == ftq.PATH_GROUPED
                   else f"{args.wtype} x q8_1 (int8 dot4 block dots, fp32 scale-accumulate)"),
         "data": "synthetic",
         "config": dict(wl, T=T, pairs=pairs, path={1: "gemv", 2: "grouped"}[path], wtype=args.wtype),

@@ -323,17 +323,23 @@ int ftq_moe_q4_0_q8_1_act_routed(const void* w, const void* a, const int32_t* to
  * z the zero point (8 for Q4_0, 16 for Q5_0, else 0) and m the offset (Q4_1,
  * Q5_1; else 0): the dot product of the dequantised weights and activations.
  * The integer sums are exact; the offset term uses the exact integer sum of
- * the activation codes, not the fp16 s field.  Evaluation: fp32, per block
- * acc = fma(P, d*d8, acc) then, for offset types, acc = fma(S, m*d8, acc).
+ * the activation codes, not the fp16 s field.  Evaluation in fp32.  GEMV path:
+ * per block acc = fma(P, d*d8, acc) then, for offset types, acc = fma(S,
+ * m*d8, acc), S = sum q8.  Grouped path: per block acc = fma(P, d*d8, acc) with
+ * P from an int8 matrix product; the Q4_1 offset terms are summed apart, by
+ * bf16 matrix products whose operands split d8*S (exact in fp32) and m into
+ * bf16 pieces with exact products, and added to acc at the end.
  *   w:          [E][N][K/32] blocks of wtype;
  *   a:          Q8_1, [T][K/32] (act_per_pair == 0) or [T*top_k][K/32] (one
  *               row per pair, as ftq_moe_q4_0_q8_1_pairs);
  *   other arguments as ftq_moe_q4_0_q8_1; the workspace is
- *   ftq_moe_workspace_bytes(E, N, K, T, top_k, FTQ_PATH_GEMV) bytes.
- * FTQ_W_Q4_0 runs the Q4_0 paths (both).  The other types run on the GEMV
- * path (FTQ_PATH_AUTO selects it); FTQ_PATH_GROUPED returns
- * FTQ_ERR_UNSUPPORTED, as do weight rows that are not 4-byte aligned (Q5_0 and
- * Q8_0 with an odd K/32).  Unknown wtype: FTQ_ERR_INVALID_ARG.
+ *   ftq_moe_workspace_bytes(E, N, K, T, top_k, path) bytes.
+ * FTQ_W_Q4_0 runs the Q4_0 paths.  Q4_1 and Q8_0 run on both paths, chosen as
+ * for Q4_0 under FTQ_PATH_AUTO (the grouped path at prefill sizes); Q5_0 and
+ * Q5_1 on the GEMV path only (FTQ_PATH_AUTO selects it; FTQ_PATH_GROUPED returns
+ * FTQ_ERR_UNSUPPORTED).  Weight rows that are not 4-byte aligned (Q5_0 and
+ * Q8_0 with an odd K/32) return FTQ_ERR_UNSUPPORTED on either path.  Unknown
+ * wtype: FTQ_ERR_INVALID_ARG.
  * ftq_moe_gguf_q8_1_partials writes the integer parts sum((q - z) * q8) as
  * int32 [T*top_k][N][K/32] instead (checking aid).
  */

@@ -166,10 +166,10 @@ int moe_common(const void* w, const void* a, const int32_t* ids, float* out, int
         set_error("unknown weight type %d", wtype);
         return FTQ_ERR_INVALID_ARG;
     }
-    if (wtype != FTQ_W_Q4_0) {
-        // the other block types run on the GEMV path only
+    if (wtype == FTQ_W_Q5_0 || wtype == FTQ_W_Q5_1) {
+        // the five-bit types run on the GEMV path only
         if (path == FTQ_PATH_GROUPED) {
-            set_error("weight type %d: the grouped path takes Q4_0 only; use FTQ_PATH_GEMV or FTQ_PATH_AUTO", wtype);
+            set_error("weight type %d: the grouped path takes Q4_0, Q4_1 and Q8_0; use FTQ_PATH_GEMV or FTQ_PATH_AUTO", wtype);
             return FTQ_ERR_UNSUPPORTED;
         }
         if (path == FTQ_PATH_AUTO) path = FTQ_PATH_GEMV;

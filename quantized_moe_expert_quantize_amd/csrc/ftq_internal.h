@@ -106,7 +106,7 @@ struct MoeArgs {
     int64_t E, N, K, T, top_k;
     int64_t act_div;       // activation row of pair p: p / act_div (top_k: per token; 1: per pair)
     int act;               // 0: plain output [T*k][N]; FTQ_ACT_*: act(gate) * up, [T*k][N/2]
-    int wtype;             // weight block type (FTQ_W_*); the grouped path takes Q4_0 only
+    int wtype;             // weight block type (FTQ_W_*); the grouped path takes Q4_0, Q4_1 and Q8_0
 };
 
 // Gated activation of one fp32 value ("Current Bug: CuTeDSLMoERunner", Bug 6:

@@ -61,6 +61,7 @@ typedef float v16f __attribute__((ext_vector_type(16)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef int v4i __attribute__((ext_vector_type(4)));
 typedef int v16i __attribute__((ext_vector_type(16)));
+typedef __bf16 v8bf __attribute__((ext_vector_type(8)));
 
 constexpr int kThreads = 256;
 constexpr int kBN = 128;          // weight rows per tile
@@ -98,6 +99,40 @@ __device__ __forceinline__ int lds_chunk_i8(int r, int c) { return r * kRowBytes
 // below 0x100 in every byte (no carries), and flipping bit 7 then gives
 // v - 8 modulo 256.
 __device__ __forceinline__ uint32_t nibbles_minus8(uint32_t v) { return (v + 0x78787878u) ^ 0x80808080u; }
+
+// Weight block bytes of the types the grouped path takes (GGUF layouts):
+// Q4_0 {fp16 d, 16 nibble bytes}, Q4_1 {fp16 d, fp16 m, 16 nibble bytes},
+// Q8_0 {fp16 d, 32 int8}.
+template <int WT>
+__host__ __device__ constexpr int w_bytes() { return WT == FTQ_W_Q8_0 ? 34 : WT == FTQ_W_Q4_1 ? 20 : kQ4Bytes; }
+
+// The Q4_1 offset term m4 d8 sum(q8) of a block, as one bf16 matrix product:
+// v = d8 sum(q8) is exact in fp32 (11 x 12 significant bits) and splits by
+// truncation into three bf16 pieces v1 + v2 + v3 = v (8 + 8 + 8 bits); m4 (fp16)
+// splits into ma + mb = m4 (8 + 3 bits).  The six products are exact in fp32,
+// so the operands [v1 v1 v2 v2 v3 v3 0 0] . [ma mb ma mb ma mb 0 0] give
+// v m4 up to the product's fp32 accumulation.  Packed as four words of bf16
+// pairs (the upper halves of the fp32 bit patterns).
+__device__ __forceinline__ uint32_t bf16_hi(float x) { return __float_as_uint(x) & 0xffff0000u; }
+__device__ __forceinline__ u32x4 offset_a_operand(float v)
+{
+    const uint32_t b1 = bf16_hi(v);
+    const float r1 = v - __uint_as_float(b1);
+    const uint32_t b2 = bf16_hi(r1);
+    const uint32_t b3 = bf16_hi(r1 - __uint_as_float(b2));
+    return u32x4{b1 | (b1 >> 16), b2 | (b2 >> 16), b3 | (b3 >> 16), 0u};
+}
+__device__ __forceinline__ u32x4 offset_b_operand(float m)
+{
+    const uint32_t ma = bf16_hi(m);
+    const uint32_t mb = bf16_hi(m - __uint_as_float(ma));
+    const uint32_t w = (ma >> 16) | mb;
+    return u32x4{w, w, w, 0u};
+}
+__device__ __forceinline__ float half_bits_to_float(uint32_t h)
+{
+    return (float)__builtin_bit_cast(_Float16, (uint16_t)h);
+}
 
 // Buffer resource over `range` bytes from `base` (range: a 32-bit unsigned
 // count carried in an int).  Both arguments must be wave-uniform: a resource
@@ -144,7 +179,7 @@ struct Shape {
     static_assert(SM >= 1 && SN >= 1, "tile shape");
 };
 
-template <int BM, bool kI8 = false>
+template <int BM, bool kI8 = false, bool kOff = false>
 struct Smem {
     static constexpr int RB = kI8 ? kRowBytesI8 : kRowBytes;
     // the fused epilogue exchanges BM x (kBN/2 + 4) floats through the stage
@@ -155,6 +190,9 @@ struct Smem {
     uint8_t pad[kExchange > kStage ? kExchange - kStage : 16];
     uint2 as[2][kKB][BM];        // {fp16 scale bits, 0} of the A rows
     uint2 bs[2][kKB][kBN + 1];   // {fp16 scale bits, 0} of the weight rows; entry kBN stays zero
+    // Q4_1: the offset product's operands per block of each A row and weight row
+    u32x4 aoff[2][kKB][kOff ? BM : 1];
+    u32x4 boff[2][kKB][kOff ? kBN : 1];
     int32_t row_pair[BM];
     int32_t row_tok[BM];
 };
@@ -205,13 +243,17 @@ __device__ __forceinline__ int64_t xcd_remap(int64_t bid, int64_t G)
     return xcd * q + min<int64_t>(xcd, r) + local;
 }
 
-template <int BM, int VEC, bool kWide, bool kPartials, bool kFused, bool kI8>
+template <int BM, int VEC, bool kWide, bool kPartials, bool kFused, bool kI8, int WT = FTQ_W_Q4_0>
 __global__ __launch_bounds__(Shape<BM>::kThreads, Shape<BM>::kWavesPerSimd) void moe_grouped_kernel(GroupedParams p)
 {
+    static_assert(WT == FTQ_W_Q4_0 || (kI8 && !kFused), "Q4_1 and Q8_0 weights: int8 block products, plain output");
+    static_assert(WT != FTQ_W_Q8_0 || VEC == 4, "Q8_0 rows are read as 4-byte words (K/32 even)");
     using S = Shape<BM>;
     constexpr int kThreads = S::kThreads;
+    constexpr int kWB = w_bytes<WT>();
+    constexpr bool kOff = WT == FTQ_W_Q4_1 && !kPartials;   // the Q4_1 offset term
     constexpr int RB = Smem<BM, kI8>::RB;
-    __shared__ __align__(16) Smem<BM, kI8> sm;
+    __shared__ __align__(16) Smem<BM, kI8, kOff> sm;
 
     // the wave index is uniform per wave: say so, so that what derives from it
     // (sub-tile counts, loop control) stays in scalar registers
@@ -301,7 +343,7 @@ __global__ __launch_bounds__(Shape<BM>::kThreads, Shape<BM>::kWavesPerSimd) void
         const bool b_thread = tid < kBN * kKB;
         const int bn = tid / kKB, bh = tid % kKB;   // the blocks of one row in adjacent lanes
         // uniform per tile: the tile's first weight row, or (fused) the expert's
-        const uint8_t* wtile = p.w + (uniform(bucket) * p.N + (kFused ? 0 : uniform(n0))) * nb * kQ4Bytes;
+        const uint8_t* wtile = p.w + (uniform(bucket) * p.N + (kFused ? 0 : uniform(n0))) * nb * kWB;
         const __amdgpu_buffer_rsrc_t wrs = make_rsrc(wtile, p.wtile_range);
         uint32_t bg_off;
         if constexpr (kFused) {
@@ -309,7 +351,7 @@ __global__ __launch_bounds__(Shape<BM>::kThreads, Shape<BM>::kWavesPerSimd) void
             const int64_t c = n0 + bn % (kBN / 2);
             bg_off = (uint32_t)((c < p.half ? (bn >= kBN / 2 ? p.half : 0) + c : 0) * nb * kQ4Bytes);
         } else {
-            bg_off = (uint32_t)((n0 + bn < p.N ? bn : 0) * nb * kQ4Bytes);
+            bg_off = (uint32_t)((n0 + bn < p.N ? bn : 0) * nb * kWB);
         }
         int b_lds[4];
 #pragma unroll
@@ -318,7 +360,7 @@ __global__ __launch_bounds__(Shape<BM>::kThreads, Shape<BM>::kWavesPerSimd) void
         u32x4 ra0, ra1;
         uint32_t ra2;
         bool ra_ok;
-        uint32_t rb[5];
+        uint32_t rb[9];
         bool rb_ok;
 
         auto issue = [&](int64_t kb0) {
@@ -341,8 +383,33 @@ __global__ __launch_bounds__(Shape<BM>::kThreads, Shape<BM>::kWavesPerSimd) void
             // past K/32 only in the last pass of an odd K/32; uniform per wave
             rb_ok = kb0 + bh < nb;
             if (!b_thread) return;
-            const int wsoff = uniform((int32_t)(kb0 * kQ4Bytes));
-            if constexpr (VEC == 4) {
+            const int wsoff = uniform((int32_t)(kb0 * kWB));
+            if constexpr (WT == FTQ_W_Q8_0) {
+                // a pair of 34-byte blocks starts 4-byte aligned (K/32 even): block
+                // kb0 is words 0..8 of the pair (scale in the low half of word 0,
+                // codes from byte 2), block kb0+1 words 8..16 (scale in the high
+                // half of word 8, codes in words 9..16).  Both lanes load two
+                // 16-byte pieces and word 8.
+                const u32x4 x = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(wrs, bg_off + (bh ? 36u : 0u), wsoff, 0));
+                const u32x4 y = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(wrs, bg_off + (bh ? 52u : 16u), wsoff, 0));
+                rb[0] = x.x; rb[1] = x.y; rb[2] = x.z; rb[3] = x.w;
+                rb[4] = y.x; rb[5] = y.y; rb[6] = y.z; rb[7] = y.w;
+                rb[8] = __builtin_amdgcn_raw_buffer_load_b32(wrs, bg_off + 32u, wsoff, 0);
+            } else if constexpr (WT == FTQ_W_Q4_1) {
+                // 20-byte blocks: every block starts 4-byte aligned (VEC 4), else
+                // ten 2-byte loads
+                const uint32_t boff = bg_off + (uint32_t)((rb_ok ? bh : nb - 1 - kb0) * kWB);
+                if constexpr (VEC == 4) {
+                    const u32x4 x = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(wrs, boff, wsoff, 0));
+                    rb[0] = x.x; rb[1] = x.y; rb[2] = x.z; rb[3] = x.w;
+                    rb[4] = __builtin_amdgcn_raw_buffer_load_b32(wrs, boff + 16, wsoff, 0);
+                } else {
+#pragma unroll
+                    for (int i = 0; i < 5; ++i)
+                        rb[i] = (uint32_t)__builtin_amdgcn_raw_buffer_load_b16(wrs, boff + 4 * i, wsoff, 0) |
+                                ((uint32_t)__builtin_amdgcn_raw_buffer_load_b16(wrs, boff + 4 * i + 2, wsoff, 0) << 16);
+                }
+            } else if constexpr (VEC == 4) {
                 // a pair of blocks starts 4-byte aligned (K/32 even, kb0 even):
                 // block kb0 is words 0..4 of the pair, block kb0+1 words 4..8
                 const u32x4 w4 = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(wrs, bg_off + 16 * bh, wsoff, 0));
@@ -376,8 +443,40 @@ __global__ __launch_bounds__(Shape<BM>::kThreads, Shape<BM>::kWavesPerSimd) void
                     }
                 }
                 sm.as[buf][ablk][am] = uint2{ra_ok ? (ra0.x & 0xffffu) : 0u, 0u};
+                if constexpr (kOff) {
+                    int sum = 0;
+#pragma unroll
+                    for (int j = 0; j < 8; ++j) sum = __builtin_amdgcn_sdot4((int)cw[j], 0x01010101, sum, false);
+                    const float v = ra_ok ? half_bits_to_float(ra0.x & 0xffffu) * (float)sum : 0.0f;
+                    sm.aoff[buf][ablk][am] = offset_a_operand(v);
+                }
             }
             if (!b_thread) return;
+            if constexpr (WT == FTQ_W_Q8_0) {
+                // codes as they are: chunk 0 codes 0..15, chunk 1 codes 16..31
+                const bool first = bh == 0;
+                uint32_t c[8];
+#pragma unroll
+                for (int j = 0; j < 8; ++j) c[j] = first ? __builtin_amdgcn_alignbit(rb[j + 1], rb[j], 16) : rb[j];
+                *reinterpret_cast<u32x4*>(&sm.b[buf][b_lds[0]]) = u32x4{c[0], c[1], c[2], c[3]};
+                *reinterpret_cast<u32x4*>(&sm.b[buf][b_lds[1]]) = u32x4{c[4], c[5], c[6], c[7]};
+                sm.bs[buf][bh][bn] = uint2{first ? (rb[0] & 0xffffu) : (rb[8] >> 16), 0u};
+                return;
+            } else if constexpr (WT == FTQ_W_Q4_1) {
+                // codes q in 0..15 (no zero point): chunk 0 the low nibbles (elements
+                // 0..15), chunk 1 the high nibbles (elements 16..31)
+                u32x4 lo, hi;
+#pragma unroll
+                for (int j = 0; j < 4; ++j) {
+                    lo[j] = rb[1 + j] & 0x0f0f0f0fu;
+                    hi[j] = (rb[1 + j] >> 4) & 0x0f0f0f0fu;
+                }
+                *reinterpret_cast<u32x4*>(&sm.b[buf][b_lds[0]]) = lo;
+                *reinterpret_cast<u32x4*>(&sm.b[buf][b_lds[1]]) = hi;
+                sm.bs[buf][bh][bn] = uint2{rb_ok ? (rb[0] & 0xffffu) : 0u, 0u};
+                if constexpr (kOff) sm.boff[buf][bh][bn] = rb_ok ? offset_b_operand(half_bits_to_float(rb[0] >> 16)) : u32x4{0u, 0u, 0u, 0u};
+                return;
+            }
             // weight block -> 32 fp16 values (q - 8) and its scale
             uint32_t dbits, qs[4];
             if constexpr (VEC == 4) {
@@ -508,6 +607,20 @@ __global__ __launch_bounds__(Shape<BM>::kThreads, Shape<BM>::kWavesPerSimd) void
                         __builtin_amdgcn_sched_group_barrier(0x002, 16, 0);
                         __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
                         __builtin_amdgcn_sched_group_barrier(0x002, 16, 0);
+                    }
+                }
+                if constexpr (kOff) {
+                    // the Q4_1 offset terms of both blocks of the pass, added to acc
+                    // by one bf16 product: lanes of the lower half carry block 0's
+                    // operands, the upper half block 1's
+#pragma unroll
+                    for (int i = 0; i < S::SM; ++i) {
+                        const v8bf ao = __builtin_bit_cast(v8bf, sm.aoff[buf][half][as_row + i * 32]);
+#pragma unroll
+                        for (int j = 0; j < S::SN; ++j) {
+                            const v8bf bo = __builtin_bit_cast(v8bf, sm.boff[buf][half][(wn * S::SN + j) * 32 + l32]);
+                            acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ao, bo, acc[i][j], 0, 0, 0);
+                        }
                     }
                 }
             }
@@ -1250,16 +1363,35 @@ __global__ __launch_bounds__(kThreads, 2) void moe_grouped_ws_kernel(GroupedPara
 
 }  // namespace ws
 
-template <int BM, bool kPartials, bool kFused, bool kI8>
+template <int BM, bool kPartials, bool kFused, bool kI8, int WT = FTQ_W_Q4_0>
 int launch_grouped_v(int vec, bool wide, const GroupedParams& gp, int64_t grid, hipStream_t s)
 {
     constexpr int kT = Shape<BM>::kThreads;
     if (vec == 4) {
-        return wide ? launch("moe_grouped_kernel<4,wide>", moe_grouped_kernel<BM, 4, true, kPartials, kFused, kI8>, grid, kT, 0, s, gp)
-                    : launch("moe_grouped_kernel<4>", moe_grouped_kernel<BM, 4, false, kPartials, kFused, kI8>, grid, kT, 0, s, gp);
+        return wide ? launch("moe_grouped_kernel<4,wide>", moe_grouped_kernel<BM, 4, true, kPartials, kFused, kI8, WT>, grid, kT, 0, s, gp)
+                    : launch("moe_grouped_kernel<4>", moe_grouped_kernel<BM, 4, false, kPartials, kFused, kI8, WT>, grid, kT, 0, s, gp);
     }
-    return wide ? launch("moe_grouped_kernel<2,wide>", moe_grouped_kernel<BM, 2, true, kPartials, kFused, kI8>, grid, kT, 0, s, gp)
-                : launch("moe_grouped_kernel<2>", moe_grouped_kernel<BM, 2, false, kPartials, kFused, kI8>, grid, kT, 0, s, gp);
+    if constexpr (WT == FTQ_W_Q8_0) {
+        set_error("Q8_0 weights on the grouped path need K/32 even and 4-byte aligned weights");
+        return FTQ_ERR_UNSUPPORTED;
+    } else {
+        return wide ? launch("moe_grouped_kernel<2,wide>", moe_grouped_kernel<BM, 2, true, kPartials, kFused, kI8, WT>, grid, kT, 0, s, gp)
+                    : launch("moe_grouped_kernel<2>", moe_grouped_kernel<BM, 2, false, kPartials, kFused, kI8, WT>, grid, kT, 0, s, gp);
+    }
+}
+
+// Q4_1 and Q8_0 weights: int8 block products, plain output or partials
+template <int WT>
+int launch_grouped_wt(int64_t bm, bool part, int vec, bool wide, const GroupedParams& gp, int64_t grid, hipStream_t s)
+{
+    switch (bm) {
+    case 128: return part ? launch_grouped_v<128, true, false, true, WT>(vec, wide, gp, grid, s)
+                          : launch_grouped_v<128, false, false, true, WT>(vec, wide, gp, grid, s);
+    case 64: return part ? launch_grouped_v<64, true, false, true, WT>(vec, wide, gp, grid, s)
+                         : launch_grouped_v<64, false, false, true, WT>(vec, wide, gp, grid, s);
+    default: return part ? launch_grouped_v<32, true, false, true, WT>(vec, wide, gp, grid, s)
+                         : launch_grouped_v<32, false, false, true, WT>(vec, wide, gp, grid, s);
+    }
 }
 
 template <bool kPartials, bool kFused>
@@ -1344,7 +1476,12 @@ int run_grouped(const MoeArgs& m, const BucketPlan& plan, void* ws, hipStream_t 
         gp.wtile_range = range32(m.N * nb * kQ4Bytes);
         gp.n_tiles_n = (gp.half + kBN / 2 - 1) / (kBN / 2);
     } else {
-        gp.wtile_range = range32((int64_t)kBN * nb * kQ4Bytes);
+        const int64_t wb = m.wtype == FTQ_W_Q8_0 ? w_bytes<FTQ_W_Q8_0>() : m.wtype == FTQ_W_Q4_1 ? w_bytes<FTQ_W_Q4_1>() : kQ4Bytes;
+        if ((int64_t)kBN * nb * wb > (int64_t)UINT32_MAX) {
+            set_error("grouped path: %d weight rows of K = %lld reach 4 GiB", kBN, (long long)m.K);
+            return FTQ_ERR_UNSUPPORTED;
+        }
+        gp.wtile_range = range32((int64_t)kBN * nb * wb);
         gp.n_tiles_n = (m.N + kBN - 1) / kBN;
     }
     gp.nbuckets = plan.buckets;
@@ -1353,7 +1490,10 @@ int run_grouped(const MoeArgs& m, const BucketPlan& plan, void* ws, hipStream_t 
     gp.max_mt = (plan.pairs + plan.buckets * (bm - 1)) / bm;
     const int64_t grid = std::min<int64_t>(gp.max_mt * gp.n_tiles_n, std::min<int64_t>(lim.max_grid_x, UINT32_MAX / kThreads));
     const uintptr_t wa = reinterpret_cast<uintptr_t>(m.w);
-    const int vec = (nb % 2 == 0 && wa % 4 == 0) ? 4 : 2;
+    // 4-byte weight loads where every pass's blocks start 4-byte aligned:
+    // Q4_0 (18 B) and Q8_0 (34 B) pairs of blocks need K/32 even, Q4_1 (20 B)
+    // blocks only aligned rows
+    const int vec = (wa % 4 == 0 && (nb % 2 == 0 || m.wtype == FTQ_W_Q4_1)) ? 4 : 2;
     const bool part = m.partials != nullptr;
     // activation offsets fit 32 bits unless the staged activations reach 4 GiB;
     // FTQ_FORCE_WIDE=1 selects the 64-bit variant at any size (tests)
@@ -1362,6 +1502,8 @@ int run_grouped(const MoeArgs& m, const BucketPlan& plan, void* ws, hipStream_t 
     const bool fused = m.act != 0;
     // the block partials on int8 MFMAs by default; the fp16-MFMA kernels stay
     // selectable through ftq_debug_grouped_kernel for comparisons and tests
+    if (m.wtype == FTQ_W_Q4_1) return launch_grouped_wt<FTQ_W_Q4_1>(bm, part, vec, wide, gp, grid, s);
+    if (m.wtype == FTQ_W_Q8_0) return launch_grouped_wt<FTQ_W_Q8_0>(bm, part, vec, wide, gp, grid, s);
     const int variant = grouped_kernel_variant();
     const int64_t work_bound = gp.max_mt * gp.n_tiles_n;
     if (variant == kGroupedF16Ws && bm == 128 && work_bound < INT32_MAX) {

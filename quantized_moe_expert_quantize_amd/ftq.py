@@ -23,6 +23,7 @@ GROUPED_I8, GROUPED_F16, GROUPED_F16_WS = 0, 1, 2
 # weight block types (GGUF type ids) and their block bytes
 W_Q4_0, W_Q4_1, W_Q5_0, W_Q5_1, W_Q8_0 = 2, 3, 6, 7, 8
 W_BLOCK_BYTES = {W_Q4_0: 18, W_Q4_1: 20, W_Q5_0: 22, W_Q5_1: 24, W_Q8_0: 34}
+GEMV_ONLY = (W_Q5_0, W_Q5_1)   # the other types also run on the grouped path
 QK, Q4_0_BYTES, Q8_1_BYTES = 32, 18, 36
 
 EXPORTS = (
@@ -376,7 +377,7 @@ def moe_gguf(w: torch.Tensor, wtype: int, a: torch.Tensor, topk_ids: torch.Tenso
     T, top_k = _gguf_args(w, wtype, a, topk_ids, E, N, K, per_pair)
     if out is None:
         out = torch.empty((T * top_k, N), dtype=torch.float32, device=a.device)
-    need = workspace_bytes(E, N, K, T, top_k, PATH_GEMV if wtype != W_Q4_0 else path)
+    need = workspace_bytes(E, N, K, T, top_k, PATH_GEMV if wtype in GEMV_ONLY else path)
     ws, ws_n = _workspace(workspace, need, a.device)
     _check(lib().ftq_moe_gguf_q8_1(
         _dev(w, "w", torch.uint8), wtype, _dev(a, "a", torch.uint8), _dev(topk_ids, "topk_ids", torch.int32),
@@ -390,7 +391,7 @@ def moe_gguf_partials(w: torch.Tensor, wtype: int, a: torch.Tensor, topk_ids: to
     """Integer parts sum((q - z) * q8), int32 [T*top_k, N, K/32]."""
     T, top_k = _gguf_args(w, wtype, a, topk_ids, E, N, K, per_pair)
     out = torch.empty((T * top_k, N, K // QK), dtype=torch.int32, device=a.device)
-    need = workspace_bytes(E, N, K, T, top_k, PATH_GEMV if wtype != W_Q4_0 else path)
+    need = workspace_bytes(E, N, K, T, top_k, PATH_GEMV if wtype in GEMV_ONLY else path)
     ws, ws_n = _workspace(None, need, a.device)
     _check(lib().ftq_moe_gguf_q8_1_partials(
         _dev(w, "w", torch.uint8), wtype, _dev(a, "a", torch.uint8), _dev(topk_ids, "topk_ids", torch.int32),

@@ -1,9 +1,12 @@
-"""The other GGUF weight block types (Q4_1, Q5_0, Q5_1, Q8_0) against Q8_1 on
-the GEMV path, through the C ABI (FreeToken PR #185, Problem: the GEMV's
-sibling launchers share its geometry).  Weights are quantised by the oracle
-(no GPU quantizer exists for these types) and uploaded; activations are
-quantised by each side.  Bar: integer parts bit-exact; fp32 outputs within the
-tolerance, with two roundings per block for the offset types."""
+"""The other GGUF weight block types (Q4_1, Q5_0, Q5_1, Q8_0) against Q8_1,
+through the C ABI (FreeToken PR #185, Problem: the GEMV's sibling launchers
+share its geometry): all four on the GEMV path, Q4_1 and Q8_0 on the grouped
+path too.  Weights are quantised by the oracle (no GPU quantizer exists for
+these types) and uploaded; activations are quantised by each side.  Bar:
+integer parts bit-exact; fp32 outputs within the tolerance, with two roundings
+per block for the offset types on the GEMV path, and on the grouped path up
+to six more per Q4_1 block for the offset products that the bf16 matrix
+products add into the accumulator (each product is exact; their sums round)."""
 import numpy as np
 import pytest
 import torch
@@ -16,6 +19,7 @@ pytestmark = pytest.mark.gpu
 
 SIBLINGS = {ftq.W_Q4_1: "q4_1", ftq.W_Q5_0: "q5_0", ftq.W_Q5_1: "q5_1", ftq.W_Q8_0: "q8_0"}
 OFFSET = {ftq.W_Q4_1, ftq.W_Q5_1}
+GROUPED = {ftq.W_Q4_1: "q4_1", ftq.W_Q8_0: "q8_0"}   # types the grouped path takes
 
 
 class WCase:
@@ -34,25 +38,44 @@ class WCase:
                          torch.from_numpy(self.ids).cuda())
         return self._gpu
 
+    def resolved(self, path):
+        """The path a call takes (host rule, as the library applies it)."""
+        if path != ftq.PATH_AUTO:
+            return path
+        if self.wtype in ftq.GEMV_ONLY:
+            return ftq.PATH_GEMV
+        return ftq.select_path(self.E, self.N, self.K, self.T, self.top_k)
+
     def run(self, path=ftq.PATH_AUTO):
         w, a, ids = self.gpu()
         out = ftq.moe_gguf(w, self.wtype, a, ids, self.E, self.N, self.K, per_pair=self.per_pair, path=path)
         torch.cuda.synchronize()
+        self.last_path = self.resolved(path)
         return out.cpu().numpy()
 
-    def partials(self):
+    def partials(self, path=ftq.PATH_AUTO):
         w, a, ids = self.gpu()
-        p = ftq.moe_gguf_partials(w, self.wtype, a, ids, self.E, self.N, self.K, per_pair=self.per_pair)
+        p = ftq.moe_gguf_partials(w, self.wtype, a, ids, self.E, self.N, self.K, per_pair=self.per_pair, path=path)
         torch.cuda.synchronize()
         return p.cpu().numpy()
+
+    def oracle_partials(self):
+        return oracle.moe_w_partials(self.wtype, self.wb, self.oa, self.ids, self.E, self.N, self.K, self.T,
+                                     self.top_k, per_pair=self.per_pair)
+
+    def roundings(self, path):
+        """Roundings per block in the error bound (see the module doc)."""
+        if self.wtype not in OFFSET:
+            return self.nb
+        return 7 * self.nb if path == ftq.PATH_GROUPED else 2 * self.nb
 
     def oracle_out(self, pairs=None):
         return oracle.moe_w(self.wtype, self.wb, self.oa, self.ids, self.E, self.N, self.K, self.T, self.top_k,
                             pairs=pairs, want_abssum=True, per_pair=self.per_pair)
 
-    def check(self, got, pairs=None):
+    def check(self, got, pairs=None, path=None):
         ref, ab = self.oracle_out(pairs)
-        assert_matches_oracle(got, ref, ab, 2 * self.nb if self.wtype in OFFSET else self.nb)
+        assert_matches_oracle(got, ref, ab, self.roundings(self.last_path if path is None else path))
 
 
 # (E, N, K, T, top_k, routing): K/32 = 8 (16-byte loads), 10 and 88 (4-byte
@@ -92,18 +115,24 @@ def test_odd_block_count(wtype):
 
 
 @pytest.mark.parametrize("wtype", list(SIBLINGS), ids=lambda t: SIBLINGS[t])
-def test_per_pair_masked_and_grouped_refused(wtype):
+def test_per_pair_masked_and_grouped(wtype):
     E, N, K, T, k = 6, 96, 256, 40, 3
     ids = inputs.routing(T, E, k, seed=3)
     ids[0, 0] = -1
     ids[5, 2] = E
     c = WCase(wtype, E, N, K, T, k, seed=3, per_pair=True, ids=ids)
-    got = c.run()
+    got = c.run(ftq.PATH_GEMV)
     c.check(got)
     assert not got[0].any() and not got[5 * k + 2].any()
-    with pytest.raises(ftq.FtqError) as ei:
-        c.run(ftq.PATH_GROUPED)
-    assert ei.value.status == ftq.ERR_UNSUPPORTED
+    if wtype in GROUPED:
+        got = c.run(ftq.PATH_GROUPED)
+        c.check(got)
+        assert not got[0].any() and not got[5 * k + 2].any()
+        assert np.array_equal(c.partials(ftq.PATH_GROUPED), c.oracle_partials())
+    else:
+        with pytest.raises(ftq.FtqError) as ei:
+            c.run(ftq.PATH_GROUPED)
+        assert ei.value.status == ftq.ERR_UNSUPPORTED
 
 
 def test_q4_0_through_the_gguf_entry_is_the_q4_0_call():
@@ -129,3 +158,56 @@ def test_mixtral_decode_sampled(wtype, T):
     nb_eff = 2 * c.nb if wtype in OFFSET else c.nb
     assert_matches_oracle(got[:, rows], ref[:, rows], ab[:, rows], nb_eff)
     assert_matches_oracle(got, ref, ab, nb_eff)
+
+
+# Grouped path for Q4_1 and Q8_0: (E, N, K, T, top_k, routing).  Pairs per
+# expert of >= 96, 40..95 and < 40 select 128-, 64- and 32-row tiles; N = 200
+# leaves a ragged column tile, K/32 = 10 and 88 are not multiples of 8, Zipf
+# routing leaves some experts empty and others in many tiles.
+GROUPED_SHAPES = {
+    "bm128": (4, 200, 320, 100, 4, "uniform"),
+    "bm64": (8, 136, 512, 100, 4, "uniform"),
+    "bm32_page1_rows": (16, 64, 2816, 48, 4, "uniform"),
+    "zipf": (16, 96, 256, 400, 8, "zipf"),
+}
+
+
+@pytest.mark.parametrize("shape", list(GROUPED_SHAPES))
+@pytest.mark.parametrize("wtype", list(GROUPED), ids=lambda t: GROUPED[t])
+def test_grouped_partials_and_outputs_match_oracle(wtype, shape):
+    E, N, K, T, k, kind = GROUPED_SHAPES[shape]
+    say(f"[gguf grouped] {GROUPED[wtype]} {shape}: E={E} N={N} K={K} T={T} top_k={k}")
+    c = WCase(wtype, E, N, K, T, k, seed=wtype * 10 + 3, kind=kind)
+    assert np.array_equal(c.partials(ftq.PATH_GROUPED), c.oracle_partials())
+    c.check(c.run(ftq.PATH_GROUPED))
+
+
+@pytest.mark.parametrize("wtype", list(GROUPED), ids=lambda t: GROUPED[t])
+def test_auto_takes_the_grouped_path_at_prefill(wtype):
+    E, N, K, T, k = 8, 128, 512, 256, 2
+    c = WCase(wtype, E, N, K, T, k, seed=4)
+    assert c.resolved(ftq.PATH_AUTO) == ftq.PATH_GROUPED
+    auto = c.run(ftq.PATH_AUTO)
+    assert np.array_equal(auto, c.run(ftq.PATH_GROUPED))
+    c.check(auto, path=ftq.PATH_GROUPED)
+
+
+def test_grouped_q4_1_odd_block_count():
+    # 20-byte blocks stay 4-byte aligned at any K/32 (K/32 = 3 here)
+    E, N, K, T, k = 4, 77, 96, 90, 3
+    c = WCase(ftq.W_Q4_1, E, N, K, T, k, seed=5)
+    assert np.array_equal(c.partials(ftq.PATH_GROUPED), c.oracle_partials())
+    c.check(c.run(ftq.PATH_GROUPED))
+
+
+@pytest.mark.parametrize("wtype", list(GROUPED), ids=lambda t: GROUPED[t])
+def test_grouped_page1_T8191_sampled(wtype):
+    # the FreeToken PR #185 Performance shape at T = 8191 (65528 pairs): all
+    # outputs computed, sampled pairs against the oracle
+    E, N, K, T, k = 128, 1408, 2816, 8191, 8
+    say(f"[gguf grouped page-1] {GROUPED[wtype]} T={T}")
+    c = WCase(wtype, E, N, K, T, k, seed=0)
+    assert c.resolved(ftq.PATH_AUTO) == ftq.PATH_GROUPED
+    out = c.run()
+    pairs = sample_pairs(T, k, 24, seed=5)
+    c.check(out[pairs], pairs)
