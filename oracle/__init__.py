@@ -24,7 +24,9 @@ import numpy as np
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 _SRC = os.path.join(_HERE, "oracle.c")
-_LIB = os.path.join(_HERE, "liboracle.so")
+# ORACLE_LIB_PATH: a build of oracle.c made elsewhere (the host-sanitizer run)
+_LIB_ENV = os.environ.get("ORACLE_LIB_PATH")
+_LIB = _LIB_ENV or os.path.join(_HERE, "liboracle.so")
 QK = 32
 Q4_0_BYTES = 18
 Q8_1_BYTES = 36
@@ -47,7 +49,7 @@ def _load():
     global _lib
     if _lib is not None:
         return _lib
-    if not os.path.exists(_LIB) or os.path.getmtime(_LIB) < os.path.getmtime(_SRC):
+    if not _LIB_ENV and (not os.path.exists(_LIB) or os.path.getmtime(_LIB) < os.path.getmtime(_SRC)):
         build()
     lib = ctypes.CDLL(_LIB)
     P, I64 = ctypes.c_void_p, ctypes.c_int64

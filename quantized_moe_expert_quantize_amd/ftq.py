@@ -13,7 +13,8 @@ import os
 import torch
 
 _PKG = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(_PKG, "libftq.so")
+# FTQ_LIB_PATH: a libftq.so built elsewhere (for example with host sanitizers)
+LIB_PATH = os.environ.get("FTQ_LIB_PATH") or os.path.join(_PKG, "libftq.so")
 
 OK, ERR_INVALID_ARG, ERR_WORKSPACE, ERR_LAUNCH, ERR_UNSUPPORTED, ERR_HIP = range(6)
 PATH_AUTO, PATH_GEMV, PATH_GROUPED = 0, 1, 2
