@@ -259,6 +259,19 @@ __device__ __forceinline__ void load_step(const uint8_t* src, int len, int l, Ra
     for (int i = 0; i < Raw<VEC, WT>::kUnits; ++i) R.u[i] = __builtin_nontemporal_load(s + min(kLPR * i + l, last));
 }
 
+// Sum of v over the 16 lanes of a row, in every lane of the row.  Rotations of
+// the row by 8, 4, 2 and 1 lanes (DPP, no LDS) pair each lane with the same
+// partner values as the xor butterfly 8, 4, 2, 1 (after each level the values
+// repeat with the next distance), so the bits equal that tree's.
+__device__ __forceinline__ float row16_sum(float v)
+{
+    v += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x128, 0xf, 0xf, false));   // row_ror:8
+    v += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x124, 0xf, 0xf, false));   // row_ror:4
+    v += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x122, 0xf, 0xf, false));   // row_ror:2
+    v += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x121, 0xf, 0xf, false));   // row_ror:1
+    return v;
+}
+
 // Lanes of a wave exchange data through its private LDS step buffer.  The
 // hardware keeps one wave's LDS accesses in order, but the compiler reasons per
 // lane (a lane's own writes never overlap its own reads) and would move reads
@@ -329,6 +342,7 @@ __device__ __forceinline__ void stream_tiles(const GemvParams& p, int64_t e, int
     auto src_of = [&](int64_t t, int64_t ws) {
         return wexp + min<int64_t>(row_of(t), p.N - 1) * row_bytes + ws * kGroup * kBB;
     };
+
     // steps are (tile t, first group ws of the step), tile-major
     auto advance = [&](int64_t& t, int64_t& ws) {
         ws += kStepGroups;
@@ -349,14 +363,17 @@ __device__ __forceinline__ void stream_tiles(const GemvParams& p, int64_t e, int
     // unconditional load keeps the loads in flight the same on every path.
     Raw<VEC, WT> R;
     int64_t t = t0, ws = gbeg;
+    auto load = [&](int64_t tl, int64_t wl) __attribute__((always_inline)) {
+        load_step<VEC>(src_of(tl, wl), step_len(wl), l, R);
+    };
     if constexpr (WT == FTQ_W_Q4_0) {
-        load_step<VEC>(src_of(t, ws), step_len(ws), l, R);
+        load(t, ws);
         stage();
     } else {
         // the wider blocks' step buffers would stay live through the staging
         // and spill: stage first
         stage();
-        load_step<VEC>(src_of(t, ws), step_len(ws), l, R);
+        load(t, ws);
     }
     while (t < t1) {
         const int64_t n = kFused ? col_of(t) : row_of(t);
@@ -376,7 +393,7 @@ __device__ __forceinline__ void stream_tiles(const GemvParams& p, int64_t e, int
         advance(t2, ws2);
         {
             const bool in = t2 < t1;
-            load_step<VEC>(src_of(in ? t2 : t1 - 1, in ? ws2 : gbeg), step_len(in ? ws2 : gbeg), l, R);
+            load(in ? t2 : t1 - 1, in ? ws2 : gbeg);
         }
         // lanes whose group is past the segment (partial steps) compute on a
         // valid group with scale 0 (fma(P, 0, acc) == acc); rows past N are
@@ -430,15 +447,11 @@ __device__ __forceinline__ void stream_tiles(const GemvParams& p, int64_t e, int
             }
         }
         if constexpr (!kPartials) {
-            // end of a step: the 16 lane sums by a fixed xor tree (every lane of
-            // the row gets the same value), added to the row's running sum
+            // end of a step: the 16 lane sums by a fixed tree (row16_sum: every
+            // lane of the row gets the same value), added to the row's running sum
 #pragma unroll
             for (int j = 0; j < kJ; ++j) {
-                float v = acc[j];
-                v += __shfl_xor(v, 8);
-                v += __shfl_xor(v, 4);
-                v += __shfl_xor(v, 2);
-                v += __shfl_xor(v, 1);
+                const float v = row16_sum(acc[j]);
                 acc[j] = 0.0f;
                 const bool first = ws == gbeg && !(kMultiSeg && sb > 0);
                 rs[j] = first ? v : rs[j] + v;
@@ -656,6 +669,10 @@ __global__ __launch_bounds__(kThreads, kWavesPerSimd) void moe_gemv_kernel(GemvP
                     FTQ_STREAM(1);
                 } else if (VEC == 16 && npc == 2) {
                     FTQ_STREAM(2);
+                } else if (VEC == 16 && npc == 3) {
+                    FTQ_STREAM(3);
+                } else if (VEC == 16 && npc == 4) {
+                    FTQ_STREAM(4);
                 } else {
                     FTQ_STREAM(0);
                 }
