@@ -358,9 +358,9 @@ __device__ __forceinline__ void stream_tiles(const GemvParams& p, int64_t e, int
     for (int j = 0; j < kJ; ++j) acc[j] = rs[j] = 0.0f;
 
     // Steps: (tile t, first group ws of the step); the loads of the next step
-    // are in flight while the current one is computed.  Past the range the
-    // load re-reads the last tile's first step (an L2 hit, never used): an
-    // unconditional load keeps the loads in flight the same on every path.
+    // are in flight while the current one is computed.  The last step of the
+    // range loads nothing more (a wave-uniform branch): the weight loads are
+    // non-temporal, so a re-read of an earlier step would go to HBM again.
     Raw<VEC, WT> R;
     int64_t t = t0, ws = gbeg;
     auto load = [&](int64_t tl, int64_t wl) __attribute__((always_inline)) {
@@ -391,10 +391,7 @@ __device__ __forceinline__ void stream_tiles(const GemvParams& p, int64_t e, int
         wave_lds_fence();   // and this step's writes before its reads
         int64_t t2 = t, ws2 = ws;
         advance(t2, ws2);
-        {
-            const bool in = t2 < t1;
-            load(in ? t2 : t1 - 1, in ? ws2 : gbeg);
-        }
+        if (t2 < t1) load(t2, ws2);
         // lanes whose group is past the segment (partial steps) compute on a
         // valid group with scale 0 (fma(P, 0, acc) == acc); rows past N are
         // never written
