@@ -168,6 +168,7 @@ GROUPED_SHAPES = {
     "bm128": (4, 200, 320, 100, 4, "uniform"),
     "bm64": (8, 136, 512, 100, 4, "uniform"),
     "bm32_page1_rows": (16, 64, 2816, 48, 4, "uniform"),
+    "bm128_page1_K": (4, 96, 2816, 110, 4, "uniform"),
     "zipf": (16, 96, 256, 400, 8, "zipf"),
 }
 

@@ -108,6 +108,19 @@ def test_kernels_page1_shape_sampled():
     assert_matches_oracle(outs[0].cpu().numpy()[pairs], ref, ab, c.nb)
 
 
+def test_kernels_partials_exact_at_page1_K_with_128_row_tiles():
+    # the page-1 hidden size (K = 2816, 88 blocks: 44 passes) at the tile height
+    # the bench runs (>= 96 pairs per expert), on a reduced N
+    E, N, K, T, k = 4, 160, 2816, 120, 4
+    c = Case(E, N, K, T, k, seed=14)
+    ref_part = c.oracle_partials()
+    parts = _each_variant(lambda: c.partials(ftq.PATH_GROUPED))
+    for v, p in zip(VARIANTS, parts):
+        assert np.array_equal(p, ref_part), f"variant {v}"
+    ref, ab = c.oracle_out()
+    assert_matches_oracle(c.run(ftq.PATH_GROUPED).cpu().numpy(), ref, ab, c.nb)
+
+
 def test_unknown_variant_is_rejected():
     with pytest.raises(RuntimeError, match="variant"):
         ftq.grouped_kernel(7)

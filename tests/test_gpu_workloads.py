@@ -31,7 +31,7 @@ WORKLOADS = [
     # name, E, N, K, top_k, T, routing, sampled pairs
     ("page1_T2048", 128, 1408, 2816, 8, 2048, "uniform", 48),
     ("page1_T4096", 128, 1408, 2816, 8, 4096, "uniform", 48),
-    ("page1_T8191", 128, 1408, 2816, 8, 8191, "uniform", 48),
+    ("page1_T8191", 128, 1408, 2816, 8, 8191, "uniform", 1024),
     ("page1_T1", 128, 1408, 2816, 8, 1, "uniform", 8),
     ("qwen3_up_T8192_zipf", 128, 768, 2048, 8, 8192, "zipf", 64),
     ("mixtral_T1", 8, 14336, 4096, 2, 1, "uniform", 2),
@@ -52,6 +52,21 @@ def test_workload_sampled_rows(wl):
     got = out[torch.from_numpy(pairs).cuda()].cpu().numpy()
     del out
     ref, ab = c.oracle_out(pairs)
+    assert_matches_oracle(got, ref, ab, c.nb)
+
+
+def test_page1_T8191_every_pair_on_spread_rows():
+    # all 65528 pairs of the bench workload, on 62 weight rows spread over N
+    # (every 23rd, plus the last): the oracle runs on the experts' rows
+    # restricted to those, which is the same arithmetic per output element
+    E, N, K, k, T = 128, 1408, 2816, 8, 8191
+    rows = np.unique(np.concatenate([np.arange(0, N, 23), [N - 1]]))
+    c = Case(E, N, K, T, k, seed=0, w32=_weights(E, N, K))
+    say(f"[workload] page-1 T={T}: all {T * k} pairs x {len(rows)} rows, path {ftq.select_path(E, N, K, T, k)}")
+    got = c.run()[:, torch.from_numpy(rows).cuda()].cpu().numpy()
+    sub = Case(E, len(rows), K, T, k, seed=0, w32=np.ascontiguousarray(_weights(E, N, K)[:, rows, :]),
+               x32=c.x32, ids=c.ids)
+    ref, ab = sub.oracle_out()
     assert_matches_oracle(got, ref, ab, c.nb)
 
 
