@@ -11,34 +11,36 @@
 //
 // Arithmetic, exact at every step.  Per output element and quantisation block b
 // the result needs the integer partial P_b = sum_i (q4-8)*q8 and the scale
-// product d4*d8.  On gfx950 both come from the matrix cores:
-//   * P_b: two v_mfma_f32_32x32x16_f16 over the block's 32 values.  The Q8_1
-//     codes (|q| <= 127) and the Q4_0 values (q-8 in [-8, 7]) are exact in
-//     fp16, every product is an exact small integer and every partial sum stays
-//     below 2^24, so the fp32 result is P_b exactly, in any summation order;
-//   * d4*d8: one more f16 MFMA (32x32x8) used as an outer product: both
-//     operands are read from LDS as {scale, 0, 0, 0}, so only k = 0 adds and a
-//     product of two fp16 values is exact in fp32;
-//   * the vector ALUs then do a single fp32 FMA per element and block:
-//     acc = fma(P_b, d4*d8, acc), blocks in ascending order.
-// Doing the products on the MFMA units leaves one VALU op per element-block,
-// instead of three (int->float convert, scale multiply, FMA) after an int8 MFMA.
-// The per-element arithmetic does not depend on where a pair sits in a tile,
-// so results are batch invariant.
+// product d4*d8; the vector ALUs then do a single fp32 FMA per element and
+// block, acc = fma(P_b, d4*d8, acc), blocks in ascending order.  P_b comes from
+// the matrix cores in one of two formulations, which give the same bits:
+//   * int8 (the default): one v_mfma_i32_32x32x32_i8 per 32x32 sub-tile and
+//     block on the int8 codes (weight nibbles unpacked to q - 8 while staging,
+//     Q8_1 codes staged as they are), then one int -> float convert (exact:
+//     |P_b| < 2^24) before the FMA;
+//   * fp16: two v_mfma_f32_32x32x16_f16 over the block's 32 values.  The codes
+//     (|q8| <= 127, q4 - 8 in [-8, 7]) are exact in fp16, every product is an
+//     exact small integer and every partial sum stays below 2^24, so the fp32
+//     result is P_b exactly, in any summation order; no convert is needed, but
+//     staging widens every code to fp16.
+// d4*d8 comes from one more f16 MFMA (32x32x8) used as an outer product: both
+// operands are read from LDS as {scale, 0, 0, 0}, so only k = 0 adds and a
+// product of two fp16 values is exact in fp32.  The per-element arithmetic
+// does not depend on where a pair sits in a tile, so results are batch
+// invariant.  Q8_0 and Q4_1 weights run the int8 formulation with their own
+// staging (codes as they are; nibbles 0..15); the Q4_1 offset term m*d8*sum(q8)
+// is added by one bf16 matrix product per pass (see offset_a_operand).
 //
-// Operands.  The Q8_1 activation blocks are read as they are (36 bytes: fp16
-// scale, fp16 sum, 32 int8 codes) and their codes widened to fp16 while a tile
-// is staged into LDS; the weight nibbles are unpacked to fp16 at the same step,
-// in a block-internal k order chosen so that each 32-bit word of nibbles yields
-// four packed fp16 pairs with one mask-or and one packed add each; the
-// activation codes are written in that same order, so the dot products match.
-// The two blocks of a pass that belong to one row are loaded by adjacent lanes.
-// Tiles are double buffered in LDS (loads for block pair s+1 are in flight while
-// block pair s is multiplied); the global loads are buffer loads whose per-lane
-// offsets are fixed for a tile and whose per-pass advance is a scalar offset.
-// Within a pass the matrix products of one 32x32 sub-tile are issued before the
-// scale-accumulate of the previous one, so matrix cores and vector ALUs overlap.
-// In ragged tiles a wave whose rows hold no pair skips its MFMA work.
+// Operands.  The Q8_1 activation blocks are read in place (36 bytes: fp16
+// scale, fp16 sum, 32 int8 codes) and staged into LDS per pass of two blocks,
+// with the weight blocks of the tile's 128 rows; the two blocks of a pass that
+// belong to one row are loaded by adjacent lanes.  Tiles are double buffered
+// in LDS (loads for block pair s+1 are in flight while block pair s is
+// multiplied); the global loads are buffer loads whose per-lane offsets are
+// fixed for a tile and whose per-pass advance is a scalar offset.  In ragged
+// tiles a wave whose rows hold no pair skips its MFMA work.  A third kernel
+// (namespace ws) runs the fp16 formulation warp-specialised, loader and MMA
+// waves paced by LDS counters; it is kept for comparison.
 //
 // Fused gated activation (kFused): a tile's 128 weight rows are the gate rows
 // of 64 output columns followed by their up rows; after the K loop the waves
@@ -551,6 +553,7 @@ __global__ __launch_bounds__(Shape<BM>::kThreads, Shape<BM>::kWavesPerSimd) void
         // One staged pass, int8 codes: per sub-tile and block the exact integer
         // partial from one v_mfma_i32_32x32x32_i8, converted to fp32 (exact:
         // |P| < 2^24), then one FMA with the scale product from the f16 MFMA
+        // (the outer product d8 x d4)
         auto compute_i8 = [&](int buf, int64_t kb0) {
             if (!wave_rows) return;
             v4i ai[kKB][S::SM], bi[kKB][S::SN];
