@@ -166,6 +166,12 @@ def decode_record(name: str, T: int, scrub, reps: int = 10) -> dict:
     cold = _cold_times(call, scrub, reps)
     alg = _algorithmic_bytes(E, N, K, T, k, ids)
     wm, cm = statistics.median(warm), statistics.median(cold)
+    traffic = None
+    tf = traffic_file("moe_gemv_kernel" if path == ftq.PATH_GEMV else "moe_grouped_kernel", name, T)
+    if os.path.exists(tf):
+        rec = json.load(open(tf))
+        if rec.get("lib_sha256") == _lib_hash() and rec.get("T") == T:
+            traffic = rec.get("bytes_per_launch")
     return {"workload": wl["workload"], "T": T, "pairs": T * k, "path": {1: "gemv", 2: "grouped"}[path],
             "kernel": "moe_gemv_kernel" if path == ftq.PATH_GEMV else "moe_grouped_kernel",
             "alg_bytes_per_launch": alg,
@@ -175,7 +181,7 @@ def decode_record(name: str, T: int, scrub, reps: int = 10) -> dict:
                          "achieved_warm": round(alg / (wm / 1e3) / 1e9, 1),
                          "frac_warm": round(alg / (wm / 1e3) / 1e9 / HBM_PEAK_GBS, 4),
                          "achieved_cold": round(alg / (cm / 1e3) / 1e9, 1),
-                         "frac_cold": round(alg / (cm / 1e3) / 1e9 / HBM_PEAK_GBS, 4)},
+                         "frac_cold": round(alg / (cm / 1e3) / 1e9 / HBM_PEAK_GBS, 4), "traffic": traffic},
             "timing": "warm: HIP events around a graph replay of 20 calls, per call, 5 replays; cold: HIP events "
                       f"around one call right after a 1 GiB write, {reps} calls"}
 
