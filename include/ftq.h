@@ -326,9 +326,10 @@ int ftq_moe_q4_0_q8_1_act_routed(const void* w, const void* a, const int32_t* to
  * the activation codes, not the fp16 s field.  Evaluation in fp32.  GEMV path:
  * per block acc = fma(P, d*d8, acc) then, for offset types, acc = fma(S,
  * m*d8, acc), S = sum q8.  Grouped path: per block acc = fma(P, d*d8, acc) with
- * P from an int8 matrix product; the Q4_1 offset terms are summed apart, by
- * bf16 matrix products whose operands split d8*S (exact in fp32) and m into
- * bf16 pieces with exact products, and added to acc at the end.
+ * P from an int8 matrix product; the Q4_1 offset terms of each pass of two
+ * blocks are added into acc by one bf16 matrix product whose operands split
+ * d8*S (exact in fp32) and m into bf16 pieces with exact products (only the
+ * sums round).
  *   w:          [E][N][K/32] blocks of wtype;
  *   a:          Q8_1, [T][K/32] (act_per_pair == 0) or [T*top_k][K/32] (one
  *               row per pair, as ftq_moe_q4_0_q8_1_pairs);
