@@ -212,3 +212,21 @@ def test_grouped_page1_T8191_sampled(wtype):
     out = c.run()
     pairs = sample_pairs(T, k, 24, seed=5)
     c.check(out[pairs], pairs)
+
+
+@pytest.mark.parametrize("wtype", list(GROUPED), ids=lambda t: GROUPED[t])
+def test_grouped_over_cap_batch_equals_its_halves(wtype):
+    # FreeToken PR #185, Test: one batch past 65535 pairs (T = 8192, top_k = 8)
+    # equals the concatenation of its two halves, bit for bit, on the grouped
+    # path (Q8_0 / Q4_1 weights); page-1 rows at a reduced N
+    E, N, K, T, k = 128, 96, 2816, 8192, 8
+    c = WCase(wtype, E, N, K, T, k, seed=6)
+    w, a, ids = c.gpu()
+    whole = ftq.moe_gguf(w, wtype, a, ids, E, N, K, path=ftq.PATH_GROUPED)
+    h = T // 2
+    lo = ftq.moe_gguf(w, wtype, a[:h].contiguous(), ids[:h].contiguous(), E, N, K, path=ftq.PATH_GROUPED)
+    hi = ftq.moe_gguf(w, wtype, a[h:].contiguous(), ids[h:].contiguous(), E, N, K, path=ftq.PATH_GROUPED)
+    torch.cuda.synchronize()
+    assert torch.equal(whole, torch.cat([lo, hi]))
+    pairs = sample_pairs(T, k, 16, seed=7)
+    c.check(whole.cpu().numpy()[pairs], pairs, path=ftq.PATH_GROUPED)
