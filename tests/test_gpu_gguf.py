@@ -230,3 +230,29 @@ def test_grouped_over_cap_batch_equals_its_halves(wtype):
     assert torch.equal(whole, torch.cat([lo, hi]))
     pairs = sample_pairs(T, k, 16, seed=7)
     c.check(whole.cpu().numpy()[pairs], pairs, path=ftq.PATH_GROUPED)
+
+
+@pytest.mark.parametrize("path", [ftq.PATH_GEMV, ftq.PATH_GROUPED], ids=["gemv", "grouped"])
+@pytest.mark.parametrize("wtype", [ftq.W_Q4_0, ftq.W_Q4_1], ids=["q4_0", "q4_1"])
+def test_weights_only_2_byte_aligned(wtype, path):
+    # the weight pointer 2 bytes past a 4-byte boundary (allowed: w needs 2-byte
+    # alignment): both paths fall back to 2-byte weight loads
+    E, N, K, T, k = 4, 72, 320, 110, 4
+    c = WCase(wtype, E, N, K, T, k, seed=9)
+    w, a, ids = c.gpu()
+    buf = torch.zeros(w.numel() + 2, dtype=torch.uint8, device=w.device)
+    buf[2:].copy_(w)
+    w2 = buf[2:]
+    assert w2.data_ptr() % 4 == 2
+    if wtype != ftq.W_Q4_0 and path == ftq.PATH_GEMV:
+        # the GEMV streams the wider blocks as 4-byte words only
+        with pytest.raises(ftq.FtqError) as ei:
+            ftq.moe_gguf(w2, wtype, a, ids, E, N, K, path=path)
+        assert ei.value.status == ftq.ERR_UNSUPPORTED
+        return
+    part = ftq.moe_gguf_partials(w2, wtype, a, ids, E, N, K, path=path)
+    out = ftq.moe_gguf(w2, wtype, a, ids, E, N, K, path=path)
+    torch.cuda.synchronize()
+    assert np.array_equal(part.cpu().numpy(), c.oracle_partials())
+    c.check(out.cpu().numpy(), path=path)
+    assert torch.equal(out, ftq.moe_gguf(w, wtype, a, ids, E, N, K, path=path))
