@@ -25,8 +25,10 @@ and the 256 MB last-level cache); `roofline` reports the dominant kernel (the
 grouped matmul: against the dense int8 MFMA peak, its block products run on
 int8 MFMAs) using its algorithmic operation count, timed with HIP events on the
 stream it runs on; `decode` adds the GEMV path at Mixtral-8x7B decode shapes
-(T = 1 and 8) against the HBM roofline, warm and cold; `cpu_baseline` is the
-CPU oracle on a bounded sample of the same workload, with the host CPU named.
+(T = 1 and 8) against the HBM roofline, warm and cold; `sweep` times one
+routed matmul call of the page-1 shape at T = 1 .. 8192 on the path that
+FTQ_PATH_AUTO takes, against both rooflines; `cpu_baseline` is the CPU oracle
+on a bounded sample of the same workload, with the host CPU named.
 """
 from __future__ import annotations
 
@@ -80,6 +82,9 @@ SCRUB_BYTES = 1 << 30           # written before each cold step: larger than the
 # decode records carried on every bench line: the GEMV at Mixtral-8x7B's
 # up-projection shape (mlxcel PR #652, Summary) at one and eight tokens
 DECODE = (("mixtral", 1), ("mixtral", 8))
+# the metric's batch range on the page-1 shape (one routed matmul call per
+# point, FTQ_PATH_AUTO): decode, mid-range and prefill sizes
+SWEEP_T = (1, 8, 32, 128, 512, 2048, 8192)
 
 
 def cpu_model() -> str:
@@ -184,6 +189,72 @@ def decode_record(name: str, T: int, scrub, reps: int = 10) -> dict:
                          "frac_cold": round(alg / (cm / 1e3) / 1e9 / HBM_PEAK_GBS, 4), "traffic": traffic},
             "timing": "warm: HIP events around a graph replay of 20 calls, per call, 5 replays; cold: HIP events "
                       f"around one call right after a 1 GiB write, {reps} calls"}
+
+
+def sweep_record(scrub) -> dict:
+    """The page-1 shape (128 experts, N = 1408, K = 2816, top_k = 8) over the
+    metric's batch range: per T one routed matmul call on the path that
+    FTQ_PATH_AUTO takes, warm (HIP events around a graph of R calls, per call,
+    median of 5 replays), with its algorithmic bytes and operations against the
+    HBM and the int8 MFMA roofline (the path's own bound first)."""
+    import torch
+    from quantized_moe_expert_quantize_amd import ftq, inputs
+    wl, _ = WORKLOADS["page1"]
+    E, N, K, k = wl["E"], wl["N"], wl["K"], wl["top_k"]
+    dev = scrub.device
+    gen = torch.Generator(device=dev)
+    gen.manual_seed(wl["seed"])
+    wq = torch.empty((E, N, K // 32 * 18), dtype=torch.uint8, device=dev)
+    for e in range(E):
+        w = torch.randn((N, K), generator=gen, device=dev, dtype=torch.float32) * 0.02
+        wq[e] = ftq.quantize_q4_0(w).view(N, K // 32 * 18)
+        del w
+    points = []
+    for T in SWEEP_T:
+        ids = inputs.routing(T, E, k, seed=wl["seed"], kind=wl["routing"])
+        aq = ftq.quantize_q8_1(torch.from_numpy(inputs.activations(T, K, seed=wl["seed"])).to(dev))
+        ids_d = torch.from_numpy(ids).to(dev)
+        path = ftq.select_path(E, N, K, T, k)
+        out = torch.empty((T * k, N), dtype=torch.float32, device=dev)
+        need = ftq.workspace_bytes(E, N, K, T, k, path)
+        ws = torch.empty(max(need, 256), dtype=torch.uint8, device=dev) if need else None
+        ftq.moe_route(ids_d, E, ws, path)
+
+        def call():
+            ftq.moe_routed(wq, aq, ids_d, E, N, K, out, ws, path)
+
+        for _ in range(3):
+            call()
+        torch.cuda.synchronize()
+        R = 20 if T <= 512 else 4
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            for _ in range(R):
+                call()
+        torch.cuda.synchronize()
+        per_call = []
+        for _ in range(5):
+            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            a.record()
+            g.replay()
+            b.record()
+            torch.cuda.synchronize()
+            per_call.append(a.elapsed_time(b) / R)
+        ms = statistics.median(per_call)
+        alg = _algorithmic_bytes(E, N, K, T, k, ids)
+        ops = 2 * T * k * N * K
+        gbs, tops = alg / (ms / 1e3) / 1e9, ops / (ms / 1e3) / 1e12
+        gemv = path == ftq.PATH_GEMV
+        points.append({"T": T, "pairs": T * k, "path": "gemv" if gemv else "grouped", "us": round(ms * 1e3, 2),
+                       "alg_bytes": alg, "GBps": round(gbs, 1), "hbm_frac": round(gbs / HBM_PEAK_GBS, 4),
+                       "TOPS": round(tops, 2), "int8_frac": round(tops / INT8_PEAK_TOPS, 4),
+                       "bound": "hbm" if gemv else "mfma"})
+        del g, out, ws, aq, ids_d
+    return {"workload": wl["workload"], "E": E, "N": N, "K": K, "top_k": k, "routing": wl["routing"],
+            "timing": "one routed matmul call (FTQ_PATH_AUTO; routing excluded) per point: HIP events around a graph "
+                      "replay of R calls (R = 20 up to T = 512, else 4), per call, median of 5 replays; inputs "
+                      "resident (warm)",
+            "points": points}
 
 
 def traffic_file(kernel: str, workload: str, T: int) -> str:
@@ -301,6 +372,7 @@ def main() -> None:
                     help="weight block type (not q4_0: random valid blocks, plain layers only; q5_* on the GEMV path)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-decode", action="store_true", help="skip the Mixtral decode records")
+    ap.add_argument("--no-sweep", action="store_true", help="skip the page-1 batch sweep (T = 1 .. 8192)")
     ap.add_argument("--cold-steps", type=int, default=10, help="steps timed after a 1 GiB cache scrub each")
     ap.add_argument("--cpu-sample-tokens", type=int, default=8192, help="tokens the CPU oracle runs (10-30 s on the box)")
     ap.add_argument("--summarize-pmc", metavar="DIR")
@@ -532,6 +604,9 @@ def main() -> None:
     decode = None
     if not args.no_decode:
         decode = [decode_record(name, t, scrub) for name, t in DECODE]
+    sweep = None
+    if not args.no_sweep and args.workload == "page1" and args.wtype == "q4_0":
+        sweep = sweep_record(scrub)
 
     # ---- CPU oracle on a bounded sample of the same workload ----------------
     cpu = None
@@ -598,6 +673,7 @@ def main() -> None:
         "roofline": roofline,
         "cpu_baseline": cpu,
         "decode": decode,
+        "sweep": sweep,
         "host_cpu": cpu_model(),
         "lib_sha256": _lib_hash()[:16],
     }
