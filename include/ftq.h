@@ -113,13 +113,13 @@ int ftq_quantize_q4_0(const float* w, int64_t rows, int64_t K, void* y, hipStrea
  * call has to wait for the GPU and every call stays capturable in a graph
  * ("Current Bug: CuTeDSLMoERunner", Bug 8b and Cudagraph Constraints: a host
  * readback of device values breaks capture).  Rule: the GEMV path when
- * T*top_k <= 4096 and the pairs per expert T*top_k/E are at most 4 (E <= 16)
- * or 1.5 (E > 16); the grouped path otherwise.
+ * T*top_k <= 4096 and the pairs per expert T*top_k/E are at most 7 (E <= 16)
+ * or 4 (E > 16); the grouped path otherwise.
  * Bit equality of a batch and its split halves (FreeToken PR #185, Test) holds
  * on each forced path.  Under FTQ_PATH_AUTO it holds when the batch and its
  * halves fall on the same side of the rule, which is not the case just above
- * the crossover: with 128 experts and top_k = 8, T = 25..48 runs grouped and
- * its halves run the GEMV; with 8 experts and top_k = 2, T = 17..32.  The two
+ * the crossover: with 128 experts and top_k = 8, T = 65..128 runs grouped and
+ * its halves run the GEMV; with 8 experts and top_k = 2, T = 29..56.  The two
  * paths sum in different orders, so their bits differ there (both within the
  * stated tolerance of the exact result).
  */

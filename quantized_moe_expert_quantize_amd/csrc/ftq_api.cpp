@@ -103,10 +103,9 @@ int select_path(int64_t E, int64_t T, int64_t top_k)
     const int64_t pairs = T * top_k;
     // few pairs per expert: stream each expert's rows once and serve its pairs
     // on the vector ALUs; otherwise sorted MFMA tiles.  The crossover, measured
-    // on one MI355X: about 5 pairs per expert with 8 experts (14336 x 4096
-    // rows), about 1.5 with 128 (1408 x 2816), where every tile round of the
-    // grouped path is full from a few pairs per expert on.
-    const int64_t per_expert_x2 = E <= 16 ? 8 : 3;   // twice the pairs per expert
+    // on one MI355X: about 7 pairs per expert with 8 experts (14336 x 4096
+    // rows), about 4 with 128 (1408 x 2816).
+    const int64_t per_expert_x2 = E <= 16 ? 14 : 8;   // twice the pairs per expert
     if (pairs <= kGemvScanMaxPairs && 2 * pairs <= per_expert_x2 * E) return FTQ_PATH_GEMV;
     return FTQ_PATH_GROUPED;
 }

@@ -658,10 +658,13 @@ __global__ __launch_bounds__(kThreads, kWavesPerSimd) void moe_gemv_kernel(GemvP
                 };
                 uint8_t* wrow = lds + L.wt + wave * wave_w(WT) + rw * wrow_pitch(WT);
 #define FTQ_STREAM(NPC) stream_tiles<VEC, kPartials, kMultiSeg, NPC, kFused, WT>(p, e, t0, t1, sb, len, npc, plist, wrow, codes, ds, l, rw, wave, stage)
-                // one or two pairs per expert (decode) without per-pair guards;
-                // more pairs keep the guarded loop, whose guards also stop the
-                // scheduler from interleaving all 8 blocks (which would need
-                // 8 * 10 * npc registers)
+                // a stream without per-pair guards for each pair count up to 4
+                // (and up to 8 in the plain Q4_0 kernel that scans the ids, the
+                // one the path rule gives such counts: the other kernels would
+                // spill with them); other counts keep the guarded loop, whose
+                // guards also stop the scheduler from interleaving all 8 blocks
+                // (which would need 8 * 10 * npc registers)
+                constexpr bool kWideNpc = VEC == 16 && WT == FTQ_W_Q4_0 && !kFused && !kPartials && !kBucketed;
                 if (VEC == 16 && npc == 1) {
                     FTQ_STREAM(1);
                 } else if (VEC == 16 && npc == 2) {
@@ -670,6 +673,14 @@ __global__ __launch_bounds__(kThreads, kWavesPerSimd) void moe_gemv_kernel(GemvP
                     FTQ_STREAM(3);
                 } else if (VEC == 16 && npc == 4) {
                     FTQ_STREAM(4);
+                } else if (kWideNpc && npc == 5) {
+                    FTQ_STREAM(5);
+                } else if (kWideNpc && npc == 6) {
+                    FTQ_STREAM(6);
+                } else if (kWideNpc && npc == 7) {
+                    FTQ_STREAM(7);
+                } else if (kWideNpc && npc == 8) {
+                    FTQ_STREAM(8);
                 } else {
                     FTQ_STREAM(0);
                 }

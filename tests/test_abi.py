@@ -89,11 +89,11 @@ def test_path_choice_is_host_arithmetic_of_sizes():
     assert ftq.select_path(8, 14336, 4096, 8, 2) == ftq.PATH_GEMV
     assert ftq.select_path(8, 14336, 4096, 64, 2) == ftq.PATH_GROUPED
     assert ftq.select_path(128, 1408, 2816, 1, 8) == ftq.PATH_GEMV
-    # measured crossovers: ~5 pairs per expert at 8 experts, ~1.5 at 128
-    assert ftq.select_path(8, 14336, 4096, 16, 2) == ftq.PATH_GEMV      # 4 per expert
-    assert ftq.select_path(8, 14336, 4096, 24, 2) == ftq.PATH_GROUPED   # 6 per expert
-    assert ftq.select_path(128, 1408, 2816, 16, 8) == ftq.PATH_GEMV     # 1 per expert
-    assert ftq.select_path(128, 1408, 2816, 32, 8) == ftq.PATH_GROUPED  # 2 per expert
+    # measured crossovers: ~7 pairs per expert at 8 experts, ~4 at 128
+    assert ftq.select_path(8, 14336, 4096, 28, 2) == ftq.PATH_GEMV      # 7 per expert
+    assert ftq.select_path(8, 14336, 4096, 32, 2) == ftq.PATH_GROUPED   # 8 per expert
+    assert ftq.select_path(128, 1408, 2816, 64, 8) == ftq.PATH_GEMV     # 4 per expert
+    assert ftq.select_path(128, 1408, 2816, 65, 8) == ftq.PATH_GROUPED  # just over 4 per expert
     for T in (2048, 4096, 8191, 8192, 16384):
         assert ftq.select_path(128, 1408, 2816, T, 8) == ftq.PATH_GROUPED
     assert ftq.workspace_bytes(8, 14336, 4096, 1, 2) == 0
