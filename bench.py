@@ -605,7 +605,7 @@ def main() -> None:
     if not args.no_decode:
         decode = [decode_record(name, t, scrub) for name, t in DECODE]
     sweep = None
-    if not args.no_sweep and args.workload == "page1" and args.wtype == "q4_0":
+    if not args.no_sweep and args.workload == "page1" and args.wtype == "q4_0" and T == DEFAULT_T:
         sweep = sweep_record(scrub)
 
     # ---- CPU oracle on a bounded sample of the same workload ----------------
