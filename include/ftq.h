@@ -388,6 +388,17 @@ void ftq_debug_force_block_threads(int threads);
 int ftq_debug_grouped_kernel(int variant);
 
 /*
+ * Comparison hook: with `split` non-zero, later routings on this host thread
+ * (ftq_moe_route and the routing inside the matmul calls) always run the
+ * bucketing as three kernels (per-chunk counts, one scan, the in-order
+ * scatter); with 0 (the default), batches of at most 8192 pairs whose
+ * per-chunk counts fit on chip (buckets x chunks <= 8192, at most 2048
+ * buckets) run the same three passes in one workgroup instead.  Both build
+ * the same tables bit for bit; they differ in speed only.
+ */
+void ftq_debug_route_kernels(int split);
+
+/*
  * Checking aid: the on-chip plan the GEMV path makes for these sizes, host
  * arithmetic only (no device is touched).  *seg: K/32 blocks staged per
  * segment (less than K/32 when a row is streamed in several K segments, which

@@ -37,6 +37,8 @@ void clear_error() { g_error.clear(); }
 int forced_block_threads() { return g_forced_threads; }
 
 int grouped_kernel_variant() { return g_grouped_variant; }
+thread_local int g_route_split = 0;
+int route_split_forced() { return g_route_split; }
 
 int device_limits(DeviceLimits* out)
 {
@@ -405,6 +407,8 @@ const char* ftq_last_error(void) { return g_error.c_str(); }
 const char* ftq_version(void) { return "ftq 0.1.0 gfx950"; }
 
 void ftq_debug_force_block_threads(int threads) { g_forced_threads = threads > 0 ? threads : 0; }
+
+void ftq_debug_route_kernels(int split) { g_route_split = split ? 1 : 0; }
 
 int ftq_debug_grouped_kernel(int variant)
 {

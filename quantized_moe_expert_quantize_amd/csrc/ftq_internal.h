@@ -35,6 +35,7 @@ int forced_block_threads();             // test hook value (0 = off)
 // grouped-path kernel choice (ftq_debug_grouped_kernel; int8 MFMAs by default)
 enum GroupedKernel { kGroupedI8 = 0, kGroupedF16 = 1, kGroupedF16Ws = 2 };
 int grouped_kernel_variant();
+int route_split_forced();               // test hook: bucketing in three kernels at any size
 
 // Launch `kernel` with a 1-D grid, after checking the geometry against the
 // device limits, and check the launch right after it is issued.  `name`

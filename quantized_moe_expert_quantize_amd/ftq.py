@@ -35,7 +35,7 @@ EXPORTS = (
     "ftq_moe_q4_0_q8_1_act", "ftq_moe_q4_0_q8_1_act_routed",
     "ftq_moe_gguf_q8_1", "ftq_moe_gguf_q8_1_partials",
     "ftq_last_error", "ftq_version",
-    "ftq_debug_force_block_threads", "ftq_debug_grouped_kernel", "ftq_debug_gemv_plan", "ftq_moe_q4_0_q8_1_noalloc",
+    "ftq_debug_force_block_threads", "ftq_debug_grouped_kernel", "ftq_debug_route_kernels", "ftq_debug_gemv_plan", "ftq_moe_q4_0_q8_1_noalloc",
 )
 
 
@@ -94,6 +94,8 @@ def lib() -> ctypes.CDLL:
     L.ftq_debug_force_block_threads.restype = None
     L.ftq_debug_grouped_kernel.argtypes = [I32]
     L.ftq_debug_grouped_kernel.restype = I32
+    L.ftq_debug_route_kernels.argtypes = [I32]
+    L.ftq_debug_route_kernels.restype = None
     L.ftq_debug_gemv_plan.argtypes = [I64, I64, I64, I64, I64, I32, I32, P, P, P]
     L.ftq_debug_gemv_plan.restype = I32
     L.ftq_moe_q4_0_q8_1_noalloc.argtypes = [P, P, P, P, I64, I64, I64, I64, I64, I32, P]
@@ -171,6 +173,12 @@ def grouped_kernel(variant: int):
     """Select the grouped path's kernel for later calls on this thread
     (GROUPED_I8, GROUPED_F16 or GROUPED_F16_WS)."""
     _check(lib().ftq_debug_grouped_kernel(variant))
+
+
+def route_kernels(split: bool):
+    """Bucketing in three kernels at any size (True) or, for small batches, in
+    one workgroup (False, the default) for later calls on this thread."""
+    lib().ftq_debug_route_kernels(1 if split else 0)
 
 
 def select_path(E: int, N: int, K: int, T: int, top_k: int) -> int:
